@@ -1,0 +1,190 @@
+"""fp64 CPU oracle for the MiMo-V2.6-Flash attention hot path.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the CPU-baseline leg
+of the benchmark use it; the product path never imports it.  It shares no code
+with the HIP library (see mimo_oracle.c for what is computed and where each
+step is stated on the pages).
+
+Every function takes numpy arrays (bf16 as uint16 bit patterns, positions as
+int64) and returns fp64 arrays.  Layouts follow the library's: token-major
+[tokens, heads, dim].
+
+Parity status: partial RoPE's pairing (rotate-half, not interleaved) and its
+frequency exponent over rope_dim are readings of the pages (they print the
+[rope, nope] split and the default rope type, not the rotation itself); the
+invariants in the tests hold for either pairing, so that one convention is
+"parity unpinned" by the pages.  Everything else is pinned by the tests in
+tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mimo_oracle.c")
+_LIB = os.path.join(_HERE, "libmimo_oracle.so")
+
+ROPE_DIM = 64
+SOFTMAX_SCALE = 1.0 / math.sqrt(192.0)
+V_SCALE = 0.707
+SWA_WINDOW = 128
+SWA_BASE = 1.0e4
+GLOBAL_BASE = 1.0e7
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math) and OpenMP."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+                               "-Wall", "-Werror", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=not os.path.exists(_LIB))
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        lib.oracle_rope_partial.argtypes = [P, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, P, ctypes.c_double, P]
+        lib.oracle_rope_partial.restype = None
+        lib.oracle_attention.argtypes = [
+            P, P, ctypes.c_int64, P, ctypes.c_int, P, ctypes.c_int64, P,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_double, P, ctypes.c_int64, ctypes.c_double, ctypes.c_double,
+            P, P, P, ctypes.c_int]
+        lib.oracle_attention.restype = None
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def rope_partial(x: np.ndarray, pos: np.ndarray, base: float, rope_dim: int = ROPE_DIM) -> np.ndarray:
+    """x [n_tok, n_heads, D] bf16 bits, pos [n_tok] -> rotated fp64 [n_tok, n_heads, D]."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    n, h, d = x.shape
+    out = np.empty((n, h, d), dtype=np.float64)
+    _load().oracle_rope_partial(_ptr(x), n, h, d, rope_dim, _ptr(pos), float(base), _ptr(out))
+    return out
+
+
+def attention(q, q_pos, k, k_pos, v, *, sinks=None, window: int = 0, base: float,
+              k_rotated: bool = False, softmax_scale: float = SOFTMAX_SCALE,
+              v_scale: float = V_SCALE, rope_dim: int = ROPE_DIM,
+              want_lse: bool = False, want_psink: bool = False, n_threads: int = 0):
+    """Rows of one sequence.  q [nq,Hq,Dqk], k [nk,Hkv,Dqk], v [nk,Hkv,Dv] bf16 bits.
+
+    Returns out [nq,Hq,Dv] fp64, plus lse / psink [nq,Hq] when asked."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    q_pos = np.ascontiguousarray(q_pos, dtype=np.int64)
+    k_pos = np.ascontiguousarray(k_pos, dtype=np.int64)
+    nq, hq, dqk = q.shape
+    nk, hkv, _ = k.shape
+    dv = v.shape[2]
+    assert hq % hkv == 0 and k.shape[2] == dqk and v.shape[:2] == (nk, hkv)
+    assert q_pos.shape == (nq,) and k_pos.shape == (nk,)
+    s = None if sinks is None else np.ascontiguousarray(sinks, dtype=np.float64)
+    out = np.empty((nq, hq, dv), dtype=np.float64)
+    lse = np.empty((nq, hq), dtype=np.float64) if want_lse else None
+    psink = np.empty((nq, hq), dtype=np.float64) if want_psink else None
+    _load().oracle_attention(_ptr(q), _ptr(q_pos), nq, _ptr(k), int(k_rotated), _ptr(k_pos), nk,
+                             _ptr(v), hq, hkv, dqk, dv, rope_dim, float(base), _ptr(s),
+                             int(window), float(softmax_scale), float(v_scale),
+                             _ptr(out), _ptr(lse), _ptr(psink), int(n_threads))
+    res = [out]
+    if want_lse:
+        res.append(lse)
+    if want_psink:
+        res.append(psink)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def prefill_swa(q, k, v, sinks, *, pos0: int = 0, window: int = SWA_WINDOW, base: float = SWA_BASE,
+                rows=None, want_lse: bool = False, n_threads: int = 0):
+    """Sliding-window prefill of a batch: q [B,T,Hq,192], k/v [B,T,Hkv,*], token t at pos0+t.
+
+    rows: optional array of token indices to evaluate (same for every batch entry).
+    Returns out [B,len(rows),Hq,128] (and lse [B,len(rows),Hq])."""
+    B, T = q.shape[:2]
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    kpos = pos0 + np.arange(T, dtype=np.int64)
+    outs, lses = [], []
+    for b in range(B):
+        # keys that any selected row can see: [min(rows)-window+1, max(rows)]
+        lo = max(0, int(rows.min()) - window + 1) if len(rows) else 0
+        hi = int(rows.max()) + 1 if len(rows) else 0
+        r = attention(q[b, rows], pos0 + rows, k[b, lo:hi], kpos[lo:hi], v[b, lo:hi],
+                      sinks=sinks, window=window, base=base, want_lse=want_lse, n_threads=n_threads)
+        if want_lse:
+            outs.append(r[0]); lses.append(r[1])
+        else:
+            outs.append(r)
+    out = np.stack(outs)
+    return (out, np.stack(lses)) if want_lse else out
+
+
+def prefill_global(q, k, v, *, q_pos0: int = 0, base: float = GLOBAL_BASE, rows=None,
+                   want_lse: bool = False, n_threads: int = 0):
+    """Causal prefill: q [B,Tq,Hq,192] at positions q_pos0.., k/v [B,Tk,Hkv,*] at 0..Tk-1."""
+    B, Tq = q.shape[:2]
+    rows = np.arange(Tq) if rows is None else np.asarray(rows, dtype=np.int64)
+    hi = q_pos0 + (int(rows.max()) + 1 if len(rows) else 0)
+    kpos = np.arange(hi, dtype=np.int64)
+    outs, lses = [], []
+    for b in range(B):
+        r = attention(q[b, rows], q_pos0 + rows, k[b, :hi], kpos, v[b, :hi],
+                      window=0, base=base, want_lse=want_lse, n_threads=n_threads)
+        if want_lse:
+            outs.append(r[0]); lses.append(r[1])
+        else:
+            outs.append(r)
+    out = np.stack(outs)
+    return (out, np.stack(lses)) if want_lse else out
+
+
+def cache_slots(p: int, cap: int, window: int):
+    """Cache rule: the token at position t lives in slot t mod cap.  A query at
+    position p sees positions max(0, p-window+1)..p (window > 0) or 0..p."""
+    lo = max(0, p - window + 1) if window > 0 else 0
+    tpos = np.arange(lo, p + 1, dtype=np.int64)
+    return tpos % cap, tpos
+
+
+def decode(q, q_pos, k_cache, v_cache, *, sinks=None, window: int, base: float,
+           seqs=None, n_threads: int = 0):
+    """One query per sequence over a post-RoPE KV cache [S,cap,Hkv,*].
+
+    q [S,Hq,192] unrotated.  Returns out [len(seqs),Hq,128] fp64."""
+    S = q.shape[0]
+    cap = k_cache.shape[1]
+    seqs = range(S) if seqs is None else seqs
+    outs = []
+    for s in seqs:
+        p = int(q_pos[s])
+        slots, tpos = cache_slots(p, cap, window)
+        outs.append(attention(q[s:s + 1], np.array([p]), k_cache[s, slots], tpos, v_cache[s, slots],
+                              sinks=sinks, window=window, base=base, k_rotated=True,
+                              n_threads=n_threads)[0])
+    return np.stack(outs)
+
+
+def kv_ring_append_rows(k_new, v_new, pos, base: float):
+    """What the append writes: rope(k_new) at pos and v_new unchanged, fp64."""
+    return rope_partial(k_new, pos, base), v_new

@@ -1,0 +1,184 @@
+/*
+ * fp64 CPU oracle for the MiMo-V2.6-Flash attention layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path links, loads or calls
+ * this file; only the tests, the smoke check and the CPU-baseline leg of the
+ * benchmark do.  It shares no code, header, table or constant with the HIP
+ * library: every quantity below is computed here from its definition.
+ *
+ * What it computes (one query row r, query head h, KV head g = h / (Hq/Hkv)):
+ *
+ *   partial RoPE  — "Partial RoPE" on the model-techniques-map page: the head
+ *     vector is split into its first rope_dim dims, which rotate, and the rest,
+ *     which carry no position.  rope_dim = int(192 * 0.334) = 64.  The rotation
+ *     is the default (non-YaRN) RoPE of the Hugging Face modeling code that the
+ *     page cites (rope_type set to default), in its rotate-half form: dim i and dim
+ *     i + rope_dim/2 (i < rope_dim/2) rotate together by the angle
+ *     pos * base^(-2i/rope_dim).  Angles and cos/sin are fp64 (the Gaudi
+ *     recipe page, section on required fixes, builds its tables in float64
+ *     since the fastest frequency's angle is the position itself).
+ *
+ *   scores — s_j = softmax_scale * <rope(q_r), rope(k_j)> over the visible keys
+ *     j: pos(j) <= pos(r) and, on sliding-window layers, pos(r) - pos(j) < W
+ *     (W = 128 keys counting the query itself, the HF / Megatron-Bridge
+ *     convention in "Notable quirks" of the miles recipe page).
+ *
+ *   sink — "Learnable attention sink" on the techniques-map page: one logit per
+ *     query head joins the softmax as an extra column and is dropped after the
+ *     softmax, so it enlarges the normaliser and carries no value.  It is
+ *     compared with the already-scaled scores and is not scaled itself.
+ *
+ *   softmax — two passes: m = max(all s_j, sink), Z = sum exp(s_j - m) +
+ *     exp(sink - m); output o = v_scale * sum_j exp(s_j - m) v_j / Z with
+ *     v_scale = 0.707 (the value path's fixed scale, miles recipe page,
+ *     section 1, model introduction).
+ *     GQA: consecutive query heads share one KV head (repeat_kv).
+ *
+ * bf16 inputs are taken as exact values (bf16 -> fp64 is exact); nothing is
+ * rounded in between.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double bf16_value(uint16_t bits) {
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Rotate one head vector x[0..D) at position pos into y (fp64). */
+static void rope_one(const double *x, double *y, int D, int R, double base, int64_t pos) {
+    int half = R / 2;
+    for (int d = 0; d < D; ++d) y[d] = x[d];
+    for (int i = 0; i < half; ++i) {
+        double inv_freq = pow(base, -(double)(2 * i) / (double)R);
+        double angle = (double)pos * inv_freq;
+        double c = cos(angle), s = sin(angle);
+        y[i] = x[i] * c - x[i + half] * s;
+        y[i + half] = x[i + half] * c + x[i] * s;
+    }
+}
+
+/* x: [n_tok, n_heads, D] bf16 bits; out: same shape, fp64. */
+void oracle_rope_partial(const uint16_t *x, int64_t n_tok, int n_heads, int D, int R,
+                         const int64_t *pos, double base, double *out) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n_tok; ++t) {
+        double buf[1024];
+        for (int h = 0; h < n_heads; ++h) {
+            const uint16_t *src = x + ((size_t)t * n_heads + h) * D;
+            for (int d = 0; d < D; ++d) buf[d] = bf16_value(src[d]);
+            rope_one(buf, out + ((size_t)t * n_heads + h) * D, D, R, base, pos[t]);
+        }
+    }
+}
+
+static int visible(int64_t qp, int64_t kp, int64_t window) {
+    if (kp > qp) return 0;
+    if (window > 0 && qp - kp >= window) return 0;
+    return 1;
+}
+
+/*
+ * Attention rows.
+ *   q      [nq, Hq, Dqk] bf16 bits (unrotated), positions q_pos[nq]
+ *   k      [nk, Hkv, Dqk] bf16 bits, positions k_pos[nk]; k_rotated != 0 means
+ *          the values already carry their rotation (a decode cache)
+ *   v      [nk, Hkv, Dv] bf16 bits
+ *   sinks  [Hq] or NULL
+ *   window 0 = causal over every earlier key, > 0 = keys with qp-kp < window
+ * Outputs (fp64): out [nq, Hq, Dv]; lse [nq, Hq] = log(sum exp(s_j) + exp(sink))
+ * and psink [nq, Hq] = exp(sink)/that sum, each optional (NULL).
+ * A row with no visible key and no sink gets o = 0, lse = -inf.
+ */
+void oracle_attention(const uint16_t *q, const int64_t *q_pos, int64_t nq,
+                      const uint16_t *k, int k_rotated, const int64_t *k_pos, int64_t nk,
+                      const uint16_t *v, int Hq, int Hkv, int Dqk, int Dv, int R,
+                      double base, const double *sinks, int64_t window,
+                      double softmax_scale, double v_scale,
+                      double *out, double *lse, double *psink, int n_threads) {
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+    int group = Hq / Hkv;
+
+    /* Step 1: every key, rotated once, as fp64. */
+    double *kr = (double *)malloc((size_t)nk * Hkv * Dqk * sizeof(double));
+    #pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < nk; ++j) {
+        double buf[1024];
+        for (int g = 0; g < Hkv; ++g) {
+            const uint16_t *src = k + ((size_t)j * Hkv + g) * Dqk;
+            double *dst = kr + ((size_t)j * Hkv + g) * Dqk;
+            for (int d = 0; d < Dqk; ++d) buf[d] = bf16_value(src[d]);
+            if (k_rotated) memcpy(dst, buf, Dqk * sizeof(double));
+            else rope_one(buf, dst, Dqk, R, base, k_pos[j]);
+        }
+    }
+
+    /* Step 2: each (row, head) independently. */
+    #pragma omp parallel
+    {
+        double *scores = (double *)malloc((size_t)(nk > 0 ? nk : 1) * sizeof(double));
+        int64_t *keys = (int64_t *)malloc((size_t)(nk > 0 ? nk : 1) * sizeof(int64_t));
+        double qraw[1024], qrot[1024], acc[1024];
+        #pragma omp for schedule(dynamic, 1)
+        for (int64_t idx = 0; idx < nq * Hq; ++idx) {
+            int64_t r = idx / Hq;
+            int h = (int)(idx % Hq);
+            int g = h / group;
+            const uint16_t *qs = q + ((size_t)r * Hq + h) * Dqk;
+            for (int d = 0; d < Dqk; ++d) qraw[d] = bf16_value(qs[d]);
+            rope_one(qraw, qrot, Dqk, R, base, q_pos[r]);
+
+            int64_t n = 0;
+            for (int64_t j = 0; j < nk; ++j) {
+                if (!visible(q_pos[r], k_pos[j], window)) continue;
+                const double *kj = kr + ((size_t)j * Hkv + g) * Dqk;
+                double dot = 0.0;
+                for (int d = 0; d < Dqk; ++d) dot += qrot[d] * kj[d];
+                scores[n] = softmax_scale * dot;
+                keys[n] = j;
+                ++n;
+            }
+
+            /* pass 1: the largest logit, the sink column included */
+            double m = -INFINITY;
+            for (int64_t t = 0; t < n; ++t) if (scores[t] > m) m = scores[t];
+            if (sinks && sinks[h] > m) m = sinks[h];
+
+            double *o = out + ((size_t)r * Hq + h) * Dv;
+            if (m == -INFINITY) {
+                for (int d = 0; d < Dv; ++d) o[d] = 0.0;
+                if (lse) lse[r * Hq + h] = -INFINITY;
+                if (psink) psink[r * Hq + h] = 0.0;
+                continue;
+            }
+            /* pass 2: normaliser and weighted values */
+            double z = 0.0;
+            for (int d = 0; d < Dv; ++d) acc[d] = 0.0;
+            for (int64_t t = 0; t < n; ++t) {
+                double p = exp(scores[t] - m);
+                z += p;
+                const uint16_t *vj = v + ((size_t)keys[t] * Hkv + g) * Dv;
+                for (int d = 0; d < Dv; ++d) acc[d] += p * bf16_value(vj[d]);
+            }
+            double zsink = sinks ? exp(sinks[h] - m) : 0.0;
+            z += zsink;
+            for (int d = 0; d < Dv; ++d) o[d] = v_scale * acc[d] / z;
+            if (lse) lse[r * Hq + h] = m + log(z);
+            if (psink) psink[r * Hq + h] = zsink / z;
+        }
+        free(scores);
+        free(keys);
+    }
+    free(kr);
+}
