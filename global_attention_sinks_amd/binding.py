@@ -1,0 +1,171 @@
+"""Thin Python binding of libmimo_attn.so (argument marshalling only).
+
+Functions carry the C ABI's names and take torch tensors on the GPU: bf16
+tensors for q/k/v/out/caches, int64 for positions, float32 for sinks / lse.
+Each call passes data_ptr()s and torch's current HIP stream to the library;
+every step of the computation runs in the library's kernels.  There is no
+fallback: if the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmimo_attn.so")
+
+MIMO_OK = 0
+_STATUS = {1: "MIMO_ERR_INVALID_ARGUMENT", 2: "MIMO_ERR_UNSUPPORTED", 3: "MIMO_ERR_WORKSPACE",
+           4: "MIMO_ERR_HIP"}
+
+
+class MimoAttnCfg(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim_qk", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+                ("rope_dim", ctypes.c_int32), ("rope_base", ctypes.c_double),
+                ("softmax_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+                ("window", ctypes.c_int32)]
+
+
+def swa_cfg(window: int = 128) -> MimoAttnCfg:
+    """Sliding-window layer: 64 q heads / 8 KV heads, base 1e4, window 128."""
+    return MimoAttnCfg(64, 8, 192, 128, 64, 1.0e4, 1.0 / math.sqrt(192.0), 0.707, window)
+
+
+def global_cfg() -> MimoAttnCfg:
+    """Global layer: 64 q heads / 4 KV heads, base 1e7, no window."""
+    return MimoAttnCfg(64, 4, 192, 128, 64, 1.0e7, 1.0 / math.sqrt(192.0), 0.707, 0)
+
+
+class MimoError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the built library (it is never built implicitly here)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with global_attention_sinks_amd.build.build()")
+    lib = ctypes.CDLL(path)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    C = ctypes.POINTER(MimoAttnCfg)
+    lib.mimo_rope_partial.argtypes = [C, P, P, I64, I32, P, P]
+    lib.mimo_attn_prefill_swa.argtypes = [C, P, P, P, P, I32, I32, I64, P, P, P]
+    lib.mimo_attn_prefill_global.argtypes = [C, P, P, P, I32, I32, I32, I64, P, P, P]
+    lib.mimo_attn_decode.argtypes = [C, I32, P, P, P, P, I32, P, P, P, ctypes.c_size_t, P]
+    lib.mimo_attn_decode_workspace_size.argtypes = [C, I32, I32]
+    lib.mimo_attn_decode_workspace_size.restype = ctypes.c_size_t
+    lib.mimo_kv_ring_append.argtypes = [C, I32, P, P, P, P, P, I32, P]
+    lib.mimo_last_error.restype = ctypes.c_char_p
+    for fn in ("mimo_rope_partial", "mimo_attn_prefill_swa", "mimo_attn_prefill_global",
+               "mimo_attn_decode", "mimo_kv_ring_append"):
+        getattr(lib, fn).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != MIMO_OK:
+        raise MimoError(fn, status, _lib.mimo_last_error().decode())
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, dtype, name, ndim=None):
+    if t is None:
+        return
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def mimo_rope_partial(cfg: MimoAttnCfg, x_in, x_out, pos, stream=None):
+    """x_in/x_out [n_tokens, n_heads, 192] bf16 (may be the same tensor), pos [n_tokens] int64."""
+    lib = load_library()
+    _need(x_in, torch.bfloat16, "x_in", 3); _need(x_out, torch.bfloat16, "x_out", 3)
+    _need(pos, torch.int64, "pos", 1)
+    n, h, _ = x_in.shape
+    _check("mimo_rope_partial", lib.mimo_rope_partial(ctypes.byref(cfg), _p(x_in), _p(x_out), n, h,
+                                                      _p(pos), _stream(stream)))
+    return x_out
+
+
+def mimo_attn_prefill_swa(cfg: MimoAttnCfg, q, k, v, sinks, out, pos0: int = 0, lse=None, stream=None):
+    """q [B,T,Hq,192], k [B,T,Hkv,192], v [B,T,Hkv,128], sinks [Hq] f32 or None, out [B,T,Hq,128]."""
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, torch.bfloat16, n, 4)
+    _need(sinks, torch.float32, "sinks", 1); _need(lse, torch.float32, "lse", 3)
+    B, T = q.shape[:2]
+    _check("mimo_attn_prefill_swa",
+           lib.mimo_attn_prefill_swa(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(sinks), B, T, pos0,
+                                     _p(out), _p(lse), _stream(stream)))
+    return out
+
+
+def mimo_attn_prefill_global(cfg: MimoAttnCfg, q, k, v, out, q_pos0: int = 0, lse=None, stream=None):
+    """q [B,Tq,Hq,192] at positions q_pos0.., k/v [B,Tk,Hkv,*] at 0..Tk-1, Tk = q_pos0 + Tq."""
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, torch.bfloat16, n, 4)
+    _need(lse, torch.float32, "lse", 3)
+    B, Tq = q.shape[:2]
+    Tk = k.shape[1]
+    _check("mimo_attn_prefill_global",
+           lib.mimo_attn_prefill_global(ctypes.byref(cfg), _p(q), _p(k), _p(v), B, Tq, Tk, q_pos0,
+                                        _p(out), _p(lse), _stream(stream)))
+    return out
+
+
+def mimo_attn_decode_workspace_size(cfg: MimoAttnCfg, S: int, cap: int) -> int:
+    return int(load_library().mimo_attn_decode_workspace_size(ctypes.byref(cfg), S, cap))
+
+
+def mimo_attn_decode(cfg: MimoAttnCfg, q, q_pos, k_cache, v_cache, sinks, out, ws=None, stream=None):
+    """q [S,Hq,192], q_pos [S] int64, caches [S,cap,Hkv,192|128], out [S,Hq,128].
+
+    ws: a device tensor of at least mimo_attn_decode_workspace_size bytes (any dtype)."""
+    lib = load_library()
+    _need(q, torch.bfloat16, "q", 3); _need(out, torch.bfloat16, "out", 3)
+    _need(k_cache, torch.bfloat16, "k_cache", 4); _need(v_cache, torch.bfloat16, "v_cache", 4)
+    _need(q_pos, torch.int64, "q_pos", 1); _need(sinks, torch.float32, "sinks", 1)
+    S = q.shape[0]
+    cap = k_cache.shape[1]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("mimo_attn_decode",
+           lib.mimo_attn_decode(ctypes.byref(cfg), S, _p(q), _p(q_pos), _p(k_cache), _p(v_cache), cap,
+                                _p(sinks), _p(out), _p(ws), ws_bytes, _stream(stream)))
+    return out
+
+
+def mimo_kv_ring_append(cfg: MimoAttnCfg, k_new, v_new, pos, k_cache, v_cache, stream=None):
+    """k_new [S,Hkv,192], v_new [S,Hkv,128] unrotated; writes slot pos mod cap of the caches."""
+    lib = load_library()
+    _need(k_new, torch.bfloat16, "k_new", 3); _need(v_new, torch.bfloat16, "v_new", 3)
+    _need(k_cache, torch.bfloat16, "k_cache", 4); _need(v_cache, torch.bfloat16, "v_cache", 4)
+    _need(pos, torch.int64, "pos", 1)
+    S = k_new.shape[0]
+    cap = k_cache.shape[1]
+    _check("mimo_kv_ring_append",
+           lib.mimo_kv_ring_append(ctypes.byref(cfg), S, _p(k_new), _p(v_new), _p(pos), _p(k_cache),
+                                   _p(v_cache), cap, _stream(stream)))
+    return k_cache, v_cache

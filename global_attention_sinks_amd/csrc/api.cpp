@@ -1,0 +1,204 @@
+// C ABI of the attention hot path: argument validation on the host, then one
+// or two kernel launches on the caller's stream.  No allocation, no host
+// synchronisation, no state beyond a thread-local error message.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/mimo_attn.h"
+#include "kernels.hpp"
+
+using namespace mimo;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mimo_status fail(mimo_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+mimo_status ok() {
+    g_err[0] = '\0';
+    return MIMO_OK;
+}
+
+mimo_status from_hip(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(MIMO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Shared checks of the layer configuration.
+mimo_status check_cfg(const mimo_attn_cfg *cfg) {
+    if (!cfg) return fail(MIMO_ERR_INVALID_ARGUMENT, "cfg is NULL");
+    if (cfg->num_q_heads <= 0 || cfg->num_kv_heads <= 0)
+        return fail(MIMO_ERR_INVALID_ARGUMENT, "head counts must be positive (got %d q, %d kv)",
+                    cfg->num_q_heads, cfg->num_kv_heads);
+    if (cfg->num_q_heads % cfg->num_kv_heads != 0)
+        return fail(MIMO_ERR_INVALID_ARGUMENT, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                    cfg->num_q_heads, cfg->num_kv_heads);
+    if (cfg->head_dim_qk != kDqk || cfg->head_dim_v != kDv || cfg->rope_dim != kRope)
+        return fail(MIMO_ERR_UNSUPPORTED, "head geometry qk=%d v=%d rope=%d is not 192/128/64",
+                    cfg->head_dim_qk, cfg->head_dim_v, cfg->rope_dim);
+    if (!(cfg->rope_base > 1.0) || !isfinite(cfg->rope_base))
+        return fail(MIMO_ERR_INVALID_ARGUMENT, "rope_base must be finite and > 1");
+    if (!(cfg->softmax_scale > 0.0f) || !isfinite(cfg->softmax_scale))
+        return fail(MIMO_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
+    if (!isfinite(cfg->v_scale)) return fail(MIMO_ERR_INVALID_ARGUMENT, "v_scale must be finite");
+    if (cfg->window < 0) return fail(MIMO_ERR_INVALID_ARGUMENT, "window must be >= 0");
+    return ok();
+}
+
+// Fixed-point rotary turns for a base, recomputed only when the base changes.
+const RopeTurns &rope_turns(double base) {
+    thread_local double cached_base = 0.0;
+    thread_local RopeTurns rt;
+    if (base != cached_base) {
+        const long double two_pi = 6.283185307179586476925286766559005768L;
+        for (int i = 0; i < kPairs; ++i) {
+            long double theta = powl((long double)base, -(long double)(2 * i) / (long double)kRope);
+            long double frac = theta / two_pi;           // in (0, 1/(2 pi)]
+            rt.turn[i] = (uint64_t)llroundl(ldexpl(frac, 64));
+        }
+        cached_base = base;
+    }
+    return rt;
+}
+
+float scale_log2(const mimo_attn_cfg *cfg) { return cfg->softmax_scale * 1.4426950408889634f; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    const char *pa = (const char *)a, *pb = (const char *)b;
+    return pa < pb + nb && pb < pa + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mimo_last_error(void) { return g_err; }
+
+mimo_status mimo_rope_partial(const mimo_attn_cfg *cfg, const uint16_t *x_in, uint16_t *x_out,
+                              int64_t n_tokens, int32_t n_heads, const int64_t *pos, void *stream) {
+    mimo_status st = check_cfg(cfg);
+    if (st != MIMO_OK) return st;
+    if (n_tokens < 0 || n_heads <= 0)
+        return fail(MIMO_ERR_INVALID_ARGUMENT, "n_tokens must be >= 0 and n_heads > 0");
+    if (n_tokens == 0) return ok();
+    if (!x_in || !x_out || !pos) return fail(MIMO_ERR_INVALID_ARGUMENT, "x_in, x_out and pos must be non-NULL");
+    const size_t bytes = (size_t)n_tokens * n_heads * kDqk * 2;
+    if (x_in != x_out && overlap(x_in, bytes, x_out, bytes))
+        return fail(MIMO_ERR_INVALID_ARGUMENT, "x_out must equal x_in or not overlap it");
+    return from_hip(launch_rope_partial(rope_turns(cfg->rope_base), x_in, x_out,
+                                        n_tokens * (int64_t)n_heads, n_heads, pos,
+                                        (hipStream_t)stream),
+                    "rope_partial launch");
+}
+
+static mimo_status prefill_common(const mimo_attn_cfg *cfg, const uint16_t *q, const uint16_t *k,
+                                  const uint16_t *v, uint16_t *out, int32_t B, int32_t Tq,
+                                  int32_t Tk) {
+    mimo_status st = check_cfg(cfg);
+    if (st != MIMO_OK) return st;
+    if (B < 0 || Tq < 0 || Tk < 0) return fail(MIMO_ERR_INVALID_ARGUMENT, "sizes must be >= 0");
+    if ((cfg->num_q_heads / cfg->num_kv_heads) % 4 != 0)
+        return fail(MIMO_ERR_UNSUPPORTED, "prefill needs a GQA group size that is a multiple of 4 (got %d)",
+                    cfg->num_q_heads / cfg->num_kv_heads);
+    if (B == 0 || Tq == 0) return ok();
+    if (!q || !k || !v || !out) return fail(MIMO_ERR_INVALID_ARGUMENT, "q, k, v and out must be non-NULL");
+    return ok();
+}
+
+mimo_status mimo_attn_prefill_swa(const mimo_attn_cfg *cfg, const uint16_t *q, const uint16_t *k,
+                                  const uint16_t *v, const float *sinks, int32_t B, int32_t T,
+                                  int64_t pos0, uint16_t *out, float *lse, void *stream) {
+    mimo_status st = prefill_common(cfg, q, k, v, out, B, T, T);
+    if (st != MIMO_OK) return st;
+    if (cfg->window < 1) return fail(MIMO_ERR_INVALID_ARGUMENT, "sliding-window prefill needs window >= 1");
+    if (pos0 < 0) return fail(MIMO_ERR_INVALID_ARGUMENT, "pos0 must be >= 0");
+    if (B == 0 || T == 0) return ok();
+    PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.sinks = sinks;
+    a.B = B; a.Tq = T; a.Tk = T; a.Hq = cfg->num_q_heads; a.Hkv = cfg->num_kv_heads;
+    a.q_pos0 = pos0; a.k_pos0 = pos0; a.window = cfg->window;
+    a.scale_log2 = scale_log2(cfg); a.v_scale = cfg->v_scale;
+    a.rt = rope_turns(cfg->rope_base);
+    return from_hip(launch_prefill(a, (hipStream_t)stream), "prefill_swa launch");
+}
+
+mimo_status mimo_attn_prefill_global(const mimo_attn_cfg *cfg, const uint16_t *q, const uint16_t *k,
+                                     const uint16_t *v, int32_t B, int32_t Tq, int32_t Tk,
+                                     int64_t q_pos0, uint16_t *out, float *lse, void *stream) {
+    mimo_status st = prefill_common(cfg, q, k, v, out, B, Tq, Tk);
+    if (st != MIMO_OK) return st;
+    if (cfg->window != 0) return fail(MIMO_ERR_INVALID_ARGUMENT, "global prefill needs window == 0");
+    if (q_pos0 < 0) return fail(MIMO_ERR_INVALID_ARGUMENT, "q_pos0 must be >= 0");
+    if ((int64_t)Tk != q_pos0 + Tq)
+        return fail(MIMO_ERR_INVALID_ARGUMENT, "Tk (%d) must equal q_pos0 + Tq (%lld)", Tk,
+                    (long long)(q_pos0 + Tq));
+    if (B == 0 || Tq == 0) return ok();
+    PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.sinks = nullptr;
+    a.B = B; a.Tq = Tq; a.Tk = Tk; a.Hq = cfg->num_q_heads; a.Hkv = cfg->num_kv_heads;
+    a.q_pos0 = q_pos0; a.k_pos0 = 0; a.window = 0;
+    a.scale_log2 = scale_log2(cfg); a.v_scale = cfg->v_scale;
+    a.rt = rope_turns(cfg->rope_base);
+    return from_hip(launch_prefill(a, (hipStream_t)stream), "prefill_global launch");
+}
+
+size_t mimo_attn_decode_workspace_size(const mimo_attn_cfg *cfg, int32_t S, int32_t cap) {
+    if (!cfg || S <= 0 || cap <= 0 || cfg->num_q_heads <= 0) return 0;
+    return decode_workspace_bytes(S, cfg->num_q_heads, cap);
+}
+
+mimo_status mimo_attn_decode(const mimo_attn_cfg *cfg, int32_t S, const uint16_t *q,
+                             const int64_t *q_pos, const uint16_t *k_cache, const uint16_t *v_cache,
+                             int32_t cap, const float *sinks, uint16_t *out, void *ws,
+                             size_t ws_bytes, void *stream) {
+    mimo_status st = check_cfg(cfg);
+    if (st != MIMO_OK) return st;
+    if (S < 0 || cap < 1) return fail(MIMO_ERR_INVALID_ARGUMENT, "S must be >= 0 and cap >= 1");
+    const int G = cfg->num_q_heads / cfg->num_kv_heads;
+    if (G > 16) return fail(MIMO_ERR_UNSUPPORTED, "decode needs a GQA group size <= 16 (got %d)", G);
+    if (cfg->window > 0 && cap < cfg->window)
+        return fail(MIMO_ERR_INVALID_ARGUMENT, "a ring cache needs cap (%d) >= window (%d)", cap, cfg->window);
+    if ((int64_t)S * cfg->num_kv_heads > 65535)
+        return fail(MIMO_ERR_UNSUPPORTED, "S * num_kv_heads must be <= 65535");
+    if (S == 0) return ok();
+    if (!q || !q_pos || !k_cache || !v_cache || !out)
+        return fail(MIMO_ERR_INVALID_ARGUMENT, "q, q_pos, k_cache, v_cache and out must be non-NULL");
+    const size_t need = decode_workspace_bytes(S, cfg->num_q_heads, cap);
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(MIMO_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu)", need,
+                    ws ? ws_bytes : (size_t)0);
+    DecodeArgs a{};
+    a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.pos = q_pos; a.sinks = sinks; a.out = out;
+    a.ws_o = (float *)ws; a.ws_ml = nullptr;
+    a.S = S; a.Hq = cfg->num_q_heads; a.Hkv = cfg->num_kv_heads; a.cap = cap; a.window = cfg->window;
+    a.scale_log2 = scale_log2(cfg); a.v_scale = cfg->v_scale;
+    a.rt = rope_turns(cfg->rope_base);
+    return from_hip(launch_decode(a, (hipStream_t)stream), "decode launch");
+}
+
+mimo_status mimo_kv_ring_append(const mimo_attn_cfg *cfg, int32_t S, const uint16_t *k_new,
+                                const uint16_t *v_new, const int64_t *pos, uint16_t *k_cache,
+                                uint16_t *v_cache, int32_t cap, void *stream) {
+    mimo_status st = check_cfg(cfg);
+    if (st != MIMO_OK) return st;
+    if (S < 0 || cap < 1) return fail(MIMO_ERR_INVALID_ARGUMENT, "S must be >= 0 and cap >= 1");
+    if ((int64_t)S * cfg->num_kv_heads > 0x7fffffff)
+        return fail(MIMO_ERR_UNSUPPORTED, "S * num_kv_heads is too large");
+    if (S == 0) return ok();
+    if (!k_new || !v_new || !pos || !k_cache || !v_cache)
+        return fail(MIMO_ERR_INVALID_ARGUMENT, "k_new, v_new, pos, k_cache and v_cache must be non-NULL");
+    return from_hip(launch_kv_ring_append(rope_turns(cfg->rope_base), S, cfg->num_kv_heads, k_new,
+                                          v_new, pos, k_cache, v_cache, cap, (hipStream_t)stream),
+                    "kv_ring_append launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,401 @@
+// Prefill attention for both layer types of MiMo-V2.6-Flash on gfx950.
+//
+// Sliding-window layers: 64 query heads over 8 KV heads, a 128-key window and a
+// per-head sink (techniques map page, rows Sliding-window attention, Learnable
+// attention sink, Grouped-query attention).  Global layers: 64 over 4 KV heads,
+// full causal attention, run one query chunk at a time against its whole
+// prefix (Gaudi recipe page, Launch section: tiled global prefill).
+//
+// Design (one workgroup = NW query heads of one GQA group x 32*NB query tokens;
+// one wave per head):
+//   * S^T = K Q^T and O^T = V^T P^T on 32x32x16 bf16 MFMA.  With keys on the
+//     MFMA's M side, every lane owns one query column, so the row max / row sum
+//     of the softmax are in-lane plus one permlane32 swap.
+//   * Q lives in registers for the whole kernel (B operand), rotated once on
+//     load.  Each K/V tile of 64 keys is staged once per workgroup in LDS and
+//     read by all NW heads: K rotated on its way in (fused RoPE), V transposed
+//     on its way in (the PV contraction runs over keys).
+//   * K rows are read from LDS in a bit-permuted order (bits 2 and 3 of the row
+//     swapped) so that the S^T accumulator registers of a lane hold 8
+//     consecutive keys, which are exactly its P^T operand for the PV MFMA, with
+//     no data movement between the two products.
+//   * Online softmax in the exp2 domain with the sink folded in as the initial
+//     (max, sum) = (sink * log2 e, 1); the running max is only raised when it
+//     grows by more than 2^8, which keeps every exponent <= 2^8.
+//   * Tiles wholly outside the causal band are never visited; only edge tiles
+//     evaluate the mask.  Workgroups are mapped XCD-aware (each XCD streams the
+//     K/V of one set of KV heads) and longest-first for causal balance.
+#include "kernels.hpp"
+
+namespace mimo {
+
+namespace {
+
+constexpr int NK = 64;                  // keys per tile
+constexpr int KSTR = kDqk + 8;          // LDS row stride of a K tile (bf16)
+constexpr int VSTR = NK + 8;            // LDS row stride of a V^T tile (bf16)
+constexpr int K_TILE = NK * KSTR;
+constexpr int V_TILE = kDv * VSTR;
+constexpr int STAGE = K_TILE + V_TILE;  // elements per pipeline stage
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 lds128(const uint16_t *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+}  // namespace
+
+template <int NB, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
+                          amdgpu_waves_per_eu(NB == 2 ? 1 : 2, NB == 2 ? 1 : 2)))
+void prefill_kernel(PrefillArgs a) {
+    constexpr int QW = 32 * NB;
+    constexpr int NT = 64 * NW;
+    constexpr int ROT_PER = (NK * 4 + NT - 1) / NT;      // rotating K chunk pairs per thread
+    constexpr int PLAIN_PER = (NK * 16 + NT - 1) / NT;   // pass-through K chunks per thread
+    constexpr int V_PER = (NK * 4 + NT - 1) / NT;        // 4-key x 8-dv V blocks per thread
+
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int h2 = lane >> 5, l32 = lane & 31;
+
+    // ---- which (query block, batch, KV head, head group) this workgroup owns
+    const int combos = a.B * a.Hkv * a.n_hgrp;
+    int qb, c;
+    {
+        const int i = blockIdx.x;
+        if (a.xcd_remap) {
+            const int x = i & 7, j = i >> 3, cpx = combos >> 3;
+            qb = a.n_qblk - 1 - j / cpx;
+            c = x * cpx + j % cpx;
+        } else {
+            qb = a.n_qblk - 1 - i / combos;
+            c = i % combos;
+        }
+    }
+    const int hg = c % a.n_hgrp;
+    const int bg = c / a.n_hgrp;
+    const int g = bg % a.Hkv;
+    const int b = bg / a.Hkv;
+    const int G = a.Hq / a.Hkv;
+    const int head = g * G + hg * NW + w;
+    const int q0 = qb * QW;
+
+    const size_t krow_stride = (size_t)a.Hkv * kDqk;
+    const size_t vrow_stride = (size_t)a.Hkv * kDv;
+    const uint16_t *kbase = a.k + (size_t)b * a.Tk * krow_stride + (size_t)g * kDqk;
+    const uint16_t *vbase = a.v + (size_t)b * a.Tk * vrow_stride + (size_t)g * kDv;
+
+    // ---- key range of the block
+    const int t_last = min(q0 + QW, a.Tq) - 1;
+    const int64_t qp_lo = a.q_pos0 + q0;
+    const int64_t qp_hi = a.q_pos0 + t_last;
+    int64_t jlo = 0;
+    if (a.window > 0) jlo = qp_lo - a.window + 1 - a.k_pos0;
+    if (jlo < 0) jlo = 0;
+    int64_t jhi = qp_hi - a.k_pos0;
+    if (jhi > a.Tk - 1) jhi = a.Tk - 1;
+    const int tile_lo = (int)(jlo / NK);
+    const int tile_hi = jhi >= jlo ? (int)(jhi / NK) : tile_lo - 1;
+
+    // ---- Q in registers (B operand): lane holds dims [96*h2, 96*h2+96) of one query
+    u32x4 qr[NB][12];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int t = q0 + 32 * nb + l32;
+        if (t < a.Tq) {
+            const uint16_t *src = a.q + (((size_t)b * a.Tq + t) * a.Hq + head) * kDqk + 96 * h2;
+#pragma unroll
+            for (int ks = 0; ks < 12; ++ks) qr[nb][ks] = ldg128(src + 8 * ks);
+            if (h2 == 0) {
+                const int64_t qp = a.q_pos0 + t;
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) rope_rotate8(qr[nb][cc], qr[nb][cc + 4], a.rt, 8 * cc, qp);
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 12; ++ks) qr[nb][ks] = u32x4{0, 0, 0, 0};
+        }
+    }
+
+    // ---- softmax state per query column
+    float m_run[NB], l_run[NB];
+    {
+        const float m0 = a.sinks ? a.sinks[head] * kLog2e : kNegInf;
+        const float l0 = (a.sinks && h2 == 0) ? 1.0f : 0.0f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) { m_run[nb] = m0; l_run[nb] = l0; }
+    }
+    f32x16 O[4][NB];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) O[mb][nb][e] = 0.0f;
+
+    // ---- staging registers for the next tile
+    u32x4 k_rot[ROT_PER][2], k_pl[PLAIN_PER], v_st[V_PER][4];
+
+    auto load_tile = [&](int jt) {
+        const int j0 = jt * NK;
+#pragma unroll
+        for (int r = 0; r < ROT_PER; ++r) {
+            const int u = tid + r * NT;
+            const int row = u >> 2, cc = u & 3;
+            const int j = j0 + row;
+            if (u < NK * 4 && j < a.Tk) {
+                const uint16_t *p = kbase + (size_t)j * krow_stride + 8 * cc;
+                k_rot[r][0] = ldg128(p);
+                k_rot[r][1] = ldg128(p + 32);
+            } else {
+                k_rot[r][0] = u32x4{0, 0, 0, 0};
+                k_rot[r][1] = u32x4{0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < PLAIN_PER; ++r) {
+            const int u = tid + r * NT;
+            const int row = u >> 4, cc = 8 + (u & 15);
+            const int j = j0 + row;
+            k_pl[r] = (u < NK * 16 && j < a.Tk) ? ldg128(kbase + (size_t)j * krow_stride + 8 * cc)
+                                                : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int r = 0; r < V_PER; ++r) {
+            const int u = tid + r * NT;
+            const int kg = u >> 4, cc = u & 15;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int j = j0 + 4 * kg + rr;
+                v_st[r][rr] = (u < NK * 4 && j < a.Tk)
+                                  ? ldg128(vbase + (size_t)j * vrow_stride + 8 * cc)
+                                  : u32x4{0, 0, 0, 0};
+            }
+        }
+    };
+
+    auto store_tile = [&](int jt, int buf) {
+        uint16_t *Ks = smem + buf * STAGE;
+        uint16_t *Vs = Ks + K_TILE;
+        const int j0 = jt * NK;
+#pragma unroll
+        for (int r = 0; r < ROT_PER; ++r) {
+            const int u = tid + r * NT;
+            if (u < NK * 4) {
+                const int row = u >> 2, cc = u & 3;
+                u32x4 x = k_rot[r][0], y = k_rot[r][1];
+                rope_rotate8(x, y, a.rt, 8 * cc, a.k_pos0 + j0 + row);
+                *reinterpret_cast<u32x4 *>(Ks + row * KSTR + 8 * cc) = x;
+                *reinterpret_cast<u32x4 *>(Ks + row * KSTR + 8 * cc + 32) = y;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < PLAIN_PER; ++r) {
+            const int u = tid + r * NT;
+            if (u < NK * 16) {
+                const int row = u >> 4, cc = 8 + (u & 15);
+                *reinterpret_cast<u32x4 *>(Ks + row * KSTR + 8 * cc) = k_pl[r];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < V_PER; ++r) {
+            const int u = tid + r * NT;
+            if (u < NK * 4) {
+                const int kg = u >> 4, cc = u & 15;
+                // 4 keys x 8 dv -> 8 dv rows of 4 keys
+#pragma unroll
+                for (int d = 0; d < 8; ++d) {
+                    const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
+                    u32x2 o;
+                    o[0] = __builtin_amdgcn_perm(v_st[r][1][d >> 1], v_st[r][0][d >> 1], sel);
+                    o[1] = __builtin_amdgcn_perm(v_st[r][3][d >> 1], v_st[r][2][d >> 1], sel);
+                    *reinterpret_cast<u32x2 *>(Vs + (8 * cc + d) * VSTR + 4 * kg) = o;
+                }
+            }
+        }
+    };
+
+    const float cl2 = a.scale_log2;
+    // K row read order: bits 2 and 3 of the row index swapped
+    const int prow = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+
+    if (tile_hi >= tile_lo) {
+        load_tile(tile_lo);
+        store_tile(tile_lo, 0);
+    }
+    __syncthreads();
+
+    for (int jt = tile_lo; jt <= tile_hi; ++jt) {
+        const int buf = (jt - tile_lo) & 1;
+        const bool has_next = jt < tile_hi;
+        if (has_next) load_tile(jt + 1);
+
+        const uint16_t *Ks = smem + buf * STAGE;
+        const uint16_t *Vs = Ks + K_TILE;
+        const int j0 = jt * NK;
+
+        // ---- S^T = K Q^T  (2 key blocks of 32 x NB query blocks of 32)
+        f32x16 S[2][NB];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) S[kb][nb][e] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < 12; ++ks) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const u32x4 kf = lds128(Ks + (32 * kb + prow) * KSTR + 96 * h2 + 8 * ks);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) S[kb][nb] = mfma32(kf, qr[nb][ks], S[kb][nb]);
+            }
+        }
+
+        // ---- mask on edge tiles only
+        const int64_t kp0 = a.k_pos0 + j0;
+        const bool full = (j0 + NK <= a.Tk) && (kp0 + NK - 1 <= qp_lo) &&
+                          (a.window == 0 || qp_hi - kp0 < a.window);
+        if (!full) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int64_t qp = a.q_pos0 + q0 + 32 * nb + l32;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int jrel = 32 * kb + 16 * (e >> 3) + 8 * h2 + (e & 7);
+                        const int64_t kp = kp0 + jrel;
+                        const bool vis = (j0 + jrel < a.Tk) && (kp <= qp) &&
+                                         (a.window == 0 || qp - kp < a.window);
+                        if (!vis) S[kb][nb][e] = kNegInf;
+                    }
+            }
+        }
+
+        // ---- online softmax (exp2 domain), lazy rescale
+        bool need[NB];
+        float mc[NB];
+        bool any_need = false;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            float mx = kNegInf;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, S[kb][nb][e]);
+            mx = max_xor32(mx);
+            mc[nb] = mx * cl2;
+            need[nb] = mc[nb] > m_run[nb] + 8.0f;
+            any_need |= need[nb];
+        }
+        if (__any(any_need)) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const float alpha = need[nb] ? __builtin_amdgcn_exp2f(m_run[nb] - mc[nb]) : 1.0f;
+                if (need[nb]) m_run[nb] = mc[nb];
+                l_run[nb] *= alpha;
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) O[mb][nb][e] *= alpha;
+            }
+        }
+        u32x4 P[2][2][NB];   // [kb][s][nb]
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const float mu = (m_run[nb] == kNegInf) ? 0.0f : m_run[nb];
+            float ls = 0.0f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][nb][e], cl2, -mu));
+                    S[kb][nb][e] = p;
+                    ls += p;
+                }
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+                        P[kb][s][nb][x] = pack_bf16(S[kb][nb][8 * s + 2 * x], S[kb][nb][8 * s + 2 * x + 1]);
+            }
+            l_run[nb] += ls;
+        }
+
+        // ---- O^T += V^T P^T
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const u32x4 vf = lds128(Vs + (32 * mb + l32) * VSTR + 32 * kb + 16 * s + 8 * h2);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) O[mb][nb] = mfma32(vf, P[kb][s][nb], O[mb][nb]);
+                }
+            }
+        }
+
+        if (has_next) store_tile(jt + 1, buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: o = v_scale * O / l, bf16
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const float lt = sum_xor32(l_run[nb]);
+        const int t = q0 + 32 * nb + l32;
+        if (t < a.Tq) {
+            const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
+            uint16_t *dst = a.out + (((size_t)b * a.Tq + t) * a.Hq + head) * kDv;
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    u32x2 o;
+                    o[0] = pack_bf16(O[mb][nb][4 * a4] * inv, O[mb][nb][4 * a4 + 1] * inv);
+                    o[1] = pack_bf16(O[mb][nb][4 * a4 + 2] * inv, O[mb][nb][4 * a4 + 3] * inv);
+                    *reinterpret_cast<u32x2 *>(dst + 32 * mb + 8 * a4 + 4 * h2) = o;
+                }
+            if (a.lse && h2 == 0)
+                a.lse[((size_t)b * a.Hq + head) * a.Tq + t] =
+                    lt > 0.0f ? (m_run[nb] + log2f(lt)) * kLn2 : kNegInf;
+        }
+    }
+}
+
+template <int NB, int NW>
+static hipError_t launch_variant(PrefillArgs a, hipStream_t stream) {
+    const int QW = 32 * NB;
+    const int G = a.Hq / a.Hkv;
+    a.n_qblk = (a.Tq + QW - 1) / QW;
+    a.n_hgrp = G / NW;
+    const int64_t combos = (int64_t)a.B * a.Hkv * a.n_hgrp;
+    const int64_t blocks = combos * a.n_qblk;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    a.xcd_remap = (combos % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL((prefill_kernel<NB, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, a);
+    return hipGetLastError();
+}
+
+#ifndef MIMO_PREFILL_NB
+#define MIMO_PREFILL_NB 2
+#endif
+
+hipError_t launch_prefill(PrefillArgs a, hipStream_t stream) {
+    // group sizes are multiples of 4 (checked by the caller)
+    if (MIMO_PREFILL_NB == 1 && (a.Hq / a.Hkv) % 8 == 0) return launch_variant<1, 8>(a, stream);
+    return launch_variant<2, 4>(a, stream);
+}
+
+}  // namespace mimo

@@ -68,13 +68,39 @@ def normal_bf16(seed: np.random.SeedSequence, shape) -> np.ndarray:
     return out.reshape(shape)
 
 
+def normal_bf16_slice(seed: np.random.SeedSequence, shape, lo: int, hi: int) -> np.ndarray:
+    """Elements [lo, hi) of the flattened normal_bf16(seed, shape), drawing only
+    the blocks that cover them."""
+    n = int(np.prod(shape))
+    assert 0 <= lo <= hi <= n
+    nblk = max(1, math.ceil(n / BLOCK))
+    kids = seed.spawn(nblk)
+    b0, b1 = lo // BLOCK, (hi + BLOCK - 1) // BLOCK
+    out = np.empty(hi - lo, dtype=np.uint16)
+
+    def fill(b):
+        blo, bhi = b * BLOCK, min(n, (b + 1) * BLOCK)
+        rng = np.random.Generator(np.random.PCG64(kids[b]))
+        vals = f32_to_bf16_bits(rng.standard_normal(bhi - blo, dtype=np.float32))
+        s0, s1 = max(lo, blo), min(hi, bhi)
+        out[s0 - lo:s1 - lo] = vals[s0 - blo:s1 - blo]
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, range(b0, b1)))
+    return out
+
+
 def normal_f32(seed: np.random.SeedSequence, shape) -> np.ndarray:
     rng = np.random.Generator(np.random.PCG64(seed))
     return rng.standard_normal(int(np.prod(shape)), dtype=np.float32).reshape(shape)
 
 
-def _children(seed: int):
+def children(seed: int):
+    """The five child seeds of a workload: q, k, v, sinks, positions."""
     return np.random.SeedSequence(seed).spawn(5)
+
+
+_children = children
 
 
 # Head layout of the two layer types (model facts, not method arithmetic).
@@ -141,6 +167,19 @@ def decode_inputs(S: int, cap: int, n_q_heads: int, n_kv_heads: int, seed: int,
         "q": q, "pos": pos, "k_cache": kc, "v_cache": vc,
         "sinks": normal_f32(cs, (n_q_heads,)) if with_sinks else None,
     }
+
+
+def global_prefill_chunk(T: int, n_q_heads: int, n_kv_heads: int, seed: int, t_lo: int, t_hi: int) -> dict:
+    """Query rows [t_lo, t_hi) of a B=1 prefill of T tokens and the keys/values
+    0..t_hi-1, drawn exactly as prefill_inputs(1, T, ...) would draw them."""
+    cq, ck, cv, _, _ = children(seed)
+    row_q, row_k, row_v = n_q_heads * D_QK, n_kv_heads * D_QK, n_kv_heads * D_V
+    q = normal_bf16_slice(cq, (1, T, n_q_heads, D_QK), t_lo * row_q, t_hi * row_q)
+    k = normal_bf16_slice(ck, (1, T, n_kv_heads, D_QK), 0, t_hi * row_k)
+    v = normal_bf16_slice(cv, (1, T, n_kv_heads, D_V), 0, t_hi * row_v)
+    return {"q": q.reshape(1, t_hi - t_lo, n_q_heads, D_QK),
+            "k": k.reshape(1, t_hi, n_kv_heads, D_QK),
+            "v": v.reshape(1, t_hi, n_kv_heads, D_V)}
 
 
 def append_inputs(S: int, n_kv_heads: int, seed: int, pos_lo: int, pos_hi: int) -> dict:

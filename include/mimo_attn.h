@@ -1,0 +1,157 @@
+/*
+ * mimo_attn.h — C ABI of the MiMo-V2.6-Flash attention hot path on MI355X (gfx950).
+ *
+ * The layer (miles MiMo-V2.6-Flash page, section 1 Model Introduction, and the
+ * Model techniques map page, rows Grouped-query attention, Sliding-window
+ * attention, Learnable attention sink, Partial RoPE):
+ *   - 64 query heads; sliding-window layers have 8 KV heads, a 128-key window
+ *     and one sink logit per query head; global layers have 4 KV heads, full
+ *     causal attention and no sink;
+ *   - q/k head dim 192, v head dim 128; the output is scaled by 0.707;
+ *   - partial RoPE rotates the first 64 of the 192 q/k dims (rotate-half
+ *     pairing: dim i with dim i+32), base 1e4 (sliding) or 1e7 (global);
+ *   - GQA: query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *
+ * For query position p and head h the library computes
+ *     s_j = softmax_scale * <rope(q, p), rope(k_j, pos_j)>   for visible keys j
+ *     visible: pos_j <= p and (window == 0 or p - pos_j < window)
+ *     o   = v_scale * sum_j exp(s_j) v_j / (sum_j exp(s_j) + exp(sink_h))
+ * where the sink term is present only when a sink array is given (it joins the
+ * normaliser and contributes no value: techniques map page, Learnable attention
+ * sink).  A row with no visible key and no sink gets o = 0.
+ *
+ * Conventions for every entry point
+ *   - bf16 tensors are passed as uint16_t bit patterns; all layouts are dense,
+ *     row-major, token-major: [batch or sequence, token or slot, head, dim].
+ *   - Every pointer is a DEVICE pointer owned by the caller, except cfg, which is
+ *     a host pointer read during the call only.  The library allocates nothing
+ *     and keeps no state between calls.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Success means the
+ *     work is enqueued on that stream; no call synchronises the host, so every
+ *     call can be captured into a HIP graph.
+ *   - All arguments are validated on the host before anything is enqueued.  On
+ *     error nothing is launched, outputs are untouched, and mimo_last_error()
+ *     returns a message (thread-local, valid until the thread's next call).
+ *   - Sizes of 0 (no tokens, no sequences) are valid and enqueue nothing.
+ *   - Supported head geometry: head_dim_qk 192, head_dim_v 128, rope_dim 64,
+ *     num_q_heads a multiple of num_kv_heads; prefill needs a GQA group size
+ *     (num_q_heads / num_kv_heads) that is a multiple of 4, decode a group
+ *     size of at most 16.  Anything else returns MIMO_ERR_UNSUPPORTED.
+ */
+#ifndef MIMO_ATTN_H
+#define MIMO_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mimo_status {
+    MIMO_OK = 0,
+    MIMO_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, inconsistent sizes */
+    MIMO_ERR_UNSUPPORTED = 2,      /* head geometry the kernels are not built for */
+    MIMO_ERR_WORKSPACE = 3,        /* decode workspace missing or too small */
+    MIMO_ERR_HIP = 4               /* the HIP runtime refused a launch */
+} mimo_status;
+
+/* Layer configuration (mirrors the model config keys). */
+typedef struct mimo_attn_cfg {
+    int32_t num_q_heads;   /* 64 */
+    int32_t num_kv_heads;  /* 8 on sliding-window layers, 4 on global layers */
+    int32_t head_dim_qk;   /* 192 */
+    int32_t head_dim_v;    /* 128 */
+    int32_t rope_dim;      /* 64: int(192 * 0.334), the first 64 dims rotate */
+    double rope_base;      /* 1e4 sliding, 1e7 global */
+    float softmax_scale;   /* 1/sqrt(192) */
+    float v_scale;         /* 0.707 */
+    int32_t window;        /* keys visible counting the query itself: 128; 0 = unbounded */
+} mimo_attn_cfg;
+
+/*
+ * Partial RoPE of a batch of head vectors (techniques map page, Partial RoPE;
+ * the angle of pair i is pos * rope_base^(-2i/rope_dim), computed by exact
+ * fixed-point turn reduction so it stays accurate at any position, which the
+ * Gaudi recipe page's section on required fixes shows an fp32 angle does not).
+ *   x_in, x_out : [n_tokens, n_heads, head_dim_qk] bf16; x_out may equal x_in
+ *                 (in place: then only the 64 rotated dims are rewritten).
+ *   pos         : [n_tokens] int64 positions, >= 0.
+ */
+mimo_status mimo_rope_partial(const mimo_attn_cfg *cfg, const uint16_t *x_in, uint16_t *x_out,
+                              int64_t n_tokens, int32_t n_heads, const int64_t *pos,
+                              void *stream);
+
+/*
+ * Sliding-window prefill with the per-head sink (techniques map page, rows
+ * Sliding-window attention and Learnable attention sink; window convention of
+ * the miles page, section 5.4 Notable quirks: window keys in total, the query
+ * included).  q/k are unrotated; RoPE is applied on load.
+ *   q     : [B, T, num_q_heads, 192]   token t has position pos0 + t
+ *   k     : [B, T, num_kv_heads, 192]  the same tokens as q
+ *   v     : [B, T, num_kv_heads, 128]
+ *   sinks : [num_q_heads] fp32 sink logits, or NULL for none
+ *   out   : [B, T, num_q_heads, 128] bf16
+ *   lse   : [B, num_q_heads, T] fp32 natural-log normaliser (sink included), or NULL
+ * Needs cfg->window >= 1.
+ */
+mimo_status mimo_attn_prefill_swa(const mimo_attn_cfg *cfg, const uint16_t *q, const uint16_t *k,
+                                  const uint16_t *v, const float *sinks, int32_t B, int32_t T,
+                                  int64_t pos0, uint16_t *out, float *lse, void *stream);
+
+/*
+ * Global causal prefill of one query chunk against its whole prefix (the tiled
+ * global-attention prefill of the Gaudi recipe page, Launch section: query tiles
+ * instead of a dense bias).
+ *   q     : [B, Tq, num_q_heads, 192]   query t has position q_pos0 + t
+ *   k, v  : [B, Tk, num_kv_heads, 192|128], key j has position j
+ *   Tk must equal q_pos0 + Tq (each chunk sees its full prefix).
+ *   out   : [B, Tq, num_q_heads, 128] bf16;  lse : [B, num_q_heads, Tq] fp32 or NULL.
+ * Needs cfg->window == 0.
+ */
+mimo_status mimo_attn_prefill_global(const mimo_attn_cfg *cfg, const uint16_t *q, const uint16_t *k,
+                                     const uint16_t *v, int32_t B, int32_t Tq, int32_t Tk,
+                                     int64_t q_pos0, uint16_t *out, float *lse, void *stream);
+
+/*
+ * One decode query per sequence over a KV cache (window-sized ring on sliding
+ * layers, Gaudi recipe page, Launch section; a long cache on global layers).
+ * Split-K flash decoding: partial results per key chunk go to `ws`, then a
+ * combine pass merges them by their log-sum-exp.
+ *   q       : [S, num_q_heads, 192] unrotated; q_pos : [S] int64 positions
+ *   k_cache : [S, cap, num_kv_heads, 192] rotated keys (as mimo_kv_ring_append writes)
+ *   v_cache : [S, cap, num_kv_heads, 128]
+ *   Cache rule: the token at position t lives in slot t mod cap.  window > 0:
+ *   the query sees positions max(0, p-window+1)..p, which needs cap >= window.
+ *   window == 0: it sees 0..p, which needs p < cap (later positions are cut off
+ *   at cap).  A negative position sees nothing.
+ *   sinks   : [num_q_heads] fp32 or NULL.   out : [S, num_q_heads, 128] bf16.
+ *   ws      : device workspace of at least mimo_attn_decode_workspace_size() bytes.
+ */
+mimo_status mimo_attn_decode(const mimo_attn_cfg *cfg, int32_t S, const uint16_t *q,
+                             const int64_t *q_pos, const uint16_t *k_cache, const uint16_t *v_cache,
+                             int32_t cap, const float *sinks, uint16_t *out, void *ws,
+                             size_t ws_bytes, void *stream);
+
+/* Workspace bytes mimo_attn_decode needs for S sequences over caches of cap slots. */
+size_t mimo_attn_decode_workspace_size(const mimo_attn_cfg *cfg, int32_t S, int32_t cap);
+
+/*
+ * Append one new token per sequence: rotate k_new at pos (partial RoPE) and
+ * write it and v_new into slot pos mod cap (the window-sized KV of the Gaudi
+ * recipe page keeps only the window; a global cache with cap above every
+ * position never wraps).
+ *   k_new : [S, num_kv_heads, 192] unrotated;  v_new : [S, num_kv_heads, 128]
+ *   pos   : [S] int64, >= 0;  k_cache / v_cache as in mimo_attn_decode.
+ */
+mimo_status mimo_kv_ring_append(const mimo_attn_cfg *cfg, int32_t S, const uint16_t *k_new,
+                                const uint16_t *v_new, const int64_t *pos, uint16_t *k_cache,
+                                uint16_t *v_cache, int32_t cap, void *stream);
+
+/* Message for the calling thread's last error ("" if none). */
+const char *mimo_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MIMO_ATTN_H */

@@ -1,0 +1,167 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any launch.
+
+None of these calls reaches a kernel launch: each one fails validation first
+(the pointer values are never dereferenced on the host)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from global_attention_sinks_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mimo_attn.h")
+
+OK, INVAL, UNSUP, WS, HIPERR = 0, 1, 2, 3, 4
+FAKE = ctypes.c_void_p(0x10000)   # a non-NULL device address, never touched on the host
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from global_attention_sinks_amd import build
+        build.build()
+    return B.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:mimo_status|size_t|const char \*)\s*(mimo_\w+)\s*\(", text, re.M)))
+
+
+def test_header_lists_the_five_entry_points():
+    fns = header_functions()
+    for name in ("mimo_attn_prefill_swa", "mimo_attn_prefill_global", "mimo_attn_decode",
+                 "mimo_rope_partial", "mimo_kv_ring_append"):
+        assert name in fns
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def cfg_swa(**kw):
+    c = B.swa_cfg()
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def cfg_glob(**kw):
+    c = B.global_cfg()
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def err(lib):
+    return lib.mimo_last_error().decode()
+
+
+def swa(lib, cfg, q=FAKE, k=FAKE, v=FAKE, sinks=FAKE, Bn=1, T=16, pos0=0, out=FAKE):
+    return lib.mimo_attn_prefill_swa(ctypes.byref(cfg), q, k, v, sinks, Bn, T, pos0, out, None, None)
+
+
+def glob(lib, cfg, Bn=1, Tq=16, Tk=16, q_pos0=0, q=FAKE, out=FAKE):
+    return lib.mimo_attn_prefill_global(ctypes.byref(cfg), q, FAKE, FAKE, Bn, Tq, Tk, q_pos0, out, None, None)
+
+
+def test_null_cfg(lib):
+    assert lib.mimo_attn_prefill_swa(None, FAKE, FAKE, FAKE, FAKE, 1, 1, 0, FAKE, None, None) == INVAL
+    assert "cfg" in err(lib)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("num_q_heads", 0, INVAL), ("num_kv_heads", -1, INVAL), ("num_kv_heads", 7, INVAL),
+    ("head_dim_qk", 128, UNSUP), ("head_dim_v", 192, UNSUP), ("rope_dim", 32, UNSUP),
+    ("rope_base", 0.5, INVAL), ("rope_base", float("inf"), INVAL),
+    ("softmax_scale", 0.0, INVAL), ("softmax_scale", float("nan"), INVAL),
+    ("v_scale", float("inf"), INVAL), ("window", -1, INVAL), ("window", 0, INVAL),
+])
+def test_bad_cfg_swa(lib, field, value, code):
+    assert swa(lib, cfg_swa(**{field: value})) == code
+    assert err(lib)
+
+
+def test_group_size_support(lib):
+    # 64 q heads over 32 KV heads: group 2 is not a multiple of 4
+    assert swa(lib, cfg_swa(num_kv_heads=32)) == UNSUP
+    assert "multiple of 4" in err(lib)
+
+
+def test_null_pointers_and_sizes(lib):
+    c = cfg_swa()
+    assert swa(lib, c, q=None) == INVAL
+    assert swa(lib, c, out=None) == INVAL
+    assert swa(lib, c, T=-1) == INVAL
+    assert swa(lib, c, pos0=-5) == INVAL
+    # empty work is valid and enqueues nothing, NULL data included
+    assert swa(lib, c, q=None, k=None, v=None, out=None, T=0) == OK
+    assert swa(lib, c, Bn=0) == OK
+
+
+def test_global_prefill_contract(lib):
+    assert glob(lib, cfg_glob(window=128)) == INVAL
+    assert glob(lib, cfg_glob(), Tq=16, Tk=17) == INVAL
+    assert "q_pos0 + Tq" in err(lib)
+    assert glob(lib, cfg_glob(), Tq=16, Tk=48, q_pos0=-32) == INVAL
+    assert glob(lib, cfg_glob(), Tq=0, Tk=0, q=None, out=None) == OK
+
+
+def dec(lib, cfg, S=4, cap=128, ws=FAKE, ws_bytes=1 << 30, q=FAKE):
+    return lib.mimo_attn_decode(ctypes.byref(cfg), S, q, FAKE, FAKE, FAKE, cap, None, FAKE, ws, ws_bytes, None)
+
+
+def test_decode_contract(lib):
+    assert dec(lib, cfg_swa(), cap=64) == INVAL          # ring shorter than the window
+    assert "cap" in err(lib)
+    assert dec(lib, cfg_swa(), S=-1) == INVAL
+    assert dec(lib, cfg_swa(num_kv_heads=2), cap=128) == UNSUP   # group 32 > 16
+    assert dec(lib, cfg_glob(), q=None) == INVAL
+    assert dec(lib, cfg_glob(), S=0, q=None) == OK
+
+
+def test_decode_workspace(lib):
+    g = cfg_glob()
+    need = lib.mimo_attn_decode_workspace_size(ctypes.byref(g), 16, 131072)
+    # partial (max, sum, 128 outputs) in fp32 per (sequence, head, 2048-slot chunk)
+    assert need == 16 * 64 * (131072 // 2048) * (128 + 2) * 4
+    assert lib.mimo_attn_decode_workspace_size(ctypes.byref(cfg_swa()), 64, 128) == 0
+    assert dec(lib, g, S=16, cap=131072, ws=None, ws_bytes=0) == WS
+    assert dec(lib, g, S=16, cap=131072, ws_bytes=need - 1) == WS
+    assert str(need) in err(lib)
+
+
+def test_rope_and_append_contract(lib):
+    c = cfg_swa()
+    assert lib.mimo_rope_partial(ctypes.byref(c), FAKE, None, 4, 8, FAKE, None) == INVAL
+    assert lib.mimo_rope_partial(ctypes.byref(c), FAKE, FAKE, -1, 8, FAKE, None) == INVAL
+    assert lib.mimo_rope_partial(ctypes.byref(c), FAKE, FAKE, 4, 0, FAKE, None) == INVAL
+    # partial overlap of input and output
+    x = ctypes.c_void_p(0x100000)
+    y = ctypes.c_void_p(0x100000 + 384)
+    assert lib.mimo_rope_partial(ctypes.byref(c), x, y, 4, 8, FAKE, None) == INVAL
+    assert lib.mimo_rope_partial(ctypes.byref(c), FAKE, FAKE, 0, 8, FAKE, None) == OK
+    assert lib.mimo_kv_ring_append(ctypes.byref(c), 2, FAKE, FAKE, None, FAKE, FAKE, 128, None) == INVAL
+    assert lib.mimo_kv_ring_append(ctypes.byref(c), 2, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == INVAL
+    assert lib.mimo_kv_ring_append(ctypes.byref(c), 0, None, None, None, None, None, 128, None) == OK
+
+
+def test_error_message_cleared_on_success(lib):
+    assert swa(lib, cfg_swa(), q=None) == INVAL
+    assert err(lib) != ""
+    assert swa(lib, cfg_swa(), Bn=0) == OK
+    assert err(lib) == ""
+
+
+def test_binding_refuses_missing_library(tmp_path):
+    saved = B._lib
+    B._lib = None
+    try:
+        with pytest.raises(ImportError):
+            B.load_library(str(tmp_path / "nope.so"))
+    finally:
+        B._lib = saved

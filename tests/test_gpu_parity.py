@@ -1,0 +1,274 @@
+"""GPU parity: every entry point of the C ABI against the fp64 oracle on the same
+seeded inputs, at sizes the oracle finishes in seconds (several tiles and a
+ragged tail), plus the edge cases of the method.  Bar: max-abs <= 2e-2 and
+mean-abs <= 2e-3 on bf16 outputs; RoPE outputs within bf16 rounding."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from global_attention_sinks_amd import binding as Bd
+from global_attention_sinks_amd import inputs as gen
+from tests.gpu_util import assert_parity, dev, dev_bf16, host_bits, host_f64, say
+
+pytestmark = pytest.mark.gpu
+
+
+def cfg_for(hq, hkv, window, base):
+    return Bd.MimoAttnCfg(hq, hkv, 192, 128, 64, base, 1.0 / math.sqrt(192.0), 0.707, window)
+
+
+# ---------------------------------------------------------------- RoPE
+
+@pytest.mark.parametrize("base", [1e4, 1e7])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_rope_partial(base, in_place):
+    n, h = 1000, 8
+    d = gen.rope_inputs(n, h, seed=2001, pos_lo=0, pos_hi=1 << 20)
+    pos = d["pos"].copy()
+    pos[:6] = [0, 1, 127, 200000, 524287, (1 << 20) - 1]
+    say(f"rope_partial base={base} in_place={in_place} n={n} h={h}")
+    x = dev_bf16(d["x"])
+    out = x if in_place else torch.empty_like(x)
+    Bd.mimo_rope_partial(cfg_for(64, 8, 0, base), x, out, dev(pos))
+    torch.cuda.synchronize()
+    got = host_f64(out)
+    ref = oracle.rope_partial(d["x"], pos, base)
+    assert np.array_equal(host_bits(out)[..., 64:], d["x"][..., 64:])      # pass-through dims untouched
+    err = np.abs(got - ref)
+    assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 2e-5), float(err.max())
+    # nearly every value is the correctly rounded bf16 of the fp64 rotation
+    rne = gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(ref.astype(np.float32))).astype(np.float64)
+    frac = float(np.mean(got[..., :64] == rne[..., :64]))
+    say(f"  correctly rounded fraction {frac:.5f}, max err {err.max():.3e}")
+    assert frac > 0.99
+
+
+def test_rope_cos_200000_on_device():
+    """The page's check (Gaudi recipe, Verified): cos(200000) must read 0.9974, not 0."""
+    x = np.zeros((1, 1, 192), np.float32)
+    x[0, 0, 0] = 1.0
+    xb = dev_bf16(gen.f32_to_bf16_bits(x))
+    out = torch.empty_like(xb)
+    Bd.mimo_rope_partial(cfg_for(64, 8, 0, 1e4), xb, out, dev(np.array([200000], np.int64)))
+    v = host_f64(out)[0, 0]
+    assert abs(v[0] - 0.9974) < 2 ** -8 and abs(v[32] - math.sin(200000.0)) < 2 ** -8
+
+
+# ---------------------------------------------------------------- ring append
+
+@pytest.mark.parametrize("hkv,cap,base,pos_hi", [(8, 128, 1e4, 131072), (4, 3000, 1e7, 3000)])
+def test_kv_ring_append(hkv, cap, base, pos_hi):
+    S = 24
+    d = gen.append_inputs(S, hkv, seed=2002, pos_lo=0, pos_hi=pos_hi)
+    say(f"kv_ring_append S={S} hkv={hkv} cap={cap}")
+    kc = torch.full((S, cap, hkv, 192), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vc = torch.full((S, cap, hkv, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    Bd.mimo_kv_ring_append(cfg_for(64, hkv, 128 if cap == 128 else 0, base), dev_bf16(d["k"]),
+                           dev_bf16(d["v"]), dev(d["pos"]), kc, vc)
+    torch.cuda.synchronize()
+    kr, _ = oracle.kv_ring_append_rows(d["k"], d["v"], d["pos"], base)
+    kh, vh = host_f64(kc), host_bits(vc)
+    slots = d["pos"] % cap
+    for s in range(S):
+        got = kh[s, slots[s]]
+        assert np.all(np.abs(got - kr[s]) <= 2.0 ** -8 * np.abs(kr[s]) + 2e-5)
+        assert np.array_equal(vh[s, slots[s]], d["v"][s])
+        others = np.ones(cap, bool)
+        others[slots[s]] = False
+        assert np.all(np.isnan(kh[s, others]))
+
+
+# ---------------------------------------------------------------- prefill
+
+def run_swa(d, hq, hkv, window, pos0=0, want_lse=False):
+    q, k, v = dev_bf16(d["q"]), dev_bf16(d["k"]), dev_bf16(d["v"])
+    B, T = d["q"].shape[:2]
+    out = torch.empty((B, T, hq, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, hq, T), dtype=torch.float32, device="cuda") if want_lse else None
+    sinks = None if d["sinks"] is None else dev(d["sinks"])
+    Bd.mimo_attn_prefill_swa(cfg_for(hq, hkv, window, 1e4), q, k, v, sinks, out, pos0=pos0, lse=lse)
+    torch.cuda.synchronize()
+    return (host_f64(out), lse.cpu().numpy().astype(np.float64)) if want_lse else host_f64(out)
+
+
+SWA_CASES = [
+    # B, T, pos0, window, sinks, (hq, hkv)
+    (1, 512, 0, 128, True, (64, 8)),     # the small sliding-window workload, in full
+    (2, 300, 0, 128, True, (64, 8)),     # ragged tail, two sequences
+    (1, 200, 5000, 128, True, (64, 8)),  # positions far from 0
+    (1, 150, 0, 129, True, (64, 8)),     # the 129-key convention
+    (1, 100, 0, 1, True, (64, 8)),       # window 1: the sigmoid gate
+    (1, 100, 0, 1000, True, (64, 8)),    # window >= T: full causal
+    (1, 77, 3, 128, False, (64, 8)),     # no sink
+    (3, 65, 0, 128, True, (16, 4)),      # GQA group of 4
+    (1, 1, 0, 128, True, (64, 8)),       # one token
+]
+
+
+@pytest.mark.parametrize("B,T,pos0,window,with_sinks,heads", SWA_CASES)
+def test_prefill_swa(B, T, pos0, window, with_sinks, heads):
+    hq, hkv = heads
+    say(f"prefill_swa B={B} T={T} pos0={pos0} W={window} sinks={with_sinks} heads={heads}")
+    d = gen.prefill_inputs(B, T, hq, hkv, seed=3000 + T, with_sinks=with_sinks)
+    got, lse = run_swa(d, hq, hkv, window, pos0=pos0, want_lse=True)
+    ref, rlse = oracle.prefill_swa(d["q"], d["k"], d["v"], d["sinks"], pos0=pos0, window=window,
+                                   base=1e4, want_lse=True)
+    assert_parity(got, ref, "out")
+    assert np.max(np.abs(lse - rlse.transpose(0, 2, 1))) < 1e-2
+
+
+def test_prefill_swa_sink_dominates():
+    """Large sink logits (sink = +10): the output shrinks toward 0 and stays exact."""
+    d = gen.prefill_inputs(1, 200, 64, 8, seed=3100, with_sinks=True)
+    d["sinks"] = (d["sinks"] + 10.0).astype(np.float32)
+    got = run_swa(d, 64, 8, 128)
+    ref = oracle.prefill_swa(d["q"], d["k"], d["v"], d["sinks"], window=128, base=1e4)
+    assert_parity(got, ref, "out")
+
+
+def run_global(q, k, v, hq, hkv, q_pos0=0, want_lse=False):
+    B, Tq = q.shape[:2]
+    out = torch.empty((B, Tq, hq, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, hq, Tq), dtype=torch.float32, device="cuda") if want_lse else None
+    Bd.mimo_attn_prefill_global(cfg_for(hq, hkv, 0, 1e7), dev_bf16(q), dev_bf16(k), dev_bf16(v), out,
+                                q_pos0=q_pos0, lse=lse)
+    torch.cuda.synchronize()
+    return (host_f64(out), lse.cpu().numpy().astype(np.float64)) if want_lse else host_f64(out)
+
+
+GLOBAL_CASES = [
+    # B, T, q_pos0 (the chunk starts here; keys 0..T-1), heads
+    (1, 1000, 0, (64, 4)),
+    (1, 1000, 600, (64, 4)),     # a chunk against its whole prefix
+    (2, 257, 0, (64, 4)),
+    (1, 300, 128, (32, 8)),      # GQA group of 4
+    (1, 1, 0, (64, 4)),
+]
+
+
+@pytest.mark.parametrize("B,T,q_pos0,heads", GLOBAL_CASES)
+def test_prefill_global(B, T, q_pos0, heads):
+    hq, hkv = heads
+    say(f"prefill_global B={B} Tk={T} q_pos0={q_pos0} heads={heads}")
+    d = gen.prefill_inputs(B, T, hq, hkv, seed=4000 + T, with_sinks=False)
+    q = d["q"][:, q_pos0:]
+    got, lse = run_global(q, d["k"], d["v"], hq, hkv, q_pos0=q_pos0, want_lse=True)
+    ref, rlse = oracle.prefill_global(q, d["k"], d["v"], q_pos0=q_pos0, base=1e7, want_lse=True)
+    assert_parity(got, ref, "out")
+    assert np.max(np.abs(lse - rlse.transpose(0, 2, 1))) < 1e-2
+
+
+# ---------------------------------------------------------------- decode
+
+def run_decode(d, hq, hkv, window, base, cap):
+    S = d["q"].shape[0]
+    cfg = cfg_for(hq, hkv, window, base)
+    out = torch.empty((S, hq, 128), dtype=torch.bfloat16, device="cuda")
+    nws = Bd.mimo_attn_decode_workspace_size(cfg, S, cap)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    sinks = None if d["sinks"] is None else dev(d["sinks"])
+    Bd.mimo_attn_decode(cfg, dev_bf16(d["q"]), dev(d["pos"]), dev_bf16(d["k_cache"]),
+                        dev_bf16(d["v_cache"]), sinks, out, ws=ws)
+    torch.cuda.synchronize()
+    return host_f64(out)
+
+
+def test_decode_swa_ring():
+    S, cap = 64, 128
+    pos = np.random.Generator(np.random.PCG64(5001)).integers(128, 131072, size=S)
+    pos[:6] = [0, 5, 126, 127, 128, 129]   # early rows see fewer keys; unused slots hold NaN
+    d = _decode_with_positions(S, cap, 64, 8, 5001, 128, pos, True)
+    say(f"decode sliding S={S} cap={cap}")
+    got = run_decode(d, 64, 8, 128, 1e4, cap)
+    ref = oracle.decode(d["q"], d["pos"], d["k_cache"], d["v_cache"], sinks=d["sinks"], window=128, base=1e4)
+    assert_parity(got, ref, "out")
+
+
+def _decode_with_positions(S, cap, hq, hkv, seed, window, pos, with_sinks):
+    """decode_inputs with chosen positions: same draws, poison matching the positions."""
+    cq, ck, cv, cs, _ = gen.children(seed)
+    q = gen.normal_bf16(cq, (S, hq, 192))
+    kc = np.full((S, cap, hkv, 192), gen.BF16_NAN, np.uint16)
+    vc = np.full((S, cap, hkv, 128), gen.BF16_NAN, np.uint16)
+    ks, vs = ck.spawn(S), cv.spawn(S)
+    for s in range(S):
+        p = int(pos[s])
+        slots, _ = oracle.cache_slots(p, cap, window)
+        kc[s, slots] = gen.normal_bf16(ks[s], (len(slots), hkv, 192))
+        vc[s, slots] = gen.normal_bf16(vs[s], (len(slots), hkv, 128))
+    return {"q": q, "pos": np.asarray(pos, np.int64), "k_cache": kc, "v_cache": vc,
+            "sinks": gen.normal_f32(cs, (hq,)) if with_sinks else None}
+
+
+@pytest.mark.parametrize("with_sinks", [False, True])
+def test_decode_global_splits(with_sinks):
+    cap = 9000
+    lens = [1, 100, 2048, 2049, 5000, 9000, 4097]
+    pos = np.array([L - 1 for L in lens], np.int64)
+    d = _decode_with_positions(len(lens), cap, 64, 4, 5002, 0, pos, with_sinks)
+    say(f"decode global lens={lens} cap={cap} sinks={with_sinks}")
+    got = run_decode(d, 64, 4, 0, 1e7, cap)
+    ref = oracle.decode(d["q"], d["pos"], d["k_cache"], d["v_cache"], sinks=d["sinks"], window=0, base=1e7)
+    assert_parity(got, ref, "out")
+
+
+def test_decode_negative_position_is_empty():
+    d = _decode_with_positions(3, 128, 64, 8, 5003, 128, np.array([10, 200, 300]), True)
+    d["pos"][1] = -1
+    got = run_decode(d, 64, 8, 128, 1e4, 128)
+    assert np.all(got[1] == 0.0)
+    ref = oracle.decode(d["q"], d["pos"], d["k_cache"], d["v_cache"], sinks=d["sinks"], window=128,
+                        base=1e4, seqs=[0, 2])
+    assert_parity(got[[0, 2]], ref, "out")
+
+
+# ---------------------------------------------------------------- GPU-vs-GPU consistency
+
+def test_append_then_decode_equals_prefill_row():
+    """Decode over a ring filled by mimo_kv_ring_append reproduces the prefill row."""
+    T, cap = 300, 128
+    d = gen.prefill_inputs(1, T, 64, 8, seed=6001, with_sinks=True)
+    pref = run_swa(d, 64, 8, 128)
+    cfg = cfg_for(64, 8, 128, 1e4)
+    kc = torch.full((1, cap, 8, 192), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vc = torch.full((1, cap, 8, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    k, v = dev_bf16(d["k"][0]), dev_bf16(d["v"][0])
+    sinks = dev(d["sinks"])
+    ws = torch.empty(1, dtype=torch.uint8, device="cuda")
+    worst = 0.0
+    for p in range(T):
+        Bd.mimo_kv_ring_append(cfg, k[p:p + 1].contiguous(), v[p:p + 1].contiguous(),
+                               dev(np.array([p], np.int64)), kc, vc)
+        if p in (0, 1, 126, 127, 128, 200, 299):
+            out = torch.empty((1, 64, 128), dtype=torch.bfloat16, device="cuda")
+            Bd.mimo_attn_decode(cfg, dev_bf16(d["q"][0, p][None]), dev(np.array([p], np.int64)), kc, vc,
+                                sinks, out, ws=ws)
+            torch.cuda.synchronize()
+            worst = max(worst, float(np.abs(host_f64(out)[0] - pref[0, p]).max()))
+    say(f"  decode vs prefill row: max-abs {worst:.3e}")
+    assert worst <= 1e-2
+
+
+def test_chunked_global_equals_whole_and_is_deterministic():
+    T = 2048
+    d = gen.prefill_inputs(1, T, 64, 4, seed=6002, with_sinks=False)
+    whole = run_global(d["q"], d["k"], d["v"], 64, 4)
+    again = run_global(d["q"], d["k"], d["v"], 64, 4)
+    assert np.array_equal(whole, again)   # fixed reduction order: bitwise repeatable
+    parts = [run_global(d["q"][:, :1024], d["k"][:, :1024], d["v"][:, :1024], 64, 4),
+             run_global(d["q"][:, 1024:], d["k"], d["v"], 64, 4, q_pos0=1024)]
+    diff = np.abs(np.concatenate(parts, axis=1) - whole).max()
+    say(f"  chunked vs whole: max-abs {diff:.3e}")
+    assert diff <= 1e-2
+
+
+def test_position_shift_invariance_on_device():
+    d = gen.prefill_inputs(1, 256, 64, 8, seed=6003, with_sinks=True)
+    a = run_swa(d, 64, 8, 128, pos0=0)
+    b = run_swa(d, 64, 8, 128, pos0=100000)
+    diff = float(np.abs(a - b).max())
+    say(f"  shift by 1e5: max-abs {diff:.3e}")
+    assert diff <= 2e-2
