@@ -1,0 +1,337 @@
+#!/usr/bin/env python3
+"""Benchmark of the MiMo-V2.6-Flash attention hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  1. sliding-window + sink prefill, B=4 x T=8192, 64 q / 8 KV heads, window 128
+  2. global causal prefill, B=1 x T=32768, 64 q / 4 KV heads
+  3. mixed decode step: ring append of the new token for 64 sliding and 16
+     global sequences, then sliding decode (ring of 128) and global split-K
+     decode (KV lengths ~ U[32768, 131072]).
+Inputs are resident in HBM before the timed region.  The reported value is the
+step's algorithmic attention FLOPs (2*(192+128)*64 per visible query-key pair)
+over the measured step time.  Per-launch durations are taken with HIP events
+on the stream the kernels are launched on (torch's current stream).
+
+--workload long_prefill instead times the 524288-token global prefill run as 8
+query chunks of 65536, each against its full causal prefix.
+
+The fp64 oracle is timed on a bounded sample of the same workload on the host
+cores (rank 0, N=1) as a CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention prefill TFLOP/s (% bf16 MFMA peak); decode HBM GB/s (% peak)"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+FLOP_PER_PAIR_HEAD = 2 * (192 + 128)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------ algorithmic counts
+
+def swa_pairs(T: int, W: int) -> int:
+    """Visible (query, key) pairs of one sequence of T tokens, window W."""
+    full = max(0, T - W + 1) * W
+    early = sum(min(t + 1, W) for t in range(min(T, W - 1)))
+    return full + early
+
+
+def causal_pairs(q_lo: int, q_hi: int) -> int:
+    """Pairs of queries at positions q_lo..q_hi-1 over all earlier keys."""
+    return (q_hi * (q_hi + 1) - q_lo * (q_lo + 1)) // 2
+
+
+def prefill_bytes(B, Tq, Tk, hq, hkv, sinks: bool) -> int:
+    return B * (Tq * hq * 192 * 2 + Tk * hkv * (192 + 128) * 2 + Tq * hq * 128 * 2) + (hq * 4 if sinks else 0)
+
+
+# ------------------------------------------------------------ workloads
+
+def _dev_bf16(torch, bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+
+def setup_layer_step(torch, gen, Bd):
+    def dev_bf16(bits):
+        return _dev_bf16(torch, bits)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+    ph = {}
+    # 1. sliding-window prefill
+    log("setup: sliding-window prefill B=4 T=8192")
+    d = gen.prefill_inputs(4, 8192, 64, 8, seed=1001, with_sinks=True)
+    ph["swa_prefill"] = dict(
+        cfg=Bd.swa_cfg(), q=dev_bf16(d["q"]), k=dev_bf16(d["k"]), v=dev_bf16(d["v"]),
+        sinks=dev(d["sinks"]), out=torch.empty((4, 8192, 64, 128), dtype=torch.bfloat16, device="cuda"),
+        flops=FLOP_PER_PAIR_HEAD * 64 * 4 * swa_pairs(8192, 128),
+        bytes=prefill_bytes(4, 8192, 8192, 64, 8, True), host=d)
+    # 2. global prefill
+    log("setup: global prefill B=1 T=32768")
+    d = gen.prefill_inputs(1, 32768, 64, 4, seed=1002, with_sinks=False)
+    ph["global_prefill"] = dict(
+        cfg=Bd.global_cfg(), q=dev_bf16(d["q"]), k=dev_bf16(d["k"]), v=dev_bf16(d["v"]),
+        out=torch.empty((1, 32768, 64, 128), dtype=torch.bfloat16, device="cuda"),
+        flops=FLOP_PER_PAIR_HEAD * 64 * causal_pairs(0, 32768),
+        bytes=prefill_bytes(1, 32768, 32768, 64, 4, False), host=d)
+    # 3. mixed decode
+    log("setup: mixed decode (64 sliding seqs, ring 128; 16 global seqs, cap 131072)")
+    sw = gen.decode_inputs(64, 128, 64, 8, seed=1003, window=128, pos_lo=128, pos_hi=131072, with_sinks=True)
+    gl = gen.decode_inputs(16, 131072, 64, 4, seed=2003, window=0, pos_lo=32768, pos_hi=131072,
+                           with_sinks=False)
+    ap_s = gen.append_inputs(64, 8, seed=3003, pos_lo=0, pos_hi=1)
+    ap_g = gen.append_inputs(16, 4, seed=4003, pos_lo=0, pos_hi=1)
+    dec = {}
+    for name, dd, ap, cfg, cap in (("swa", sw, ap_s, Bd.swa_cfg(), 128),
+                                   ("global", gl, ap_g, Bd.global_cfg(), 131072)):
+        S = dd["q"].shape[0]
+        ws_n = Bd.mimo_attn_decode_workspace_size(cfg, S, cap)
+        L = np.minimum(dd["pos"] + 1, 128 if name == "swa" else dd["pos"] + 1)
+        hkv = cfg.num_kv_heads
+        dec[name] = dict(
+            cfg=cfg, q=dev_bf16(dd["q"]), pos=dev(dd["pos"]), kc=dev_bf16(dd["k_cache"]),
+            vc=dev_bf16(dd["v_cache"]), sinks=None if dd["sinks"] is None else dev(dd["sinks"]),
+            out=torch.empty((S, 64, 128), dtype=torch.bfloat16, device="cuda"),
+            ws=torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda"),
+            k_new=dev_bf16(ap["k"]), v_new=dev_bf16(ap["v"]),
+            flops=FLOP_PER_PAIR_HEAD * 64 * int(L.sum()),
+            bytes=int(L.sum()) * hkv * 320 * 2 + S * 64 * (192 + 128) * 2 + S * 8 + (64 * 4 if dd["sinks"] is not None else 0),
+            append_bytes=S * hkv * (192 * 2 + 320) * 2 + S * 8, host=dd)
+    ph["decode"] = dec
+    return ph
+
+
+def run_layer_step(ph, Bd, ev=None):
+    """Enqueue one step; ev maps a launch name to (start, end) events to record."""
+    def rec(name, fn):
+        if ev is not None:
+            ev[name][0].record()
+        fn()
+        if ev is not None:
+            ev[name][1].record()
+
+    s = ph["swa_prefill"]
+    rec("swa_prefill", lambda: Bd.mimo_attn_prefill_swa(s["cfg"], s["q"], s["k"], s["v"], s["sinks"], s["out"]))
+    g = ph["global_prefill"]
+    rec("global_prefill", lambda: Bd.mimo_attn_prefill_global(g["cfg"], g["q"], g["k"], g["v"], g["out"]))
+    for name in ("swa", "global"):
+        d = ph["decode"][name]
+        rec(f"append_{name}", lambda d=d: Bd.mimo_kv_ring_append(d["cfg"], d["k_new"], d["v_new"], d["pos"],
+                                                                  d["kc"], d["vc"]))
+    for name in ("swa", "global"):
+        d = ph["decode"][name]
+        rec(f"decode_{name}", lambda d=d: Bd.mimo_attn_decode(d["cfg"], d["q"], d["pos"], d["kc"], d["vc"],
+                                                               d["sinks"], d["out"], ws=d["ws"]))
+
+
+# ------------------------------------------------------------ CPU baseline
+
+def cpu_baseline_layer_step(ph, budget_s: float):
+    """Time the fp64 oracle on a bounded sample of each phase and extrapolate
+    each phase by its FLOP count; returns the oracle's step-equivalent rate."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    rng = np.random.default_rng(0)
+    parts, desc = [], []
+    # sliding prefill: 48 rows per sequence
+    d = ph["swa_prefill"]["host"]
+    rows = np.unique(np.concatenate([[0, 127, 128, 8191], rng.integers(0, 8192, 44)]))
+    t0 = time.perf_counter()
+    oracle.prefill_swa(d["q"], d["k"], d["v"], d["sinks"], window=128, base=1e4, rows=rows, n_threads=threads)
+    dt = time.perf_counter() - t0
+    sample_pairs = 4 * sum(min(int(r) + 1, 128) for r in rows)
+    parts.append((dt, FLOP_PER_PAIR_HEAD * 64 * sample_pairs, ph["swa_prefill"]["flops"]))
+    desc.append(f"sliding prefill {len(rows)} rows x 4 seqs")
+    # global prefill: rows spread over the sequence
+    d = ph["global_prefill"]["host"]
+    rows = np.unique(np.concatenate([[0, 32767], rng.integers(0, 32768, 14)]))
+    t0 = time.perf_counter()
+    oracle.prefill_global(d["q"], d["k"], d["v"], base=1e7, rows=rows, n_threads=threads)
+    dt = time.perf_counter() - t0
+    parts.append((dt, FLOP_PER_PAIR_HEAD * 64 * int(sum(int(r) + 1 for r in rows)), ph["global_prefill"]["flops"]))
+    desc.append(f"global prefill {len(rows)} rows")
+    # decode: 8 sliding sequences, 2 global sequences
+    for name, seqs, window, base in (("swa", list(range(8)), 128, 1e4), ("global", [0, 1], 0, 1e7)):
+        dd = ph["decode"][name]["host"]
+        t0 = time.perf_counter()
+        oracle.decode(dd["q"], dd["pos"], dd["k_cache"], dd["v_cache"], sinks=dd["sinks"], window=window,
+                      base=base, seqs=seqs, n_threads=threads)
+        dt = time.perf_counter() - t0
+        L = [min(int(dd["pos"][s]) + 1, window if window else int(dd["pos"][s]) + 1) for s in seqs]
+        parts.append((dt, FLOP_PER_PAIR_HEAD * 64 * sum(L), ph["decode"][name]["flops"]))
+        desc.append(f"{name} decode {len(seqs)} seqs")
+    total_sample_s = sum(p[0] for p in parts)
+    step_s = sum(dt * full / max(sf, 1) for dt, sf, full in parts)
+    step_flops = sum(full for _, _, full in parts)
+    return {"value": step_flops / step_s / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "; ".join(desc) + f" ({total_sample_s:.1f} s of fp64 oracle time, each phase "
+                                        f"extrapolated to the full step by its FLOP count)"}
+
+
+# ------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", choices=["layer_step", "long_prefill"], default="layer_step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one MI355X: this build has no multi-GPU path (each GPU would run "
+              "its own shard of heads or sequences with no communication); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from global_attention_sinks_amd import binding as Bd
+    from global_attention_sinks_amd import inputs as gen
+    Bd.load_library()   # fails loudly if the HIP library is not built
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(2)
+
+    if args.workload == "long_prefill":
+        return main_long_prefill(args, torch, gen, Bd)
+
+    ph = setup_layer_step(torch, gen, Bd)
+    names = ["swa_prefill", "global_prefill", "append_swa", "append_global", "decode_swa", "decode_global"]
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        run_layer_step(ph, Bd)
+    torch.cuda.synchronize()
+    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+           for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run_layer_step(ph, Bd, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in evs])) for n in names}
+    ms_step = wall * 1e3 / args.steps
+
+    s, g = ph["swa_prefill"], ph["global_prefill"]
+    ds, dg = ph["decode"]["swa"], ph["decode"]["global"]
+    step_flops = s["flops"] + g["flops"] + ds["flops"] + dg["flops"]
+    value = step_flops / (ms_step * 1e-3) / 1e12
+
+    def tf(f, t):
+        return f / (t * 1e-3) / 1e12
+
+    def gbs(b, t):
+        return b / (t * 1e-3) / 1e9
+
+    phases = {
+        "swa_prefill_b4_t8192": {"ms": ms["swa_prefill"], "tflops": tf(s["flops"], ms["swa_prefill"]),
+                                 "gbs": gbs(s["bytes"], ms["swa_prefill"])},
+        "global_prefill_t32768": {"ms": ms["global_prefill"], "tflops": tf(g["flops"], ms["global_prefill"]),
+                                  "gbs": gbs(g["bytes"], ms["global_prefill"])},
+        "ring_append_80seqs": {"ms": ms["append_swa"] + ms["append_global"]},
+        "decode_swa_64seqs": {"ms": ms["decode_swa"], "gbs": gbs(ds["bytes"], ms["decode_swa"]),
+                              "tflops": tf(ds["flops"], ms["decode_swa"])},
+        "decode_global_16seqs": {"ms": ms["decode_global"], "gbs": gbs(dg["bytes"], ms["decode_global"]),
+                                 "tflops": tf(dg["flops"], ms["decode_global"])},
+    }
+    for p in phases.values():
+        if "tflops" in p:
+            p["frac_mfma_peak"] = p["tflops"] / PEAK_BF16_TFLOPS
+        if "gbs" in p:
+            p["frac_hbm_peak"] = p["gbs"] / PEAK_HBM_GBS
+    mixed_ms = ms["append_swa"] + ms["append_global"] + ms["decode_swa"] + ms["decode_global"]
+    mixed_bytes = ds["bytes"] + dg["bytes"] + ds["append_bytes"] + dg["append_bytes"]
+    phases["mixed_decode_step"] = {"ms": mixed_ms, "gbs": gbs(mixed_bytes, mixed_ms),
+                                   "frac_hbm_peak": gbs(mixed_bytes, mixed_ms) / PEAK_HBM_GBS}
+
+    achieved = tf(g["flops"], ms["global_prefill"])
+    roofline = {"bound": "mfma", "kernel": "prefill_kernel (global causal, T=32768)",
+                "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: timing the fp64 oracle on a sample")
+        cpu = cpu_baseline_layer_step(ph, args.cpu_budget)
+
+    out = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic: seeded N(0,1) bf16 q/k/v and caches, N(0,1) fp32 sinks",
+           "config": {"workload": "mimo_layer_step = swa_prefill_b4_t8192 + global_prefill_t32768 + "
+                                  "mixed_decode_64swa_16global (append + decode)",
+                      "step_gflop": step_flops / 1e9},
+           "roofline": roofline, "cpu_baseline": cpu, "phases": phases}
+    print(json.dumps(out))
+
+
+def main_long_prefill(args, torch, gen, Bd):
+    def dev_bf16(bits):
+        return _dev_bf16(torch, bits)
+
+    T, C = 524288, 65536
+    log("setup: long global prefill T=524288 (k/v full, q per chunk)")
+    kv = gen.global_prefill_chunk(T, 64, 4, seed=1004, t_lo=0, t_hi=T)
+    k, v = dev_bf16(kv["k"]), dev_bf16(kv["v"])
+    q = dev_bf16(kv["q"])
+    del kv
+    out = torch.empty((1, T, 64, 128), dtype=torch.bfloat16, device="cuda")
+    cfg = Bd.global_cfg()
+    n_chunks = T // C
+
+    def step(ev=None):
+        for c in range(n_chunks):
+            if ev is not None:
+                ev[c][0].record()
+            Bd.mimo_attn_prefill_global(cfg, q[:, c * C:(c + 1) * C], k[:, :(c + 1) * C], v[:, :(c + 1) * C],
+                                        out[:, c * C:(c + 1) * C], q_pos0=c * C)
+            if ev is not None:
+                ev[c][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_chunks)]
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+        log(f"step {i} enqueued")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    flops = FLOP_PER_PAIR_HEAD * 64 * causal_pairs(0, T)
+    chunk_ms = [float(np.mean([e[c][0].elapsed_time(e[c][1]) for e in evs])) for c in range(n_chunks)]
+    value = flops / (ms_step * 1e-3) / 1e12
+    out_j = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+             "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+             "vs_baseline": None, "dtype": "bf16", "data": "synthetic: seeded N(0,1) bf16 q/k/v",
+             "config": {"workload": "global_prefill_t524288 in 8 query chunks of 65536 against the full prefix"},
+             "roofline": {"bound": "mfma", "kernel": "prefill_kernel (global causal chunks)", "achieved": value,
+                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": value / PEAK_BF16_TFLOPS,
+                          "traffic": None},
+             "cpu_baseline": None,
+             "chunks_ms": chunk_ms}
+    print(json.dumps(out_j))
+
+
+if __name__ == "__main__":
+    main()
