@@ -34,6 +34,13 @@ __device__ __forceinline__ void rope_sincos(uint64_t turn, int64_t pos, float &s
     c = __builtin_amdgcn_cosf(r);
 }
 
+// Same angle from a turn count already reduced mod 2^64 (fixed point, 64 fraction bits).
+__device__ __forceinline__ void turn_sincos(uint64_t t, float &s, float &c) {
+    float r = (float)(int32_t)(uint32_t)(t >> 32) * 2.3283064365386963e-10f;
+    s = __builtin_amdgcn_sinf(r);
+    c = __builtin_amdgcn_cosf(r);
+}
+
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

@@ -51,15 +51,17 @@ __device__ __forceinline__ u32x4 lds128(const uint16_t *p) {
 
 }  // namespace
 
-template <int NB, int NW>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
-                          amdgpu_waves_per_eu(NB == 2 ? 1 : 2, NB == 2 ? 1 : 2)))
+template <int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillArgs a) {
-    constexpr int QW = 32 * NB;
+    constexpr int QW = 32;                          // queries per wave (one MFMA column block)
     constexpr int NT = 64 * NW;
-    constexpr int ROT_PER = (NK * 4 + NT - 1) / NT;      // rotating K chunk pairs per thread
-    constexpr int PLAIN_PER = (NK * 16 + NT - 1) / NT;   // pass-through K chunks per thread
-    constexpr int V_PER = (NK * 4 + NT - 1) / NT;        // 4-key x 8-dv V blocks per thread
+    // staging work per tile, spread evenly over the NT threads
+    constexpr int ROT_UNITS = NK * 8;               // (row, 4 rotating pairs): 8-byte pieces
+    constexpr int PLAIN_UNITS = NK * 16;            // (row, 16-byte pass-through chunk)
+    constexpr int V_UNITS = (NK / 2) * 16;          // (key pair, 8-dv chunk)
+    constexpr int ROT_PER = ROT_UNITS / NT, PLAIN_PER = PLAIN_UNITS / NT, V_PER = V_UNITS / NT;
+    static_assert(ROT_UNITS % NT == 0 && PLAIN_UNITS % NT == 0 && V_UNITS % NT == 0, "staging split");
 
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
 
@@ -106,59 +108,52 @@ void prefill_kernel(PrefillArgs a) {
     const int tile_lo = (int)(jlo / NK);
     const int tile_hi = jhi >= jlo ? (int)(jhi / NK) : tile_lo - 1;
 
-    // ---- Q in registers (B operand): lane holds dims [96*h2, 96*h2+96) of one query
-    u32x4 qr[NB][12];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int t = q0 + 32 * nb + l32;
+    // ---- Q in registers (B operand): lane holds dims [96*h2, 96*h2+96) of query q0 + l32
+    u32x4 qr[12];
+    {
+        const int t = q0 + l32;
         if (t < a.Tq) {
             const uint16_t *src = a.q + (((size_t)b * a.Tq + t) * a.Hq + head) * kDqk + 96 * h2;
 #pragma unroll
-            for (int ks = 0; ks < 12; ++ks) qr[nb][ks] = ldg128(src + 8 * ks);
+            for (int ks = 0; ks < 12; ++ks) qr[ks] = ldg128(src + 8 * ks);
             if (h2 == 0) {
                 const int64_t qp = a.q_pos0 + t;
 #pragma unroll
-                for (int cc = 0; cc < 4; ++cc) rope_rotate8(qr[nb][cc], qr[nb][cc + 4], a.rt, 8 * cc, qp);
+                for (int cc = 0; cc < 4; ++cc) rope_rotate8(qr[cc], qr[cc + 4], a.rt, 8 * cc, qp);
             }
         } else {
 #pragma unroll
-            for (int ks = 0; ks < 12; ++ks) qr[nb][ks] = u32x4{0, 0, 0, 0};
+            for (int ks = 0; ks < 12; ++ks) qr[ks] = u32x4{0, 0, 0, 0};
         }
     }
 
-    // ---- softmax state per query column
-    float m_run[NB], l_run[NB];
-    {
-        const float m0 = a.sinks ? a.sinks[head] * kLog2e : kNegInf;
-        const float l0 = (a.sinks && h2 == 0) ? 1.0f : 0.0f;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) { m_run[nb] = m0; l_run[nb] = l0; }
-    }
-    f32x16 O[4][NB];
+    // ---- softmax state of this lane's query column
+    float m_run = a.sinks ? a.sinks[head] * kLog2e : kNegInf;
+    float l_run = (a.sinks && h2 == 0) ? 1.0f : 0.0f;
+    f32x16 O[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) O[mb][nb][e] = 0.0f;
+        for (int e = 0; e < 16; ++e) O[mb][e] = 0.0f;
 
     // ---- staging registers for the next tile
-    u32x4 k_rot[ROT_PER][2], k_pl[PLAIN_PER], v_st[V_PER][4];
+    u32x2 k_rx[ROT_PER], k_ry[ROT_PER];
+    u32x4 k_pl[PLAIN_PER], v_st[V_PER][2];
 
     auto load_tile = [&](int jt) {
         const int j0 = jt * NK;
 #pragma unroll
         for (int r = 0; r < ROT_PER; ++r) {
             const int u = tid + r * NT;
-            const int row = u >> 2, cc = u & 3;
+            const int row = u >> 3, hq = u & 7;
             const int j = j0 + row;
-            if (u < NK * 4 && j < a.Tk) {
-                const uint16_t *p = kbase + (size_t)j * krow_stride + 8 * cc;
-                k_rot[r][0] = ldg128(p);
-                k_rot[r][1] = ldg128(p + 32);
+            if (j < a.Tk) {
+                const uint16_t *p = kbase + (size_t)j * krow_stride + 4 * hq;
+                k_rx[r] = *reinterpret_cast<const u32x2 *>(p);
+                k_ry[r] = *reinterpret_cast<const u32x2 *>(p + 32);
             } else {
-                k_rot[r][0] = u32x4{0, 0, 0, 0};
-                k_rot[r][1] = u32x4{0, 0, 0, 0};
+                k_rx[r] = u32x2{0, 0};
+                k_ry[r] = u32x2{0, 0};
             }
         }
 #pragma unroll
@@ -166,19 +161,16 @@ void prefill_kernel(PrefillArgs a) {
             const int u = tid + r * NT;
             const int row = u >> 4, cc = 8 + (u & 15);
             const int j = j0 + row;
-            k_pl[r] = (u < NK * 16 && j < a.Tk) ? ldg128(kbase + (size_t)j * krow_stride + 8 * cc)
-                                                : u32x4{0, 0, 0, 0};
+            k_pl[r] = (j < a.Tk) ? ldg128(kbase + (size_t)j * krow_stride + 8 * cc) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int r = 0; r < V_PER; ++r) {
             const int u = tid + r * NT;
-            const int kg = u >> 4, cc = u & 15;
+            const int kp = u & 31, cc = u >> 5;    // consecutive lanes: consecutive key pairs
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int j = j0 + 4 * kg + rr;
-                v_st[r][rr] = (u < NK * 4 && j < a.Tk)
-                                  ? ldg128(vbase + (size_t)j * vrow_stride + 8 * cc)
-                                  : u32x4{0, 0, 0, 0};
+            for (int rr = 0; rr < 2; ++rr) {
+                const int j = j0 + 2 * kp + rr;
+                v_st[r][rr] = (j < a.Tk) ? ldg128(vbase + (size_t)j * vrow_stride + 8 * cc) : u32x4{0, 0, 0, 0};
             }
         }
     };
@@ -187,39 +179,45 @@ void prefill_kernel(PrefillArgs a) {
         uint16_t *Ks = smem + buf * STAGE;
         uint16_t *Vs = Ks + K_TILE;
         const int j0 = jt * NK;
+        const int64_t tile_pos = a.k_pos0 + j0;
 #pragma unroll
         for (int r = 0; r < ROT_PER; ++r) {
             const int u = tid + r * NT;
-            if (u < NK * 4) {
-                const int row = u >> 2, cc = u & 3;
-                u32x4 x = k_rot[r][0], y = k_rot[r][1];
-                rope_rotate8(x, y, a.rt, 8 * cc, a.k_pos0 + j0 + row);
-                *reinterpret_cast<u32x4 *>(Ks + row * KSTR + 8 * cc) = x;
-                *reinterpret_cast<u32x4 *>(Ks + row * KSTR + 8 * cc + 32) = y;
+            const int row = u >> 3, hq = u & 7;
+            u32x2 x = k_rx[r], y = k_ry[r];
+#pragma unroll
+            for (int wd = 0; wd < 2; ++wd) {
+                const int i0 = 4 * hq + 2 * wd;
+                // angle(pos0 + row) = tile base + row offset, both as 64-bit turn fractions
+                const uint64_t base0 = (uint64_t)tile_pos * a.rt.turn[i0];
+                const uint64_t base1 = (uint64_t)tile_pos * a.rt.turn[i0 + 1];
+                float s0, c0, s1, c1;
+                turn_sincos(base0 + (uint64_t)row * a.rt.turn[i0], s0, c0);
+                turn_sincos(base1 + (uint64_t)row * a.rt.turn[i0 + 1], s1, c1);
+                const float x0 = bf_lo(x[wd]), x1 = bf_hi(x[wd]);
+                const float y0 = bf_lo(y[wd]), y1 = bf_hi(y[wd]);
+                x[wd] = pack_bf16(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
+                y[wd] = pack_bf16(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
             }
+            *reinterpret_cast<u32x2 *>(Ks + row * KSTR + 4 * hq) = x;
+            *reinterpret_cast<u32x2 *>(Ks + row * KSTR + 4 * hq + 32) = y;
         }
 #pragma unroll
         for (int r = 0; r < PLAIN_PER; ++r) {
             const int u = tid + r * NT;
-            if (u < NK * 16) {
-                const int row = u >> 4, cc = 8 + (u & 15);
-                *reinterpret_cast<u32x4 *>(Ks + row * KSTR + 8 * cc) = k_pl[r];
-            }
+            const int row = u >> 4, cc = 8 + (u & 15);
+            *reinterpret_cast<u32x4 *>(Ks + row * KSTR + 8 * cc) = k_pl[r];
         }
 #pragma unroll
         for (int r = 0; r < V_PER; ++r) {
             const int u = tid + r * NT;
-            if (u < NK * 4) {
-                const int kg = u >> 4, cc = u & 15;
-                // 4 keys x 8 dv -> 8 dv rows of 4 keys
+            const int kp = u & 31, cc = u >> 5;
+            // 2 keys x 8 dv -> 8 dv rows of V^T, one dword (2 keys) each
 #pragma unroll
-                for (int d = 0; d < 8; ++d) {
-                    const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
-                    u32x2 o;
-                    o[0] = __builtin_amdgcn_perm(v_st[r][1][d >> 1], v_st[r][0][d >> 1], sel);
-                    o[1] = __builtin_amdgcn_perm(v_st[r][3][d >> 1], v_st[r][2][d >> 1], sel);
-                    *reinterpret_cast<u32x2 *>(Vs + (8 * cc + d) * VSTR + 4 * kg) = o;
-                }
+            for (int d = 0; d < 8; ++d) {
+                const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
+                const uint32_t wv = __builtin_amdgcn_perm(v_st[r][1][d >> 1], v_st[r][0][d >> 1], sel);
+                *reinterpret_cast<uint32_t *>(Vs + (8 * cc + d) * VSTR + 2 * kp) = wv;
             }
         }
     };
@@ -227,6 +225,7 @@ void prefill_kernel(PrefillArgs a) {
     const float cl2 = a.scale_log2;
     // K row read order: bits 2 and 3 of the row index swapped
     const int prow = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+    const int64_t qp = a.q_pos0 + q0 + l32;
 
     if (tile_hi >= tile_lo) {
         load_tile(tile_lo);
@@ -243,106 +242,95 @@ void prefill_kernel(PrefillArgs a) {
         const uint16_t *Vs = Ks + K_TILE;
         const int j0 = jt * NK;
 
-        // ---- S^T = K Q^T  (2 key blocks of 32 x NB query blocks of 32)
-        f32x16 S[2][NB];
+        // ---- S^T = K Q^T: 2 key blocks of 32 x 32 queries, 4 fragment reads in flight
+        f32x16 S[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+            for (int e = 0; e < 16; ++e) S[kb][e] = 0.0f;
+        {
+            const uint16_t *kr0 = Ks + prow * KSTR + 96 * h2;
+            u32x4 kf[4];
 #pragma unroll
-                for (int e = 0; e < 16; ++e) S[kb][nb][e] = 0.0f;
+            for (int i = 0; i < 4; ++i) kf[i] = lds128(kr0 + (i & 1) * 32 * KSTR + 8 * (i >> 1));
 #pragma unroll
-        for (int ks = 0; ks < 12; ++ks) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const u32x4 kf = lds128(Ks + (32 * kb + prow) * KSTR + 96 * h2 + 8 * ks);
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) S[kb][nb] = mfma32(kf, qr[nb][ks], S[kb][nb]);
+            for (int i = 0; i < 24; ++i) {
+                const int kb = i & 1, ks = i >> 1;
+                S[kb] = mfma32(kf[i & 3], qr[ks], S[kb]);
+                if (i + 4 < 24) kf[i & 3] = lds128(kr0 + ((i + 4) & 1) * 32 * KSTR + 8 * ((i + 4) >> 1));
             }
         }
 
-        // ---- mask on edge tiles only
+        // ---- mask on edge tiles only (offsets are small there, so 32-bit)
         const int64_t kp0 = a.k_pos0 + j0;
         const bool full = (j0 + NK <= a.Tk) && (kp0 + NK - 1 <= qp_lo) &&
                           (a.window == 0 || qp_hi - kp0 < a.window);
         if (!full) {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const int64_t qp = a.q_pos0 + q0 + 32 * nb + l32;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int jrel = 32 * kb + 16 * (e >> 3) + 8 * h2 + (e & 7);
-                        const int64_t kp = kp0 + jrel;
-                        const bool vis = (j0 + jrel < a.Tk) && (kp <= qp) &&
-                                         (a.window == 0 || qp - kp < a.window);
-                        if (!vis) S[kb][nb][e] = kNegInf;
-                    }
-            }
-        }
-
-        // ---- online softmax (exp2 domain), lazy rescale
-        bool need[NB];
-        float mc[NB];
-        bool any_need = false;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            float mx = kNegInf;
+            int64_t d64 = qp - kp0;
+            d64 = d64 < -(1 << 30) ? -(1 << 30) : (d64 > (1 << 30) ? (1 << 30) : d64);
+            const int d = (int)d64;                 // query position - first key position
+            const int kmax = a.Tk - j0;             // keys past the end of k/v
+            const int win = a.window > 0 ? a.window : 0x7fffffff;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, S[kb][nb][e]);
-            mx = max_xor32(mx);
-            mc[nb] = mx * cl2;
-            need[nb] = mc[nb] > m_run[nb] + 8.0f;
-            any_need |= need[nb];
-        }
-        if (__any(any_need)) {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const float alpha = need[nb] ? __builtin_amdgcn_exp2f(m_run[nb] - mc[nb]) : 1.0f;
-                if (need[nb]) m_run[nb] = mc[nb];
-                l_run[nb] *= alpha;
-#pragma unroll
-                for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) O[mb][nb][e] *= alpha;
-            }
-        }
-        u32x4 P[2][2][NB];   // [kb][s][nb]
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const float mu = (m_run[nb] == kNegInf) ? 0.0f : m_run[nb];
-            float ls = 0.0f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][nb][e], cl2, -mu));
-                    S[kb][nb][e] = p;
-                    ls += p;
+                    const int jrel = 32 * kb + 16 * (e >> 3) + 8 * h2 + (e & 7);
+                    const bool vis = (jrel < kmax) && (jrel <= d) && (d - jrel < win);
+                    if (!vis) S[kb][e] = kNegInf;
                 }
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-#pragma unroll
-                    for (int x = 0; x < 4; ++x)
-                        P[kb][s][nb][x] = pack_bf16(S[kb][nb][8 * s + 2 * x], S[kb][nb][8 * s + 2 * x + 1]);
-            }
-            l_run[nb] += ls;
         }
 
-        // ---- O^T += V^T P^T
+        // ---- online softmax (exp2 domain), lazy rescale
+        float mx = kNegInf;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, S[kb][e]);
+        mx = max_xor32(mx);
+        const float mc = mx * cl2;
+        const bool need = mc > m_run + 8.0f;
+        if (__any(need)) {
+            const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mc) : 1.0f;
+            if (need) m_run = mc;
+            l_run *= alpha;
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const u32x4 vf = lds128(Vs + (32 * mb + l32) * VSTR + 32 * kb + 16 * s + 8 * h2);
+            for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) O[mb][nb] = mfma32(vf, P[kb][s][nb], O[mb][nb]);
-                }
+                for (int e = 0; e < 16; ++e) O[mb][e] *= alpha;
+        }
+        const float mu = (m_run == kNegInf) ? 0.0f : m_run;
+        u32x4 P[2][2];   // [kb][s]
+        float ls = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e], cl2, -mu));
+                S[kb][e] = p;
+                ls += p;
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    P[kb][s][x] = pack_bf16(S[kb][8 * s + 2 * x], S[kb][8 * s + 2 * x + 1]);
+        }
+        l_run += ls;
+
+        // ---- O^T += V^T P^T, 4 fragment reads in flight
+        {
+            const uint16_t *vr0 = Vs + l32 * VSTR + 8 * h2;
+            auto vaddr = [&](int i) {   // i = 4*mb + 2*kb + s
+                return vr0 + (i >> 2) * 32 * VSTR + 32 * ((i >> 1) & 1) + 16 * (i & 1);
+            };
+            u32x4 vf[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vf[i] = lds128(vaddr(i));
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                O[i >> 2] = mfma32(vf[i & 3], P[(i >> 1) & 1][i & 1], O[i >> 2]);
+                if (i + 4 < 16) vf[i & 3] = lds128(vaddr(i + 4));
             }
         }
 
@@ -351,32 +339,28 @@ void prefill_kernel(PrefillArgs a) {
     }
 
     // ---- epilogue: o = v_scale * O / l, bf16
+    const float lt = sum_xor32(l_run);
+    const int t = q0 + l32;
+    if (t < a.Tq) {
+        const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
+        uint16_t *dst = a.out + (((size_t)b * a.Tq + t) * a.Hq + head) * kDv;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const float lt = sum_xor32(l_run[nb]);
-        const int t = q0 + 32 * nb + l32;
-        if (t < a.Tq) {
-            const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
-            uint16_t *dst = a.out + (((size_t)b * a.Tq + t) * a.Hq + head) * kDv;
+        for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                for (int a4 = 0; a4 < 4; ++a4) {
-                    u32x2 o;
-                    o[0] = pack_bf16(O[mb][nb][4 * a4] * inv, O[mb][nb][4 * a4 + 1] * inv);
-                    o[1] = pack_bf16(O[mb][nb][4 * a4 + 2] * inv, O[mb][nb][4 * a4 + 3] * inv);
-                    *reinterpret_cast<u32x2 *>(dst + 32 * mb + 8 * a4 + 4 * h2) = o;
-                }
-            if (a.lse && h2 == 0)
-                a.lse[((size_t)b * a.Hq + head) * a.Tq + t] =
-                    lt > 0.0f ? (m_run[nb] + log2f(lt)) * kLn2 : kNegInf;
-        }
+            for (int a4 = 0; a4 < 4; ++a4) {
+                u32x2 o;
+                o[0] = pack_bf16(O[mb][4 * a4] * inv, O[mb][4 * a4 + 1] * inv);
+                o[1] = pack_bf16(O[mb][4 * a4 + 2] * inv, O[mb][4 * a4 + 3] * inv);
+                *reinterpret_cast<u32x2 *>(dst + 32 * mb + 8 * a4 + 4 * h2) = o;
+            }
+        if (a.lse && h2 == 0)
+            a.lse[((size_t)b * a.Hq + head) * a.Tq + t] = lt > 0.0f ? (m_run + log2f(lt)) * kLn2 : kNegInf;
     }
 }
 
-template <int NB, int NW>
+template <int NW>
 static hipError_t launch_variant(PrefillArgs a, hipStream_t stream) {
-    const int QW = 32 * NB;
+    const int QW = 32;
     const int G = a.Hq / a.Hkv;
     a.n_qblk = (a.Tq + QW - 1) / QW;
     a.n_hgrp = G / NW;
@@ -384,18 +368,15 @@ static hipError_t launch_variant(PrefillArgs a, hipStream_t stream) {
     const int64_t blocks = combos * a.n_qblk;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     a.xcd_remap = (combos % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((prefill_kernel<NB, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, a);
     return hipGetLastError();
 }
 
-#ifndef MIMO_PREFILL_NB
-#define MIMO_PREFILL_NB 2
-#endif
-
 hipError_t launch_prefill(PrefillArgs a, hipStream_t stream) {
-    // group sizes are multiples of 4 (checked by the caller)
-    if (MIMO_PREFILL_NB == 1 && (a.Hq / a.Hkv) % 8 == 0) return launch_variant<1, 8>(a, stream);
-    return launch_variant<2, 4>(a, stream);
+    // GQA group sizes are multiples of 4 (checked by the caller); 8 heads share a
+    // workgroup when the group allows it.
+    if ((a.Hq / a.Hkv) % 8 == 0) return launch_variant<8>(a, stream);
+    return launch_variant<4>(a, stream);
 }
 
 }  // namespace mimo
