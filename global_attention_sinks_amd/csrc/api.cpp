@@ -167,8 +167,11 @@ mimo_status mimo_attn_decode(const mimo_attn_cfg *cfg, int32_t S, const uint16_t
     if (G > 16) return fail(MIMO_ERR_UNSUPPORTED, "decode needs a GQA group size <= 16 (got %d)", G);
     if (cfg->window > 0 && cap < cfg->window)
         return fail(MIMO_ERR_INVALID_ARGUMENT, "a ring cache needs cap (%d) >= window (%d)", cap, cfg->window);
-    if ((int64_t)S * cfg->num_kv_heads > 65535)
-        return fail(MIMO_ERR_UNSUPPORTED, "S * num_kv_heads must be <= 65535");
+    if (cfg->num_kv_heads > 8)
+        return fail(MIMO_ERR_UNSUPPORTED, "decode needs num_kv_heads <= 8 (got %d)", cfg->num_kv_heads);
+    if (S > 65535) return fail(MIMO_ERR_UNSUPPORTED, "decode needs S <= 65535");
+    if ((int64_t)cap > (int64_t)kDecodeChunk * kDecodeMaxSplits)
+        return fail(MIMO_ERR_UNSUPPORTED, "decode needs cap <= %lld", (long long)kDecodeChunk * kDecodeMaxSplits);
     if (S == 0) return ok();
     if (!q || !q_pos || !k_cache || !v_cache || !out)
         return fail(MIMO_ERR_INVALID_ARGUMENT, "q, q_pos, k_cache, v_cache and out must be non-NULL");

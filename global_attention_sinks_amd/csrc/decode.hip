@@ -2,27 +2,27 @@
 // layer types (sliding layers over their window-sized ring, Gaudi recipe page,
 // Launch section; global layers over a long cache).  Split-K flash decoding:
 //
-//   pass 1 (decode_partial_kernel): one workgroup per (sequence, KV head,
-//     chunk of kDecodeChunk cache slots); its 4 waves take interleaved 32-key
-//     steps.  Per step a wave computes S^T = K Q^T for the GQA group's query
-//     heads (<= 16, the N side of a 16x16x32 bf16 MFMA) and O^T += V^T P^T.
-//     K is read straight from HBM in operand layout (each lane reads 96
-//     contiguous bytes of a key row); V is read row-major and transposed in
-//     registers with byte permutes.  The next step's K/V are in flight while
-//     the current one is computed.  The 4 wave partials (max, sum, O) merge
-//     through LDS; a sequence whose slots fit one chunk writes its output here.
-//   pass 2 (decode_combine_kernel): merges the chunk partials of longer
-//     sequences by their log-sum-exp.
+//   pass 1 (decode_partial_kernel): one workgroup per (sequence, chunk of
+//     kDecodeChunk cache slots) with one wave per KV head, so a workgroup
+//     streams whole token rows [slot][all KV heads] of the cache.  Per 32-key
+//     step a wave computes S^T = K Q^T for its GQA group's query heads (<= 16,
+//     the N side of a 16x16x32 bf16 MFMA) and O^T += V^T P^T.  K is read
+//     straight from HBM in operand layout (each lane reads 96 contiguous bytes
+//     of a key row); V is read row-major and transposed in registers with byte
+//     permutes.  The next step's K/V loads are in flight while the current step
+//     is computed.  A sequence whose live slots fit one chunk writes its output
+//     directly; otherwise the wave writes its (max, sum, O) partial.
+//   pass 2 (decode_combine_kernel): merges the chunk partials by their
+//     log-sum-exp.
 //
 // The sink logit (techniques map page, Learnable attention sink) is folded into
-// chunk 0 / wave 0 as the initial (max, sum) = (sink * log2 e, 1).
+// chunk 0 as the initial (max, sum) = (sink * log2 e, 1).
 #include "kernels.hpp"
 
 namespace mimo {
 
 namespace {
 
-constexpr int NWD = 4;   // waves per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 
@@ -31,9 +31,9 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 // Number of cache slots a query at position p can see (slots >= this hold nothing).
-__device__ __forceinline__ int64_t live_slots(int64_t p, int32_t cap) {
+__device__ __forceinline__ int live_slots(int64_t p, int32_t cap) {
     if (p < 0) return 0;
-    return p + 1 < cap ? p + 1 : cap;
+    return p + 1 < cap ? (int)(p + 1) : cap;
 }
 
 struct StepBuf {
@@ -43,20 +43,16 @@ struct StepBuf {
 
 }  // namespace
 
-__global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
-    __shared__ float sm_o[NWD][16][kDv + 4];
-    __shared__ float sm_m[NWD][16], sm_l[NWD][16];
-
+__global__ __launch_bounds__(512) void decode_partial_kernel(DecodeArgs a) {
     const int sp = blockIdx.x;
-    const int sg = blockIdx.y;
-    const int s = sg / a.Hkv, g = sg - s * a.Hkv;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int s = blockIdx.y;
+    const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;   // one wave per KV head
     const int lg = lane >> 4, r16 = lane & 15;
     const int G = a.Hq / a.Hkv;
 
     const int64_t p = a.pos[s];
-    const int64_t n = live_slots(p, a.cap);
-    const int nsplit = (int)((n + kDecodeChunk - 1) / kDecodeChunk);
+    const int n = live_slots(p, a.cap);
+    const int nsplit = (n + kDecodeChunk - 1) / kDecodeChunk;
     if (sp >= (nsplit > 0 ? nsplit : 1)) return;
 
     const int head = g * G + r16;
@@ -82,7 +78,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
     }
 
     float m_run, l_run;
-    if (sp == 0 && w == 0 && a.sinks && head_ok) {
+    if (sp == 0 && a.sinks && head_ok) {
         m_run = a.sinks[head] * kLog2e;
         l_run = (lg == 0) ? 1.0f : 0.0f;
     } else {
@@ -96,35 +92,41 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
     const size_t krs = (size_t)a.Hkv * kDqk, vrs = (size_t)a.Hkv * kDv;
     const uint16_t *kbase = a.k_cache + (size_t)s * a.cap * krs + (size_t)g * kDqk + 48 * lg;
     const uint16_t *vbase = a.v_cache + (size_t)s * a.cap * vrs + (size_t)g * kDv + 8 * r16;
-    const int64_t kbeg = (int64_t)sp * kDecodeChunk;
-    const int64_t kend = (kbeg + kDecodeChunk < n) ? kbeg + kDecodeChunk : n;
+    const int kbeg = sp * kDecodeChunk;
+    const int kend = (kbeg + kDecodeChunk < n) ? kbeg + kDecodeChunk : n;
     const float cl2 = a.scale_log2;
+    // ring rule: slot j holds position p - ((p - j) mod cap); with pm = p mod cap
+    // that distance is pm - j, or pm - j + cap when j > pm
+    const int pm = p >= 0 ? (int)(p % a.cap) : 0;
+    const int win = a.window > 0 ? a.window : 0x7fffffff;
+    const int64_t pcap = p;
 
-    auto load = [&](StepBuf &bf, int64_t j0) {
+    auto load = [&](StepBuf &bf, int j0) {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
-            const int64_t j = j0 + 16 * sb + r16;
+            const int j = j0 + 16 * sb + r16;
 #pragma unroll
             for (int ch = 0; ch < 6; ++ch)
-                bf.k[sb][ch] = (j < a.cap) ? ldg128(kbase + j * krs + 8 * ch) : u32x4{0, 0, 0, 0};
+                bf.k[sb][ch] = (j < a.cap) ? ldg128(kbase + (size_t)j * krs + 8 * ch) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-            const int64_t j = j0 + 16 * (jj >> 2) + 4 * lg + (jj & 3);
-            bf.v[jj] = (j < a.cap) ? ldg128(vbase + j * vrs) : u32x4{0, 0, 0, 0};
+            const int j = j0 + 16 * (jj >> 2) + 4 * lg + (jj & 3);
+            bf.v[jj] = (j < a.cap) ? ldg128(vbase + (size_t)j * vrs) : u32x4{0, 0, 0, 0};
         }
     };
 
-    auto visible = [&](int64_t j) -> bool {
+    auto visible = [&](int j) -> bool {
         if (j >= n) return false;
         if (a.window > 0) {
-            const int64_t t = p - ((p - j) % a.cap);   // position held by slot j
-            return p - t < a.window;
+            int d = pm - j;
+            if (d < 0) d += a.cap;
+            return d < win && (int64_t)d <= pcap;
         }
         return true;
     };
 
-    auto compute = [&](StepBuf &bf, int64_t j0) {
+    auto compute = [&](StepBuf &bf, int j0) {
         f32x4 S[2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
@@ -133,20 +135,19 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
             for (int ch = 0; ch < 6; ++ch) S[sb] = mfma16(bf.k[sb][ch], qf[ch], S[sb]);
         }
         // lane's keys: j0 + 16*sb + 4*lg + i  (rows of its S^T registers and of its V loads)
+        if (j0 + 32 > kend || a.window > 0) {
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
+            for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (!visible(j0 + 16 * sb + 4 * lg + i)) {
-                    S[sb][i] = kNegInf;
-                    bf.v[4 * sb + i] = u32x4{0, 0, 0, 0};
+                for (int i = 0; i < 4; ++i) {
+                    if (!visible(j0 + 16 * sb + 4 * lg + i)) {
+                        S[sb][i] = kNegInf;
+                        bf.v[4 * sb + i] = u32x4{0, 0, 0, 0};
+                    }
                 }
-            }
-        float mx = kNegInf;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, S[sb][i]);
+        }
+        float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
+                         fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
         mx = max_xor16(mx);
         mx = max_xor32(mx);
         const float mc = mx * cl2;
@@ -188,92 +189,90 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
 
     {
         StepBuf A, B;
-        const int64_t stride = 32 * NWD;
-        int64_t j0 = kbeg + 32 * w;
+        int j0 = kbeg;
         if (j0 < kend) load(A, j0);
         while (j0 < kend) {
-            int64_t j1 = j0 + stride;
+            int j1 = j0 + 32;
             if (j1 < kend) load(B, j1);
             compute(A, j0);
             j0 = j1;
             if (j0 >= kend) break;
-            j1 = j0 + stride;
+            j1 = j0 + 32;
             if (j1 < kend) load(A, j1);
             compute(B, j0);
             j0 = j1;
         }
     }
 
-    // ---- merge the 4 waves through LDS
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sm_o[w][r16][8 * (4 * lg + i) + t] = O[t][i];
-    if (lg == 0) {
-        sm_m[w][r16] = m_run;
-        sm_l[w][r16] = l_run;
-    }
-    __syncthreads();
-
-    const int hh = tid >> 4;          // head within the group
-    const int d0 = (tid & 15) * 8;    // 8 dv per thread
-    if (hh >= G) return;
-    float M = kNegInf;
-#pragma unroll
-    for (int ww = 0; ww < NWD; ++ww) M = fmaxf(M, sm_m[ww][hh]);
-    float L = 0.0f, o[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = 0.0f;
-#pragma unroll
-    for (int ww = 0; ww < NWD; ++ww) {
-        const float mw = sm_m[ww][hh];
-        const float sc = (mw == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-        L += sm_l[ww][hh] * sc;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] += sm_o[ww][hh][d0 + e] * sc;
-    }
-    const int qh = g * G + hh;
+    // ---- this wave's partial for its heads: lane (lg, r16) holds, for each i,
+    // dv [32*lg + 8*i, +8) of head r16 in O[0..7][i]
+    l_run = sum_xor16(l_run);
+    l_run = sum_xor32(l_run);
+    if (!head_ok) return;
     if (nsplit <= 1) {
-        const float inv = L > 0.0f ? a.v_scale / L : 0.0f;
-        u32x4 r;
+        const float inv = l_run > 0.0f ? a.v_scale / l_run : 0.0f;
+        uint16_t *dst = a.out + ((size_t)s * a.Hq + head) * kDv + 32 * lg;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = pack_bf16(o[2 * e] * inv, o[2 * e + 1] * inv);
-        stg128(a.out + ((size_t)s * a.Hq + qh) * kDv + d0, r);
+        for (int i = 0; i < 4; ++i) {
+            u32x4 r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = pack_bf16(O[2 * e][i] * inv, O[2 * e + 1][i] * inv);
+            stg128(dst + 8 * i, r);
+        }
     } else {
-        const size_t part = ((size_t)s * a.Hq + qh) * a.n_split_max + sp;
-        float *dst = a.ws_o + part * kDv + d0;
+        const size_t part = ((size_t)s * a.Hq + head) * a.n_split_max + sp;
+        float *dst = a.ws_o + part * kDv + 32 * lg;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dst[e] = o[e];
-        if ((tid & 15) == 0) {
-            a.ws_ml[2 * part] = M;
-            a.ws_ml[2 * part + 1] = L;
+        for (int i = 0; i < 4; ++i) {
+            f32x4 lo = {O[0][i], O[1][i], O[2][i], O[3][i]};
+            f32x4 hi = {O[4][i], O[5][i], O[6][i], O[7][i]};
+            *reinterpret_cast<f32x4 *>(dst + 8 * i) = lo;
+            *reinterpret_cast<f32x4 *>(dst + 8 * i + 4) = hi;
+        }
+        if (lg == 0) {
+            a.ws_ml[2 * part] = m_run;
+            a.ws_ml[2 * part + 1] = l_run;
         }
     }
 }
 
 // One workgroup of 128 threads (one per dv) per (sequence, query head).
 __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
+    __shared__ float wsc[kDecodeMaxSplits];
+    __shared__ float red[2][4];
     const int s = blockIdx.x / a.Hq;
     const int qh = blockIdx.x - s * a.Hq;
-    const int64_t n = live_slots(a.pos[s], a.cap);
-    const int nsplit = (int)((n + kDecodeChunk - 1) / kDecodeChunk);
+    const int n = live_slots(a.pos[s], a.cap);
+    const int nsplit = (n + kDecodeChunk - 1) / kDecodeChunk;
     if (nsplit <= 1) return;
     const size_t part0 = ((size_t)s * a.Hq + qh) * a.n_split_max;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // 1) max over the chunk maxima
     float M = kNegInf;
-    for (int i = 0; i < nsplit; ++i) M = fmaxf(M, a.ws_ml[2 * (part0 + i)]);
-    float L = 0.0f, o = 0.0f;
-    const int d = threadIdx.x;
-    for (int i = 0; i < nsplit; ++i) {
+    for (int i = tid; i < nsplit; i += 128) M = fmaxf(M, a.ws_ml[2 * (part0 + i)]);
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    if (lane == 0) red[0][w] = M;
+    __syncthreads();
+    M = fmaxf(red[0][0], red[0][1]);
+    // 2) chunk weights and the total sum
+    float L = 0.0f;
+    for (int i = tid; i < nsplit; i += 128) {
         const float mi = a.ws_ml[2 * (part0 + i)];
         const float sc = (mi == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(mi - M);
+        wsc[i] = sc;
         L += a.ws_ml[2 * (part0 + i) + 1] * sc;
-        o += a.ws_o[(part0 + i) * kDv + d] * sc;
     }
+    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
+    if (lane == 0) red[1][w] = L;
+    __syncthreads();
+    L = red[1][0] + red[1][1];
+    // 3) weighted sum of the partial outputs
+    float o = 0.0f;
+    const float *src = a.ws_o + part0 * kDv + tid;
+    for (int i = 0; i < nsplit; ++i) o += src[(size_t)i * kDv] * wsc[i];
     const float r = L > 0.0f ? o * (a.v_scale / L) : 0.0f;
     const uint32_t pk = pack_bf16(r, 0.0f);
-    a.out[((size_t)s * a.Hq + qh) * kDv + d] = (uint16_t)(pk & 0xffffu);
+    a.out[((size_t)s * a.Hq + qh) * kDv + tid] = (uint16_t)(pk & 0xffffu);
 }
 
 size_t decode_workspace_bytes(int32_t S, int32_t Hq, int32_t cap) {
@@ -284,11 +283,9 @@ size_t decode_workspace_bytes(int32_t S, int32_t Hq, int32_t cap) {
 
 hipError_t launch_decode(DecodeArgs a, hipStream_t stream) {
     a.n_split_max = (int)(((int64_t)a.cap + kDecodeChunk - 1) / kDecodeChunk);
-    if (a.n_split_max > 1) {
-        a.ws_ml = a.ws_o + (size_t)a.S * a.Hq * a.n_split_max * kDv;
-    }
-    hipLaunchKernelGGL(decode_partial_kernel, dim3(a.n_split_max, a.S * a.Hkv), dim3(64 * NWD), 0,
-                       stream, a);
+    if (a.n_split_max > kDecodeMaxSplits) return hipErrorInvalidValue;
+    if (a.n_split_max > 1) a.ws_ml = a.ws_o + (size_t)a.S * a.Hq * a.n_split_max * kDv;
+    hipLaunchKernelGGL(decode_partial_kernel, dim3(a.n_split_max, a.S), dim3(64 * a.Hkv), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_split_max <= 1) return e;
     hipLaunchKernelGGL(decode_combine_kernel, dim3(a.S * a.Hq), dim3(kDv), 0, stream, a);

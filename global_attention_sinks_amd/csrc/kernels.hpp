@@ -35,7 +35,8 @@ struct PrefillArgs {
 hipError_t launch_prefill(PrefillArgs a, hipStream_t stream);
 
 // ---- decode (decode.hip)
-constexpr int kDecodeChunk = 2048;   // keys per split
+constexpr int kDecodeChunk = 1024;       // cache slots per split
+constexpr int kDecodeMaxSplits = 1024;   // so caches of up to 1M slots
 struct DecodeArgs {
     const uint16_t *q, *k_cache, *v_cache;
     const int64_t *pos;

@@ -35,8 +35,10 @@
  *   - Sizes of 0 (no tokens, no sequences) are valid and enqueue nothing.
  *   - Supported head geometry: head_dim_qk 192, head_dim_v 128, rope_dim 64,
  *     num_q_heads a multiple of num_kv_heads; prefill needs a GQA group size
- *     (num_q_heads / num_kv_heads) that is a multiple of 4, decode a group
- *     size of at most 16.  Anything else returns MIMO_ERR_UNSUPPORTED.
+ *     (num_q_heads / num_kv_heads) that is a multiple of 4; decode needs a
+ *     group size of at most 16, at most 8 KV heads, at most 65535 sequences
+ *     and caches of at most 2^20 slots.  Anything else returns
+ *     MIMO_ERR_UNSUPPORTED.
  */
 #ifndef MIMO_ATTN_H
 #define MIMO_ATTN_H

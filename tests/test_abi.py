@@ -120,6 +120,8 @@ def test_decode_contract(lib):
     assert "cap" in err(lib)
     assert dec(lib, cfg_swa(), S=-1) == INVAL
     assert dec(lib, cfg_swa(num_kv_heads=2), cap=128) == UNSUP   # group 32 > 16
+    assert dec(lib, cfg_swa(num_q_heads=64, num_kv_heads=16), cap=128) == UNSUP   # 16 KV heads
+    assert dec(lib, cfg_glob(), cap=(1 << 20) + 1) == UNSUP
     assert dec(lib, cfg_glob(), q=None) == INVAL
     assert dec(lib, cfg_glob(), S=0, q=None) == OK
 
@@ -127,8 +129,8 @@ def test_decode_contract(lib):
 def test_decode_workspace(lib):
     g = cfg_glob()
     need = lib.mimo_attn_decode_workspace_size(ctypes.byref(g), 16, 131072)
-    # partial (max, sum, 128 outputs) in fp32 per (sequence, head, 2048-slot chunk)
-    assert need == 16 * 64 * (131072 // 2048) * (128 + 2) * 4
+    # partial (max, sum, 128 outputs) in fp32 per (sequence, head, 1024-slot chunk)
+    assert need == 16 * 64 * (131072 // 1024) * (128 + 2) * 4
     assert lib.mimo_attn_decode_workspace_size(ctypes.byref(cfg_swa()), 64, 128) == 0
     assert dec(lib, g, S=16, cap=131072, ws=None, ws_bytes=0) == WS
     assert dec(lib, g, S=16, cap=131072, ws_bytes=need - 1) == WS
