@@ -60,6 +60,35 @@ def prefill_bytes(B, Tq, Tk, hq, hkv, sinks: bool) -> int:
     return B * (Tq * hq * 192 * 2 + Tk * hkv * (192 + 128) * 2 + Tq * hq * 128 * 2) + (hq * 4 if sinks else 0)
 
 
+# ------------------------------------------------------------ HBM traffic from the committed profile
+
+_PREFILL_SOURCES = ["global_attention_sinks_amd/csrc/prefill.hip", "global_attention_sinks_amd/csrc/common.hpp",
+                    "global_attention_sinks_amd/csrc/kernels.hpp"]
+_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hot_path_step_hbm_traffic.md")
+
+
+def profiled_traffic(workload_label: str):
+    """Bytes one launch moved to and from HBM, as the committed FETCH_SIZE / WRITE_SIZE
+    profile recorded them (already scaled by the copy calibration), or None when the
+    profile is missing or the kernel source changed since it was taken."""
+    import hashlib
+    import re
+    if not os.path.exists(_TRAFFIC_PROFILE):
+        return None
+    text = open(_TRAFFIC_PROFILE).read()
+    h = hashlib.sha256()
+    for f in _PREFILL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    m = re.search(r"prefill sha256\[:16\] ([0-9a-f]{16})", text)
+    if not m or m.group(1) != h.hexdigest()[:16]:
+        return None
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.strip("|").split("|")]
+        if len(cells) == 6 and cells[1] == workload_label:
+            return (float(cells[4]) + float(cells[5])) * 1e9
+    return None
+
+
 # ------------------------------------------------------------ workloads
 
 def _dev_bf16(torch, bits):
@@ -194,6 +223,9 @@ def main():
     ap.add_argument("--workload", choices=["layer_step", "long_prefill"], default="layer_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run three 1 GiB device-to-device copies (a known-size reference "
+                         "for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -209,6 +241,15 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("copy calibration: 3 x 1 GiB device-to-device copies done")
 
     if args.workload == "long_prefill":
         return main_long_prefill(args, torch, gen, Bd)
@@ -266,7 +307,8 @@ def main():
     achieved = tf(g["flops"], ms["global_prefill"])
     roofline = {"bound": "mfma", "kernel": "prefill_kernel (global causal, T=32768)",
                 "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None}
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": profiled_traffic("global prefill T32768"),
+                "algorithmic_flops": g["flops"], "algorithmic_bytes": g["bytes"]}
 
     cpu = None
     if not args.no_cpu_baseline:
