@@ -178,9 +178,9 @@ def cpu_baseline_layer_step(ph, budget_s: float):
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     rng = np.random.default_rng(0)
     parts, desc = [], []
-    # sliding prefill: 48 rows per sequence
+    # sliding prefill: ~480 rows per sequence
     d = ph["swa_prefill"]["host"]
-    rows = np.unique(np.concatenate([[0, 127, 128, 8191], rng.integers(0, 8192, 44)]))
+    rows = np.unique(np.concatenate([[0, 127, 128, 8191], rng.integers(0, 8192, 480)]))
     t0 = time.perf_counter()
     oracle.prefill_swa(d["q"], d["k"], d["v"], d["sinks"], window=128, base=1e4, rows=rows, n_threads=threads)
     dt = time.perf_counter() - t0
@@ -189,14 +189,14 @@ def cpu_baseline_layer_step(ph, budget_s: float):
     desc.append(f"sliding prefill {len(rows)} rows x 4 seqs")
     # global prefill: rows spread over the sequence
     d = ph["global_prefill"]["host"]
-    rows = np.unique(np.concatenate([[0, 32767], rng.integers(0, 32768, 14)]))
+    rows = np.unique(np.concatenate([[0, 32767], rng.integers(0, 32768, 126)]))
     t0 = time.perf_counter()
     oracle.prefill_global(d["q"], d["k"], d["v"], base=1e7, rows=rows, n_threads=threads)
     dt = time.perf_counter() - t0
     parts.append((dt, FLOP_PER_PAIR_HEAD * 64 * int(sum(int(r) + 1 for r in rows)), ph["global_prefill"]["flops"]))
     desc.append(f"global prefill {len(rows)} rows")
     # decode: 8 sliding sequences, 2 global sequences
-    for name, seqs, window, base in (("swa", list(range(8)), 128, 1e4), ("global", [0, 1], 0, 1e7)):
+    for name, seqs, window, base in (("swa", list(range(64)), 128, 1e4), ("global", list(range(6)), 0, 1e7)):
         dd = ph["decode"][name]["host"]
         t0 = time.perf_counter()
         oracle.decode(dd["q"], dd["pos"], dd["k_cache"], dd["v_cache"], sinks=dd["sinks"], window=window,
