@@ -6,15 +6,16 @@
 // full causal attention, run one query chunk at a time against its whole
 // prefix (Gaudi recipe page, Launch section: tiled global prefill).
 //
-// Design (one workgroup = NW query heads of one GQA group x 32*NB query tokens;
-// one wave per head):
+// Design (one workgroup = NW query heads of one GQA group x 32 query tokens;
+// one wave per head, two waves per SIMD):
 //   * S^T = K Q^T and O^T = V^T P^T on 32x32x16 bf16 MFMA.  With keys on the
 //     MFMA's M side, every lane owns one query column, so the row max / row sum
 //     of the softmax are in-lane plus one permlane32 swap.
 //   * Q lives in registers for the whole kernel (B operand), rotated once on
-//     load.  Each K/V tile of 64 keys is staged once per workgroup in LDS and
-//     read by all NW heads: K rotated on its way in (fused RoPE), V transposed
-//     on its way in (the PV contraction runs over keys).
+//     load.  Each K/V tile of NK keys is staged once per workgroup in LDS
+//     (double-buffered) and read by all NW heads: K rotated on its way in
+//     (fused RoPE; angle = exact fixed-point tile base + per-row offset), V
+//     transposed on its way in (the PV contraction runs over keys).
 //   * K rows are read from LDS in a bit-permuted order (bits 2 and 3 of the row
 //     swapped) so that the S^T accumulator registers of a lane hold 8
 //     consecutive keys, which are exactly its P^T operand for the PV MFMA, with
@@ -25,21 +26,21 @@
 //   * Tiles wholly outside the causal band are never visited; only edge tiles
 //     evaluate the mask.  Workgroups are mapped XCD-aware (each XCD streams the
 //     K/V of one set of KV heads) and longest-first for causal balance.
+//   * Two shapes: 8 heads x 64-key tiles (88 KB of LDS, one workgroup per CU;
+//     long global prefixes) and 4 heads x 32-key tiles (46 KB, two workgroups
+//     per CU so one's prologue and stores overlap the other's math; the short
+//     sliding-window band, where 32-key tiles also waste fewer masked keys).
 #include "kernels.hpp"
 
 namespace mimo {
 
 namespace {
 
-constexpr int NK = 64;                  // keys per tile
 constexpr int KSTR = kDqk + 8;          // LDS row stride of a K tile (bf16)
-constexpr int VSTR = NK + 8;            // LDS row stride of a V^T tile (bf16)
-constexpr int K_TILE = NK * KSTR;
-constexpr int V_TILE = kDv * VSTR;
-constexpr int STAGE = K_TILE + V_TILE;  // elements per pipeline stage
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
+constexpr int RING = 4;                 // LDS fragment reads issued ahead of their MFMA
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
@@ -51,19 +52,26 @@ __device__ __forceinline__ u32x4 lds128(const uint16_t *p) {
 
 }  // namespace
 
-template <int NW>
+template <int NW, int NK>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillArgs a) {
     constexpr int QW = 32;                          // queries per wave (one MFMA column block)
     constexpr int NT = 64 * NW;
+    constexpr int KB = NK / 32;                     // 32-key MFMA row blocks per tile
+    constexpr int VSTR = NK + 8;                    // LDS row stride of a V^T tile (bf16)
+    constexpr int K_TILE = NK * KSTR;
+    constexpr int V_TILE = kDv * VSTR;
+    constexpr int STAGE = K_TILE + V_TILE;
     // staging work per tile, spread evenly over the NT threads
     constexpr int ROT_UNITS = NK * 8;               // (row, 4 rotating pairs): 8-byte pieces
     constexpr int PLAIN_UNITS = NK * 16;            // (row, 16-byte pass-through chunk)
     constexpr int V_UNITS = (NK / 2) * 16;          // (key pair, 8-dv chunk)
     constexpr int ROT_PER = ROT_UNITS / NT, PLAIN_PER = PLAIN_UNITS / NT, V_PER = V_UNITS / NT;
     static_assert(ROT_UNITS % NT == 0 && PLAIN_UNITS % NT == 0 && V_UNITS % NT == 0, "staging split");
+    static_assert(NK % 32 == 0, "tile of whole MFMA blocks");
 
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+    __shared__ float2 rope_base[2][kPairs];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -136,41 +144,78 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) O[mb][e] = 0.0f;
 
-    // ---- staging registers for the next tile
+    // ---- staging: fixed per-thread pieces of every tile
+    // rotating K piece r: row u>>3, pairs 4*(u&7)..+3; pass-through chunk r: row u>>4,
+    // chunk 8+(u&15); V block r: key pair u%(NK/2) (consecutive lanes), 8-dv chunk u/(NK/2)
+    int k_rot_off[ROT_PER], k_rot_row[ROT_PER], k_pl_off[PLAIN_PER], v_off[V_PER];
+    float rope_oc[ROT_PER][4], rope_os[ROT_PER][4];   // cos/sin(row * theta) of the piece's pairs
+#pragma unroll
+    for (int r = 0; r < ROT_PER; ++r) {
+        const int u = tid + r * NT, row = u >> 3, hq = u & 7;
+        k_rot_row[r] = row;
+        k_rot_off[r] = row * (int)krow_stride + 4 * hq;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) turn_sincos((uint64_t)row * a.rt.turn[4 * hq + e], rope_os[r][e], rope_oc[r][e]);
+    }
+#pragma unroll
+    for (int r = 0; r < PLAIN_PER; ++r) {
+        const int u = tid + r * NT;
+        k_pl_off[r] = (u >> 4) * (int)krow_stride + 8 * (8 + (u & 15));
+    }
+#pragma unroll
+    for (int r = 0; r < V_PER; ++r) {
+        const int u = tid + r * NT;
+        v_off[r] = 2 * (u % (NK / 2)) * (int)vrow_stride + 8 * (u / (NK / 2));
+    }
+    // exact cos/sin(tile position * theta_i) for the 32 pairs, one tile ahead, two
+    // slots; lane i < 32 of wave 0 loads pair i's frequency once
+    const uint64_t my_turn = a.rt.turn[tid & (kPairs - 1)];
+    auto tile_bases = [&](int jt) {
+        if (tid < kPairs) {
+            float sn, cs;
+            turn_sincos((uint64_t)(a.k_pos0 + (int64_t)jt * NK) * my_turn, sn, cs);
+            rope_base[jt & 1][tid] = float2{cs, sn};
+        }
+    };
+
     u32x2 k_rx[ROT_PER], k_ry[ROT_PER];
     u32x4 k_pl[PLAIN_PER], v_st[V_PER][2];
 
     auto load_tile = [&](int jt) {
         const int j0 = jt * NK;
+        const uint16_t *kt = kbase + (size_t)j0 * krow_stride;
+        const uint16_t *vt = vbase + (size_t)j0 * vrow_stride;
+        if (j0 + NK <= a.Tk) {
 #pragma unroll
-        for (int r = 0; r < ROT_PER; ++r) {
-            const int u = tid + r * NT;
-            const int row = u >> 3, hq = u & 7;
-            const int j = j0 + row;
-            if (j < a.Tk) {
-                const uint16_t *p = kbase + (size_t)j * krow_stride + 4 * hq;
-                k_rx[r] = *reinterpret_cast<const u32x2 *>(p);
-                k_ry[r] = *reinterpret_cast<const u32x2 *>(p + 32);
-            } else {
-                k_rx[r] = u32x2{0, 0};
-                k_ry[r] = u32x2{0, 0};
+            for (int r = 0; r < ROT_PER; ++r) {
+                k_rx[r] = *reinterpret_cast<const u32x2 *>(kt + k_rot_off[r]);
+                k_ry[r] = *reinterpret_cast<const u32x2 *>(kt + k_rot_off[r] + 32);
             }
-        }
 #pragma unroll
-        for (int r = 0; r < PLAIN_PER; ++r) {
-            const int u = tid + r * NT;
-            const int row = u >> 4, cc = 8 + (u & 15);
-            const int j = j0 + row;
-            k_pl[r] = (j < a.Tk) ? ldg128(kbase + (size_t)j * krow_stride + 8 * cc) : u32x4{0, 0, 0, 0};
-        }
+            for (int r = 0; r < PLAIN_PER; ++r) k_pl[r] = ldg128(kt + k_pl_off[r]);
 #pragma unroll
-        for (int r = 0; r < V_PER; ++r) {
-            const int u = tid + r * NT;
-            const int kp = u & 31, cc = u >> 5;    // consecutive lanes: consecutive key pairs
+            for (int r = 0; r < V_PER; ++r) {
+                v_st[r][0] = ldg128(vt + v_off[r]);
+                v_st[r][1] = ldg128(vt + v_off[r] + vrow_stride);
+            }
+        } else {   // ragged last tile: rows past Tk are zero
+            const int nrow = a.Tk - j0;
 #pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {
-                const int j = j0 + 2 * kp + rr;
-                v_st[r][rr] = (j < a.Tk) ? ldg128(vbase + (size_t)j * vrow_stride + 8 * cc) : u32x4{0, 0, 0, 0};
+            for (int r = 0; r < ROT_PER; ++r) {
+                const bool ok = k_rot_row[r] < nrow;
+                k_rx[r] = ok ? *reinterpret_cast<const u32x2 *>(kt + k_rot_off[r]) : u32x2{0, 0};
+                k_ry[r] = ok ? *reinterpret_cast<const u32x2 *>(kt + k_rot_off[r] + 32) : u32x2{0, 0};
+            }
+#pragma unroll
+            for (int r = 0; r < PLAIN_PER; ++r) {
+                const int u = tid + r * NT;
+                k_pl[r] = ((u >> 4) < nrow) ? ldg128(kt + k_pl_off[r]) : u32x4{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int r = 0; r < V_PER; ++r) {
+                const int u = tid + r * NT, k2 = 2 * (u % (NK / 2));
+                v_st[r][0] = (k2 < nrow) ? ldg128(vt + v_off[r]) : u32x4{0, 0, 0, 0};
+                v_st[r][1] = (k2 + 1 < nrow) ? ldg128(vt + v_off[r] + vrow_stride) : u32x4{0, 0, 0, 0};
             }
         }
     };
@@ -178,22 +223,22 @@ void prefill_kernel(PrefillArgs a) {
     auto store_tile = [&](int jt, int buf) {
         uint16_t *Ks = smem + buf * STAGE;
         uint16_t *Vs = Ks + K_TILE;
-        const int j0 = jt * NK;
-        const int64_t tile_pos = a.k_pos0 + j0;
 #pragma unroll
         for (int r = 0; r < ROT_PER; ++r) {
             const int u = tid + r * NT;
             const int row = u >> 3, hq = u & 7;
             u32x2 x = k_rx[r], y = k_ry[r];
+            const float4 b01 = *reinterpret_cast<const float4 *>(&rope_base[jt & 1][4 * hq]);
+            const float4 b23 = *reinterpret_cast<const float4 *>(&rope_base[jt & 1][4 * hq + 2]);
+            const float bc[4] = {b01.x, b01.z, b23.x, b23.z}, bs[4] = {b01.y, b01.w, b23.y, b23.w};
 #pragma unroll
             for (int wd = 0; wd < 2; ++wd) {
-                const int i0 = 4 * hq + 2 * wd;
-                // angle(pos0 + row) = tile base + row offset, both as 64-bit turn fractions
-                const uint64_t base0 = (uint64_t)tile_pos * a.rt.turn[i0];
-                const uint64_t base1 = (uint64_t)tile_pos * a.rt.turn[i0 + 1];
-                float s0, c0, s1, c1;
-                turn_sincos(base0 + (uint64_t)row * a.rt.turn[i0], s0, c0);
-                turn_sincos(base1 + (uint64_t)row * a.rt.turn[i0 + 1], s1, c1);
+                // angle(tile position + row) = base(tile) + offset(row)
+                const int e0 = 2 * wd, e1 = 2 * wd + 1;
+                const float c0 = bc[e0] * rope_oc[r][e0] - bs[e0] * rope_os[r][e0];
+                const float s0 = bs[e0] * rope_oc[r][e0] + bc[e0] * rope_os[r][e0];
+                const float c1 = bc[e1] * rope_oc[r][e1] - bs[e1] * rope_os[r][e1];
+                const float s1 = bs[e1] * rope_oc[r][e1] + bc[e1] * rope_os[r][e1];
                 const float x0 = bf_lo(x[wd]), x1 = bf_hi(x[wd]);
                 const float y0 = bf_lo(y[wd]), y1 = bf_hi(y[wd]);
                 x[wd] = pack_bf16(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
@@ -211,7 +256,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int r = 0; r < V_PER; ++r) {
             const int u = tid + r * NT;
-            const int kp = u & 31, cc = u >> 5;
+            const int kp = u % (NK / 2), cc = u / (NK / 2);
             // 2 keys x 8 dv -> 8 dv rows of V^T, one dword (2 keys) each
 #pragma unroll
             for (int d = 0; d < 8; ++d) {
@@ -228,6 +273,9 @@ void prefill_kernel(PrefillArgs a) {
     const int64_t qp = a.q_pos0 + q0 + l32;
 
     if (tile_hi >= tile_lo) {
+        tile_bases(tile_lo);
+        if (tile_lo + 1 <= tile_hi) tile_bases(tile_lo + 1);
+        __syncthreads();
         load_tile(tile_lo);
         store_tile(tile_lo, 0);
     }
@@ -237,27 +285,28 @@ void prefill_kernel(PrefillArgs a) {
         const int buf = (jt - tile_lo) & 1;
         const bool has_next = jt < tile_hi;
         if (has_next) load_tile(jt + 1);
+        if (jt + 2 <= tile_hi) tile_bases(jt + 2);   // slot jt&1: last read by store_tile(jt)
 
         const uint16_t *Ks = smem + buf * STAGE;
         const uint16_t *Vs = Ks + K_TILE;
         const int j0 = jt * NK;
 
-        // ---- S^T = K Q^T: 2 key blocks of 32 x 32 queries, 4 fragment reads in flight
-        f32x16 S[2];
+        // ---- S^T = K Q^T: KB key blocks of 32 x 32 queries, RING fragment reads in flight
+        f32x16 S[KB];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) S[kb][e] = 0.0f;
         {
             const uint16_t *kr0 = Ks + prow * KSTR + 96 * h2;
-            u32x4 kf[4];
+            auto kaddr = [&](int i) { return kr0 + (i % KB) * 32 * KSTR + 8 * (i / KB); };
+            u32x4 kf[RING];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) kf[i] = lds128(kr0 + (i & 1) * 32 * KSTR + 8 * (i >> 1));
+            for (int i = 0; i < RING; ++i) kf[i] = lds128(kaddr(i));
 #pragma unroll
-            for (int i = 0; i < 24; ++i) {
-                const int kb = i & 1, ks = i >> 1;
-                S[kb] = mfma32(kf[i & 3], qr[ks], S[kb]);
-                if (i + 4 < 24) kf[i & 3] = lds128(kr0 + ((i + 4) & 1) * 32 * KSTR + 8 * ((i + 4) >> 1));
+            for (int i = 0; i < 12 * KB; ++i) {
+                S[i % KB] = mfma32(kf[i % RING], qr[i / KB], S[i % KB]);
+                if (i + RING < 12 * KB) kf[i % RING] = lds128(kaddr(i + RING));
             }
         }
 
@@ -272,7 +321,7 @@ void prefill_kernel(PrefillArgs a) {
             const int kmax = a.Tk - j0;             // keys past the end of k/v
             const int win = a.window > 0 ? a.window : 0x7fffffff;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int jrel = 32 * kb + 16 * (e >> 3) + 8 * h2 + (e & 7);
@@ -284,7 +333,7 @@ void prefill_kernel(PrefillArgs a) {
         // ---- online softmax (exp2 domain), lazy rescale
         float mx = kNegInf;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) mx = fmaxf(mx, S[kb][e]);
         mx = max_xor32(mx);
@@ -300,15 +349,15 @@ void prefill_kernel(PrefillArgs a) {
                 for (int e = 0; e < 16; ++e) O[mb][e] *= alpha;
         }
         const float mu = (m_run == kNegInf) ? 0.0f : m_run;
-        u32x4 P[2][2];   // [kb][s]
-        float ls = 0.0f;
+        u32x4 P[KB][2];   // [kb][s]
+        float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e], cl2, -mu));
                 S[kb][e] = p;
-                ls += p;
+                ls[e & 3] += p;
             }
 #pragma unroll
             for (int s = 0; s < 2; ++s)
@@ -316,21 +365,23 @@ void prefill_kernel(PrefillArgs a) {
                 for (int x = 0; x < 4; ++x)
                     P[kb][s][x] = pack_bf16(S[kb][8 * s + 2 * x], S[kb][8 * s + 2 * x + 1]);
         }
-        l_run += ls;
+        l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
-        // ---- O^T += V^T P^T, 4 fragment reads in flight
+        // ---- O^T += V^T P^T, RING fragment reads in flight
         {
             const uint16_t *vr0 = Vs + l32 * VSTR + 8 * h2;
-            auto vaddr = [&](int i) {   // i = 4*mb + 2*kb + s
-                return vr0 + (i >> 2) * 32 * VSTR + 32 * ((i >> 1) & 1) + 16 * (i & 1);
+            // i = (mb, kb, s): dv block mb, key block kb, 16-key step s
+            auto vaddr = [&](int i) {
+                const int mb = i / (2 * KB), kb = (i / 2) % KB, s = i & 1;
+                return vr0 + mb * 32 * VSTR + 32 * kb + 16 * s;
             };
-            u32x4 vf[4];
+            u32x4 vf[RING];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) vf[i] = lds128(vaddr(i));
+            for (int i = 0; i < RING; ++i) vf[i] = lds128(vaddr(i));
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                O[i >> 2] = mfma32(vf[i & 3], P[(i >> 1) & 1][i & 1], O[i >> 2]);
-                if (i + 4 < 16) vf[i & 3] = lds128(vaddr(i + 4));
+            for (int i = 0; i < 8 * KB; ++i) {
+                O[i / (2 * KB)] = mfma32(vf[i % RING], P[(i / 2) % KB][i & 1], O[i / (2 * KB)]);
+                if (i + RING < 8 * KB) vf[i % RING] = lds128(vaddr(i + RING));
             }
         }
 
@@ -358,7 +409,7 @@ void prefill_kernel(PrefillArgs a) {
     }
 }
 
-template <int NW>
+template <int NW, int NK>
 static hipError_t launch_variant(PrefillArgs a, hipStream_t stream) {
     const int QW = 32;
     const int G = a.Hq / a.Hkv;
@@ -368,15 +419,24 @@ static hipError_t launch_variant(PrefillArgs a, hipStream_t stream) {
     const int64_t blocks = combos * a.n_qblk;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     a.xcd_remap = (combos % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((prefill_kernel<NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<NW, NK>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, a);
     return hipGetLastError();
 }
 
+#ifndef MIMO_PREFILL_SHAPE
+#define MIMO_PREFILL_SHAPE 0
+#endif
+
 hipError_t launch_prefill(PrefillArgs a, hipStream_t stream) {
-    // GQA group sizes are multiples of 4 (checked by the caller); 8 heads share a
-    // workgroup when the group allows it.
-    if ((a.Hq / a.Hkv) % 8 == 0) return launch_variant<8>(a, stream);
-    return launch_variant<4>(a, stream);
+    // GQA group sizes are multiples of 4 (checked by the caller).  Sliding
+    // windows see a short band of keys: 4 heads x 32-key tiles, two workgroups
+    // per CU.  Global prefixes are long: 8 heads share each 64-key tile.
+    const bool wide = (a.Hq / a.Hkv) % 8 == 0;
+    int shape = MIMO_PREFILL_SHAPE;
+    if (shape == 0) shape = (a.window > 0 || !wide) ? 2 : 1;
+    if (shape == 1 && wide) return launch_variant<8, 64>(a, stream);
+    if (shape == 4) return launch_variant<4, 64>(a, stream);
+    return launch_variant<4, 32>(a, stream);
 }
 
 }  // namespace mimo
