@@ -7,9 +7,10 @@
 //     streams whole token rows [slot][all KV heads] of the cache.  Per 32-key
 //     step a wave computes S^T = K Q^T for its GQA group's query heads (<= 16,
 //     the N side of a 16x16x32 bf16 MFMA) and O^T += V^T P^T.  K is read
-//     straight from HBM in operand layout (each lane reads 96 contiguous bytes
-//     of a key row); V is read row-major and transposed in registers with byte
-//     permutes.  The next step's K/V loads are in flight while the current step
+//     straight from HBM in operand layout: the contraction order over the 192
+//     dims is chosen so that the 4 lanes of a key row read 64 contiguous bytes
+//     per load and consecutive loads finish each 128-byte line; V is read
+//     row-major and transposed in registers with byte permutes.  The next step's K/V loads are in flight while the current step
 //     is computed.  A sequence whose live slots fit one chunk writes its output
 //     directly; otherwise the wave writes its (max, sum, O) partial.
 //   pass 2 (decode_combine_kernel): merges the chunk partials by their
@@ -36,8 +37,20 @@ __device__ __forceinline__ int live_slots(int64_t p, int32_t cap) {
     return p + 1 < cap ? (int)(p + 1) : cap;
 }
 
+#ifndef MIMO_DECODE_NT
+#define MIMO_DECODE_NT 0
+#endif
+// K/V cache rows are read exactly once: stream them past the caches
+__device__ __forceinline__ u32x4 ldg_stream(const uint16_t *p) {
+#if MIMO_DECODE_NT
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+#else
+    return *reinterpret_cast<const u32x4 *>(p);
+#endif
+}
+
 struct StepBuf {
-    u32x4 k[2][6];   // [16-key sub-block][chunk]: 48 dims of one key row
+    u32x4 k[2][6];   // [16-key sub-block][chunk]: dims 32*ch + 8*lg .. +8 of one key row
     u32x4 v[8];      // 8 key rows x 8 dv
 };
 
@@ -58,23 +71,18 @@ __global__ __launch_bounds__(512) void decode_partial_kernel(DecodeArgs a) {
     const int head = g * G + r16;
     const bool head_ok = r16 < G;
 
-    // ---- q (B operand): head r16, dims 48*lg + 8*ch + e, rotated at p
+    // ---- q (B operand): head r16; contraction slot (ch, lg, e) is dim 32*ch + 8*lg + e,
+    // so the 4 lanes of a K row read 64 contiguous bytes per load instruction.
+    // Chunks 0 and 1 of a lane are rotate-half partners (dims i and i+32).
     u32x4 qf[6];
+    if (head_ok && p >= 0) {
+        const uint16_t *qrow = a.q + ((size_t)s * a.Hq + head) * kDqk + 8 * lg;
 #pragma unroll
-    for (int ch = 0; ch < 6; ++ch) {
-        const int db = 48 * lg + 8 * ch;
-        if (head_ok && p >= 0) {
-            const uint16_t *qrow = a.q + ((size_t)s * a.Hq + head) * kDqk;
-            u32x4 x = ldg128(qrow + db);
-            if (db < kRope) {
-                u32x4 y = ldg128(qrow + (db ^ 32));
-                if (db < 32) rope_rotate8(x, y, a.rt, db, p);
-                else rope_rotate8(y, x, a.rt, db - 32, p);
-            }
-            qf[ch] = x;
-        } else {
-            qf[ch] = u32x4{0, 0, 0, 0};
-        }
+        for (int ch = 0; ch < 6; ++ch) qf[ch] = ldg128(qrow + 32 * ch);
+        rope_rotate8(qf[0], qf[1], a.rt, 8 * lg, p);
+    } else {
+#pragma unroll
+        for (int ch = 0; ch < 6; ++ch) qf[ch] = u32x4{0, 0, 0, 0};
     }
 
     float m_run, l_run;
@@ -90,7 +98,7 @@ __global__ __launch_bounds__(512) void decode_partial_kernel(DecodeArgs a) {
     for (int t = 0; t < 8; ++t) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const size_t krs = (size_t)a.Hkv * kDqk, vrs = (size_t)a.Hkv * kDv;
-    const uint16_t *kbase = a.k_cache + (size_t)s * a.cap * krs + (size_t)g * kDqk + 48 * lg;
+    const uint16_t *kbase = a.k_cache + (size_t)s * a.cap * krs + (size_t)g * kDqk + 8 * lg;
     const uint16_t *vbase = a.v_cache + (size_t)s * a.cap * vrs + (size_t)g * kDv + 8 * r16;
     const int kbeg = sp * kDecodeChunk;
     const int kend = (kbeg + kDecodeChunk < n) ? kbeg + kDecodeChunk : n;
@@ -107,12 +115,12 @@ __global__ __launch_bounds__(512) void decode_partial_kernel(DecodeArgs a) {
             const int j = j0 + 16 * sb + r16;
 #pragma unroll
             for (int ch = 0; ch < 6; ++ch)
-                bf.k[sb][ch] = (j < a.cap) ? ldg128(kbase + (size_t)j * krs + 8 * ch) : u32x4{0, 0, 0, 0};
+                bf.k[sb][ch] = (j < a.cap) ? ldg_stream(kbase + (size_t)j * krs + 32 * ch) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
             const int j = j0 + 16 * (jj >> 2) + 4 * lg + (jj & 3);
-            bf.v[jj] = (j < a.cap) ? ldg128(vbase + (size_t)j * vrs) : u32x4{0, 0, 0, 0};
+            bf.v[jj] = (j < a.cap) ? ldg_stream(vbase + (size_t)j * vrs) : u32x4{0, 0, 0, 0};
         }
     };
 

@@ -35,7 +35,10 @@ struct PrefillArgs {
 hipError_t launch_prefill(PrefillArgs a, hipStream_t stream);
 
 // ---- decode (decode.hip)
-constexpr int kDecodeChunk = 1024;       // cache slots per split
+#ifndef MIMO_DECODE_CHUNK
+#define MIMO_DECODE_CHUNK 1024
+#endif
+constexpr int kDecodeChunk = MIMO_DECODE_CHUNK;   // cache slots per split
 constexpr int kDecodeMaxSplits = 1024;   // so caches of up to 1M slots
 struct DecodeArgs {
     const uint16_t *q, *k_cache, *v_cache;
