@@ -173,35 +173,56 @@ def run_layer_step(ph, Bd, ev=None):
 
 def cpu_baseline_layer_step(ph, budget_s: float):
     """Time the fp64 oracle on a bounded sample of each phase and extrapolate
-    each phase by its FLOP count; returns the oracle's step-equivalent rate."""
+    each phase by its FLOP count; returns the oracle's step-equivalent rate.
+
+    Each prefill phase first runs a small pilot sample, then a sample sized to
+    take about a quarter of budget_s; decode runs whole sequences."""
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     rng = np.random.default_rng(0)
     parts, desc = [], []
-    # sliding prefill: ~480 rows per sequence
+    share = budget_s / 4
+
+    def sized(run, n_pilot, n_max):
+        t = run(n_pilot)[0]
+        n = int(min(n_max, max(n_pilot, n_pilot * share / max(t, 1e-3))))
+        return run(n)
+
+    # sliding prefill: random rows of each of the 4 sequences
     d = ph["swa_prefill"]["host"]
-    rows = np.unique(np.concatenate([[0, 127, 128, 8191], rng.integers(0, 8192, 480)]))
-    t0 = time.perf_counter()
-    oracle.prefill_swa(d["q"], d["k"], d["v"], d["sinks"], window=128, base=1e4, rows=rows, n_threads=threads)
-    dt = time.perf_counter() - t0
+
+    def swa_rows(n):
+        rows = np.unique(np.concatenate([[0, 127, 128, 8191], rng.integers(0, 8192, n)]))
+        t0 = time.perf_counter()
+        oracle.prefill_swa(d["q"], d["k"], d["v"], d["sinks"], window=128, base=1e4, rows=rows, n_threads=threads)
+        return time.perf_counter() - t0, rows
+    dt, rows = sized(swa_rows, 64, 8192)
     sample_pairs = 4 * sum(min(int(r) + 1, 128) for r in rows)
     parts.append((dt, FLOP_PER_PAIR_HEAD * 64 * sample_pairs, ph["swa_prefill"]["flops"]))
     desc.append(f"sliding prefill {len(rows)} rows x 4 seqs")
     # global prefill: rows spread over the sequence
-    d = ph["global_prefill"]["host"]
-    rows = np.unique(np.concatenate([[0, 32767], rng.integers(0, 32768, 126)]))
-    t0 = time.perf_counter()
-    oracle.prefill_global(d["q"], d["k"], d["v"], base=1e7, rows=rows, n_threads=threads)
-    dt = time.perf_counter() - t0
+    g = ph["global_prefill"]["host"]
+
+    def glob_rows(n):
+        rows = np.unique(np.concatenate([[0, 32767], rng.integers(0, 32768, n)]))
+        t0 = time.perf_counter()
+        oracle.prefill_global(g["q"], g["k"], g["v"], base=1e7, rows=rows, n_threads=threads)
+        return time.perf_counter() - t0, rows
+    dt, rows = sized(glob_rows, 16, 32768)
     parts.append((dt, FLOP_PER_PAIR_HEAD * 64 * int(sum(int(r) + 1 for r in rows)), ph["global_prefill"]["flops"]))
     desc.append(f"global prefill {len(rows)} rows")
-    # decode: 8 sliding sequences, 2 global sequences
-    for name, seqs, window, base in (("swa", list(range(64)), 128, 1e4), ("global", list(range(6)), 0, 1e7)):
+    # decode: all 64 sliding sequences; global sequences until a quarter of the budget is spent
+    for name, window, base in (("swa", 128, 1e4), ("global", 0, 1e7)):
         dd = ph["decode"][name]["host"]
-        t0 = time.perf_counter()
-        oracle.decode(dd["q"], dd["pos"], dd["k_cache"], dd["v_cache"], sinks=dd["sinks"], window=window,
-                      base=base, seqs=seqs, n_threads=threads)
-        dt = time.perf_counter() - t0
+        seqs, dt = [], 0.0
+        for s in range(dd["q"].shape[0]):
+            if name == "global" and dt >= share:
+                break
+            t0 = time.perf_counter()
+            oracle.decode(dd["q"], dd["pos"], dd["k_cache"], dd["v_cache"], sinks=dd["sinks"], window=window,
+                          base=base, seqs=[s], n_threads=threads)
+            dt += time.perf_counter() - t0
+            seqs.append(s)
         L = [min(int(dd["pos"][s]) + 1, window if window else int(dd["pos"][s]) + 1) for s in seqs]
         parts.append((dt, FLOP_PER_PAIR_HEAD * 64 * sum(L), ph["decode"][name]["flops"]))
         desc.append(f"{name} decode {len(seqs)} seqs")

@@ -153,7 +153,8 @@ mimo_status mimo_attn_prefill_global(const mimo_attn_cfg *cfg, const uint16_t *q
 
 size_t mimo_attn_decode_workspace_size(const mimo_attn_cfg *cfg, int32_t S, int32_t cap) {
     if (!cfg || S <= 0 || cap <= 0 || cfg->num_q_heads <= 0) return 0;
-    return decode_workspace_bytes(S, cfg->num_q_heads, cap);
+    if (cfg->num_kv_heads <= 0 || cfg->num_kv_heads > 8) return 0;
+    return decode_workspace_bytes(S, cfg->num_q_heads, cfg->num_kv_heads);
 }
 
 mimo_status mimo_attn_decode(const mimo_attn_cfg *cfg, int32_t S, const uint16_t *q,
@@ -170,18 +171,17 @@ mimo_status mimo_attn_decode(const mimo_attn_cfg *cfg, int32_t S, const uint16_t
     if (cfg->num_kv_heads > 8)
         return fail(MIMO_ERR_UNSUPPORTED, "decode needs num_kv_heads <= 8 (got %d)", cfg->num_kv_heads);
     if (S > 65535) return fail(MIMO_ERR_UNSUPPORTED, "decode needs S <= 65535");
-    if ((int64_t)cap > (int64_t)kDecodeChunk * kDecodeMaxSplits)
-        return fail(MIMO_ERR_UNSUPPORTED, "decode needs cap <= %lld", (long long)kDecodeChunk * kDecodeMaxSplits);
+    if (cap > kDecodeMaxCap) return fail(MIMO_ERR_UNSUPPORTED, "decode needs cap <= %d", kDecodeMaxCap);
     if (S == 0) return ok();
     if (!q || !q_pos || !k_cache || !v_cache || !out)
         return fail(MIMO_ERR_INVALID_ARGUMENT, "q, q_pos, k_cache, v_cache and out must be non-NULL");
-    const size_t need = decode_workspace_bytes(S, cfg->num_q_heads, cap);
-    if (need > 0 && (!ws || ws_bytes < need))
+    const size_t need = decode_workspace_bytes(S, cfg->num_q_heads, cfg->num_kv_heads);
+    if (!ws || ws_bytes < need)
         return fail(MIMO_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu)", need,
                     ws ? ws_bytes : (size_t)0);
     DecodeArgs a{};
     a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.pos = q_pos; a.sinks = sinks; a.out = out;
-    a.ws_o = (float *)ws; a.ws_ml = nullptr;
+    a.ws_o = (float *)ws;
     a.S = S; a.Hq = cfg->num_q_heads; a.Hkv = cfg->num_kv_heads; a.cap = cap; a.window = cfg->window;
     a.scale_log2 = scale_log2(cfg); a.v_scale = cfg->v_scale;
     a.rt = rope_turns(cfg->rope_base);

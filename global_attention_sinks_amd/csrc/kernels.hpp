@@ -35,23 +35,34 @@ struct PrefillArgs {
 hipError_t launch_prefill(PrefillArgs a, hipStream_t stream);
 
 // ---- decode (decode.hip)
-#ifndef MIMO_DECODE_CHUNK
-#define MIMO_DECODE_CHUNK 1024
+#ifndef MIMO_DECODE_WAVES
+#define MIMO_DECODE_WAVES 1024
 #endif
-constexpr int kDecodeChunk = MIMO_DECODE_CHUNK;   // cache slots per split
-constexpr int kDecodeMaxSplits = 1024;   // so caches of up to 1M slots
+#ifndef MIMO_DECODE_MIN_STEPS
+#define MIMO_DECODE_MIN_STEPS 1
+#endif
+// The batch's 32-slot steps are split evenly over kDecodeWaves / Hkv workgroups
+// (one wave per KV head), each taking at least kDecodeMinSteps steps.
+constexpr int kDecodeWaves = MIMO_DECODE_WAVES;
+constexpr int kDecodeMinSteps = MIMO_DECODE_MIN_STEPS;
+constexpr int kDecodeMaxCap = 1 << 30;
 struct DecodeArgs {
     const uint16_t *q, *k_cache, *v_cache;
     const int64_t *pos;
     const float *sinks;   // nullable
     uint16_t *out;
-    float *ws_o;          // [S, Hq, n_split_max, 128]
-    float *ws_ml;         // [S, Hq, n_split_max, 2]
-    int32_t S, Hq, Hkv, cap, window, n_split_max;
+    float *ws_o;          // [n_groups + S, Hq, 128] partial outputs
+    float *ws_ml;         // [n_groups + S, Hq, 2] partial (max, sum)
+    int64_t *plan_start;  // [S + 1] first step of each sequence; [S] = total steps
+    int32_t *plan_first;  // [S] first workgroup on the sequence
+    int32_t *plan_cover;  // [S] workgroups on the sequence (0: nothing visible)
+    int32_t *plan_part;   // [S] first partial slot of the sequence
+    int32_t *plan_wg_seq; // [n_groups] sequence holding each workgroup's first step
+    int32_t S, Hq, Hkv, cap, window, n_groups;
     float scale_log2, v_scale;
     RopeTurns rt;
 };
-size_t decode_workspace_bytes(int32_t S, int32_t Hq, int32_t cap);
+size_t decode_workspace_bytes(int32_t S, int32_t Hq, int32_t Hkv);
 hipError_t launch_decode(DecodeArgs a, hipStream_t stream);
 
 }  // namespace mimo

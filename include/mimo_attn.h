@@ -37,7 +37,7 @@
  *     num_q_heads a multiple of num_kv_heads; prefill needs a GQA group size
  *     (num_q_heads / num_kv_heads) that is a multiple of 4; decode needs a
  *     group size of at most 16, at most 8 KV heads, at most 65535 sequences
- *     and caches of at most 2^20 slots.  Anything else returns
+ *     and caches of at most 2^30 slots.  Anything else returns
  *     MIMO_ERR_UNSUPPORTED.
  */
 #ifndef MIMO_ATTN_H
@@ -118,8 +118,11 @@ mimo_status mimo_attn_prefill_global(const mimo_attn_cfg *cfg, const uint16_t *q
 /*
  * One decode query per sequence over a KV cache (window-sized ring on sliding
  * layers, Gaudi recipe page, Launch section; a long cache on global layers).
- * Split-K flash decoding: partial results per key chunk go to `ws`, then a
- * combine pass merges them by their log-sum-exp.
+ * Split-K flash decoding balanced over the batch: the visible slots of all
+ * sequences are cut into 32-slot steps and split evenly over a fixed set of
+ * workgroups; a sequence shared by several workgroups gets one partial result
+ * per workgroup in `ws`, and a combine pass merges them by their log-sum-exp.
+ * Three kernels are enqueued (plan, partial, combine); `ws` also holds the plan.
  *   q       : [S, num_q_heads, 192] unrotated; q_pos : [S] int64 positions
  *   k_cache : [S, cap, num_kv_heads, 192] rotated keys (as mimo_kv_ring_append writes)
  *   v_cache : [S, cap, num_kv_heads, 128]
@@ -135,7 +138,8 @@ mimo_status mimo_attn_decode(const mimo_attn_cfg *cfg, int32_t S, const uint16_t
                              int32_t cap, const float *sinks, uint16_t *out, void *ws,
                              size_t ws_bytes, void *stream);
 
-/* Workspace bytes mimo_attn_decode needs for S sequences over caches of cap slots. */
+/* Workspace bytes mimo_attn_decode needs for S sequences over caches of cap
+ * slots (the size does not depend on cap; 0 for an unsupported cfg). */
 size_t mimo_attn_decode_workspace_size(const mimo_attn_cfg *cfg, int32_t S, int32_t cap);
 
 /*

@@ -121,7 +121,7 @@ def test_decode_contract(lib):
     assert dec(lib, cfg_swa(), S=-1) == INVAL
     assert dec(lib, cfg_swa(num_kv_heads=2), cap=128) == UNSUP   # group 32 > 16
     assert dec(lib, cfg_swa(num_q_heads=64, num_kv_heads=16), cap=128) == UNSUP   # 16 KV heads
-    assert dec(lib, cfg_glob(), cap=(1 << 20) + 1) == UNSUP
+    assert dec(lib, cfg_glob(), cap=(1 << 30) + 1) == UNSUP
     assert dec(lib, cfg_glob(), q=None) == INVAL
     assert dec(lib, cfg_glob(), S=0, q=None) == OK
 
@@ -129,12 +129,19 @@ def test_decode_contract(lib):
 def test_decode_workspace(lib):
     g = cfg_glob()
     need = lib.mimo_attn_decode_workspace_size(ctypes.byref(g), 16, 131072)
-    # partial (max, sum, 128 outputs) in fp32 per (sequence, head, 1024-slot chunk)
-    assert need == 16 * 64 * (131072 // 1024) * (128 + 2) * 4
-    assert lib.mimo_attn_decode_workspace_size(ctypes.byref(cfg_swa()), 64, 128) == 0
+    # partials (max, sum, 128 outputs) in fp32 for up to 1024/Hkv workgroup pieces
+    # plus one per sequence, for every query head; then the plan: an int64 step
+    # start per sequence (+1 total), three int32 per sequence and one per workgroup
+    def expect(S, hkv):
+        return (1024 // hkv + S) * 64 * (128 + 2) * 4 + (S + 1) * 8 + 3 * S * 4 + (1024 // hkv) * 4
+    assert need == expect(16, 4)
+    # independent of the cache length
+    assert lib.mimo_attn_decode_workspace_size(ctypes.byref(g), 16, 4096) == need
+    assert lib.mimo_attn_decode_workspace_size(ctypes.byref(cfg_swa()), 64, 128) == expect(64, 8)
     assert dec(lib, g, S=16, cap=131072, ws=None, ws_bytes=0) == WS
     assert dec(lib, g, S=16, cap=131072, ws_bytes=need - 1) == WS
     assert str(need) in err(lib)
+    assert dec(lib, cfg_swa(), S=4, cap=128, ws=None, ws_bytes=0) == WS
 
 
 def test_rope_and_append_contract(lib):

@@ -225,6 +225,24 @@ def test_decode_negative_position_is_empty():
     assert_parity(got[[0, 2]], ref, "out")
 
 
+def test_decode_many_short_sequences():
+    """More sequences than plan threads (several per thread), lengths from empty to
+    a full ring, so the balanced split puts many sequences in one workgroup."""
+    S, cap = 2500, 128
+    rng = np.random.Generator(np.random.PCG64(5004))
+    pos = rng.integers(-1, 400, size=S)
+    pos[:4] = [-1, 0, 127, 128]
+    d = _decode_with_positions(S, cap, 64, 8, 5004, 128, pos, True)
+    say(f"decode sliding S={S} cap={cap}")
+    got = run_decode(d, 64, 8, 128, 1e4, cap)
+    assert np.all(got[pos < 0] == 0.0)
+    seqs = np.unique(np.concatenate([[1, 2, 3, S - 1], rng.integers(0, S, 60)]))
+    seqs = seqs[pos[seqs] >= 0]
+    ref = oracle.decode(d["q"], d["pos"], d["k_cache"], d["v_cache"], sinks=d["sinks"], window=128,
+                        base=1e4, seqs=list(seqs))
+    assert_parity(got[seqs], ref, f"{len(seqs)} of {S} sequences")
+
+
 # ---------------------------------------------------------------- GPU-vs-GPU consistency
 
 def test_append_then_decode_equals_prefill_row():
@@ -237,7 +255,7 @@ def test_append_then_decode_equals_prefill_row():
     vc = torch.full((1, cap, 8, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
     k, v = dev_bf16(d["k"][0]), dev_bf16(d["v"][0])
     sinks = dev(d["sinks"])
-    ws = torch.empty(1, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(Bd.mimo_attn_decode_workspace_size(cfg, 1, cap), dtype=torch.uint8, device="cuda")
     worst = 0.0
     for p in range(T):
         Bd.mimo_kv_ring_append(cfg, k[p:p + 1].contiguous(), v[p:p + 1].contiguous(),
