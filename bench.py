@@ -15,6 +15,11 @@ on the stream the kernels are launched on (torch's current stream).
 --workload long_prefill instead times the 524288-token global prefill run as 8
 query chunks of 65536, each against its full causal prefix.
 
+--workload serving_chunks times packed (THD) serving chunks of 8192 tokens:
+four sliding-window chunks that continue sequences at positions 8192, 65536,
+131072 and 262144 (each with the 127 keys before it) and four global chunks
+after prefixes of 0, 8192, 24576 and 57344 tokens, one packed call each.
+
 The fp64 oracle is timed on a bounded sample of the same workload on the host
 cores (rank 0, N=1) as a CPU baseline.
 """
@@ -241,7 +246,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["layer_step", "long_prefill"], default="layer_step")
+    ap.add_argument("--workload", choices=["layer_step", "long_prefill", "serving_chunks"], default="layer_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -274,6 +279,8 @@ def main():
 
     if args.workload == "long_prefill":
         return main_long_prefill(args, torch, gen, Bd)
+    if args.workload == "serving_chunks":
+        return main_serving_chunks(args, torch, gen, Bd)
 
     ph = setup_layer_step(torch, gen, Bd)
     names = ["swa_prefill", "global_prefill", "append_swa", "append_global", "decode_swa", "decode_global"]
@@ -393,6 +400,79 @@ def main_long_prefill(args, torch, gen, Bd):
                           "traffic": None},
              "cpu_baseline": None,
              "chunks_ms": chunk_ms}
+    print(json.dumps(out_j))
+
+
+def main_serving_chunks(args, torch, gen, Bd):
+    def dev_bf16(bits):
+        return _dev_bf16(torch, bits)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+    C = 8192
+    packs = {}
+    log("setup: packed sliding chunks (4 x 8192, 127 earlier keys each)")
+    starts = [8192, 65536, 131072, 262144]
+    d = gen.varlen_inputs([C] * 4, [C + 127] * 4, 64, 8, seed=1005, with_sinks=True,
+                          k_pos0=[st - 127 for st in starts])
+    packs["sliding"] = dict(cfg=Bd.swa_cfg(), d=d, flops=FLOP_PER_PAIR_HEAD * 64 * 4 * C * 128)
+    log("setup: packed global chunks (4 x 8192 after prefixes 0, 8192, 24576, 57344)")
+    prefix = [0, 8192, 24576, 57344]
+    d = gen.varlen_inputs([C] * 4, [C + p for p in prefix], 64, 4, seed=1006, with_sinks=False)
+    packs["global"] = dict(cfg=Bd.global_cfg(), d=d,
+                           flops=FLOP_PER_PAIR_HEAD * 64 * sum(causal_pairs(p, p + C) for p in prefix))
+    for pk in packs.values():
+        d = pk["d"]
+        hkv = pk["cfg"].num_kv_heads
+        pk.update(q=dev_bf16(d["q"]), k=dev_bf16(d["k"]), v=dev_bf16(d["v"]), cu_q=dev(d["cu_q"]),
+                  cu_k=dev(d["cu_k"]), kpos=None if d["k_pos0"] is None else dev(d["k_pos0"]),
+                  sinks=None if d["sinks"] is None else dev(d["sinks"]),
+                  out=torch.empty((4 * C, 64, 128), dtype=torch.bfloat16, device="cuda"),
+                  bytes=4 * C * 64 * (192 + 128) * 2 + int(d["cu_k"][-1]) * hkv * (192 + 128) * 2)
+        del pk["d"]
+    names = list(packs)
+
+    def step(ev=None):
+        for n in names:
+            pk = packs[n]
+            if ev is not None:
+                ev[n][0].record()
+            Bd.mimo_attn_prefill_varlen(pk["cfg"], pk["q"], pk["k"], pk["v"], pk["sinks"], pk["cu_q"], pk["cu_k"],
+                                        C, pk["out"], k_pos0=pk["kpos"])
+            if ev is not None:
+                ev[n][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    ms = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in evs])) for n in names}
+    flops = sum(pk["flops"] for pk in packs.values())
+    value = flops / (ms_step * 1e-3) / 1e12
+    phases = {}
+    for n, pk in packs.items():
+        t = ms[n] * 1e-3
+        phases[f"{n}_chunks_4x8192"] = {"ms": ms[n], "tflops": pk["flops"] / t / 1e12, "gbs": pk["bytes"] / t / 1e9,
+                                        "frac_mfma_peak": pk["flops"] / t / 1e12 / PEAK_BF16_TFLOPS,
+                                        "frac_hbm_peak": pk["bytes"] / t / 1e9 / PEAK_HBM_GBS}
+    g = phases["global_chunks_4x8192"]
+    out_j = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+             "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+             "vs_baseline": None, "dtype": "bf16", "data": "synthetic: seeded N(0,1) bf16 q/k/v, N(0,1) fp32 sinks",
+             "config": {"workload": "serving_chunks = packed sliding chunks 4x8192 (continuing at 8K..256K) + "
+                                    "packed global chunks 4x8192 (prefixes 0..57344)"},
+             "roofline": {"bound": "mfma", "kernel": "prefill_kernel (packed global chunks)", "achieved": g["tflops"],
+                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": g["frac_mfma_peak"],
+                          "traffic": None},
+             "cpu_baseline": None, "phases": phases}
     print(json.dumps(out_j))
 
 

@@ -62,13 +62,14 @@ def load_library(path: str = LIB_PATH):
     lib.mimo_rope_partial.argtypes = [C, P, P, I64, I32, P, P]
     lib.mimo_attn_prefill_swa.argtypes = [C, P, P, P, P, I32, I32, I64, P, P, P]
     lib.mimo_attn_prefill_global.argtypes = [C, P, P, P, I32, I32, I32, I64, P, P, P]
+    lib.mimo_attn_prefill_varlen.argtypes = [C, P, P, P, P, I32, P, P, P, I32, I32, P, P, P]
     lib.mimo_attn_decode.argtypes = [C, I32, P, P, P, P, I32, P, P, P, ctypes.c_size_t, P]
     lib.mimo_attn_decode_workspace_size.argtypes = [C, I32, I32]
     lib.mimo_attn_decode_workspace_size.restype = ctypes.c_size_t
     lib.mimo_kv_ring_append.argtypes = [C, I32, P, P, P, P, P, I32, P]
     lib.mimo_last_error.restype = ctypes.c_char_p
     for fn in ("mimo_rope_partial", "mimo_attn_prefill_swa", "mimo_attn_prefill_global",
-               "mimo_attn_decode", "mimo_kv_ring_append"):
+               "mimo_attn_prefill_varlen", "mimo_attn_decode", "mimo_kv_ring_append"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -133,6 +134,24 @@ def mimo_attn_prefill_global(cfg: MimoAttnCfg, q, k, v, out, q_pos0: int = 0, ls
     _check("mimo_attn_prefill_global",
            lib.mimo_attn_prefill_global(ctypes.byref(cfg), _p(q), _p(k), _p(v), B, Tq, Tk, q_pos0,
                                         _p(out), _p(lse), _stream(stream)))
+    return out
+
+
+def mimo_attn_prefill_varlen(cfg: MimoAttnCfg, q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                             out, k_pos0=None, lse=None, stream=None):
+    """Packed sequences: q [total_q,Hq,192], k/v [total_k,Hkv,*], out [total_q,Hq,128],
+    cu_seqlens_q / cu_seqlens_k [B+1] int32, k_pos0 [B] int64 or None, lse [Hq,total_q]."""
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, torch.bfloat16, n, 3)
+    _need(cu_seqlens_q, torch.int32, "cu_seqlens_q", 1); _need(cu_seqlens_k, torch.int32, "cu_seqlens_k", 1)
+    _need(k_pos0, torch.int64, "k_pos0", 1); _need(sinks, torch.float32, "sinks", 1)
+    _need(lse, torch.float32, "lse", 2)
+    B = cu_seqlens_q.shape[0] - 1
+    _check("mimo_attn_prefill_varlen",
+           lib.mimo_attn_prefill_varlen(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(sinks), B, _p(cu_seqlens_q),
+                                        _p(cu_seqlens_k), _p(k_pos0), max_seqlen_q, q.shape[0], _p(out),
+                                        _p(lse), _stream(stream)))
     return out
 
 

@@ -125,7 +125,7 @@ mimo_status mimo_attn_prefill_swa(const mimo_attn_cfg *cfg, const uint16_t *q, c
     PrefillArgs a{};
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.sinks = sinks;
     a.B = B; a.Tq = T; a.Tk = T; a.Hq = cfg->num_q_heads; a.Hkv = cfg->num_kv_heads;
-    a.q_pos0 = pos0; a.k_pos0 = pos0; a.window = cfg->window;
+    a.q_pos0 = pos0; a.k_pos0 = pos0; a.window = cfg->window; a.lse_hstride = T;
     a.scale_log2 = scale_log2(cfg); a.v_scale = cfg->v_scale;
     a.rt = rope_turns(cfg->rope_base);
     return from_hip(launch_prefill(a, (hipStream_t)stream), "prefill_swa launch");
@@ -145,10 +145,37 @@ mimo_status mimo_attn_prefill_global(const mimo_attn_cfg *cfg, const uint16_t *q
     PrefillArgs a{};
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.sinks = nullptr;
     a.B = B; a.Tq = Tq; a.Tk = Tk; a.Hq = cfg->num_q_heads; a.Hkv = cfg->num_kv_heads;
-    a.q_pos0 = q_pos0; a.k_pos0 = 0; a.window = 0;
+    a.q_pos0 = q_pos0; a.k_pos0 = 0; a.window = 0; a.lse_hstride = Tq;
     a.scale_log2 = scale_log2(cfg); a.v_scale = cfg->v_scale;
     a.rt = rope_turns(cfg->rope_base);
     return from_hip(launch_prefill(a, (hipStream_t)stream), "prefill_global launch");
+}
+
+mimo_status mimo_attn_prefill_varlen(const mimo_attn_cfg *cfg, const uint16_t *q, const uint16_t *k,
+                                     const uint16_t *v, const float *sinks, int32_t B,
+                                     const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                                     const int64_t *k_pos0, int32_t max_seqlen_q, int32_t total_q,
+                                     uint16_t *out, float *lse, void *stream) {
+    mimo_status st = check_cfg(cfg);
+    if (st != MIMO_OK) return st;
+    if (B < 0 || max_seqlen_q < 0 || total_q < 0)
+        return fail(MIMO_ERR_INVALID_ARGUMENT, "B, max_seqlen_q and total_q must be >= 0");
+    if ((cfg->num_q_heads / cfg->num_kv_heads) % 4 != 0)
+        return fail(MIMO_ERR_UNSUPPORTED, "prefill needs a GQA group size that is a multiple of 4 (got %d)",
+                    cfg->num_q_heads / cfg->num_kv_heads);
+    if (max_seqlen_q > total_q)
+        return fail(MIMO_ERR_INVALID_ARGUMENT, "max_seqlen_q (%d) exceeds total_q (%d)", max_seqlen_q, total_q);
+    if (B == 0 || max_seqlen_q == 0) return ok();
+    if (!q || !k || !v || !out || !cu_seqlens_q || !cu_seqlens_k)
+        return fail(MIMO_ERR_INVALID_ARGUMENT, "q, k, v, out, cu_seqlens_q and cu_seqlens_k must be non-NULL");
+    PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.sinks = sinks;
+    a.B = B; a.Tq = max_seqlen_q; a.Tk = 0; a.Hq = cfg->num_q_heads; a.Hkv = cfg->num_kv_heads;
+    a.window = cfg->window; a.lse_hstride = total_q;
+    a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k; a.kpos = k_pos0;
+    a.scale_log2 = scale_log2(cfg); a.v_scale = cfg->v_scale;
+    a.rt = rope_turns(cfg->rope_base);
+    return from_hip(launch_prefill(a, (hipStream_t)stream), "prefill_varlen launch");
 }
 
 size_t mimo_attn_decode_workspace_size(const mimo_attn_cfg *cfg, int32_t S, int32_t cap) {

@@ -29,6 +29,13 @@ struct PrefillArgs {
     float scale_log2;     // softmax_scale * log2(e)
     float v_scale;
     RopeTurns rt;
+    // packed sequences (all NULL for dense batches): sequence b owns query tokens
+    // cu_q[b]..cu_q[b+1]-1 and key tokens cu_k[b]..cu_k[b+1]-1, its first key sits
+    // at position kpos[b] (0 if kpos is NULL) and its queries are its last keys;
+    // Tq is then the longest query count
+    const int32_t *cu_q, *cu_k;
+    const int64_t *kpos;
+    int64_t lse_hstride;  // lse element stride between heads
     // filled by the launcher
     int32_t n_qblk, n_hgrp, xcd_remap;
 };

@@ -25,7 +25,8 @@
 //     grows by more than 2^8, which keeps every exponent <= 2^8.
 //   * Tiles wholly outside the causal band are never visited; only edge tiles
 //     evaluate the mask.  Workgroups are mapped XCD-aware (each XCD streams the
-//     K/V of one set of KV heads) and longest-first for causal balance.
+//     K/V of one set of KV heads, sequence after sequence of the batch) and
+//     longest-first for causal balance.
 //   * Two shapes: 8 heads x 64-key tiles (88 KB of LDS, one workgroup per CU;
 //     long global prefixes) and 4 heads x 32-key tiles (46 KB, two workgroups
 //     per CU so one's prologue and stores overlap the other's math; the short
@@ -77,42 +78,82 @@ void prefill_kernel(PrefillArgs a) {
     const int lane = tid & 63, w = tid >> 6;
     const int h2 = lane >> 5, l32 = lane & 31;
 
-    // ---- which (query block, batch, KV head, head group) this workgroup owns
-    const int combos = a.B * a.Hkv * a.n_hgrp;
-    int qb, c;
+    // ---- which (query block, batch, KV head, head group) this workgroup owns.
+    // With the (KV head, head group) pairs split evenly over the 8 XCDs, an XCD
+    // walks its pairs sequence by sequence, query blocks longest-first: its
+    // resident workgroups then sweep the same K/V rows together (L2 reuse),
+    // and every XCD gets the same share of every sequence.
+    const int P = a.Hkv * a.n_hgrp;
+    int qb, b, pair;
     {
         const int i = blockIdx.x;
-        if (a.xcd_remap) {
+        if (a.xcd_remap == 2) {
+            const int x = i & 7, j = i >> 3, ppx = P >> 3;
+            const int per_b = ppx * a.n_qblk;
+            b = j / per_b;
+            const int r = j - b * per_b;
+            pair = x * ppx + r % ppx;
+            qb = a.n_qblk - 1 - r / ppx;
+        } else if (a.xcd_remap == 1) {
+            const int combos = a.B * P;
             const int x = i & 7, j = i >> 3, cpx = combos >> 3;
+            const int c = x * cpx + j % cpx;
             qb = a.n_qblk - 1 - j / cpx;
-            c = x * cpx + j % cpx;
+            b = c % a.B;
+            pair = c / a.B;
         } else {
+            const int combos = a.B * P;
+            const int c = i % combos;
             qb = a.n_qblk - 1 - i / combos;
-            c = i % combos;
+            b = c % a.B;
+            pair = c / a.B;
         }
     }
-    const int hg = c % a.n_hgrp;
-    const int bg = c / a.n_hgrp;
-    const int g = bg % a.Hkv;
-    const int b = bg / a.Hkv;
+    const int hg = pair % a.n_hgrp;
+    const int g = pair / a.n_hgrp;
     const int G = a.Hq / a.Hkv;
     const int head = g * G + hg * NW + w;
     const int q0 = qb * QW;
 
+    // ---- this sequence's tokens: dense [B, T, H, D] batches, or packed
+    // sequences (offsets cu_q / cu_k) whose queries are the last Tq of their keys
+    int Tq, Tk;
+    size_t q_tok0, k_tok0, lse_off;
+    int64_t q_pos0, k_pos0;
+    if (a.cu_q) {
+        const int qs = a.cu_q[b], ks = a.cu_k[b];
+        Tq = a.cu_q[b + 1] - qs;
+        Tk = a.cu_k[b + 1] - ks;
+        q_tok0 = (size_t)qs;
+        k_tok0 = (size_t)ks;
+        k_pos0 = a.kpos ? a.kpos[b] : 0;
+        q_pos0 = k_pos0 + Tk - Tq;
+        lse_off = (size_t)qs;
+    } else {
+        Tq = a.Tq;
+        Tk = a.Tk;
+        q_tok0 = (size_t)b * a.Tq;
+        k_tok0 = (size_t)b * a.Tk;
+        q_pos0 = a.q_pos0;
+        k_pos0 = a.k_pos0;
+        lse_off = (size_t)b * a.Hq * a.Tq;
+    }
+    if (q0 >= Tq) return;   // whole workgroup: a packed sequence shorter than the longest
+
     const size_t krow_stride = (size_t)a.Hkv * kDqk;
     const size_t vrow_stride = (size_t)a.Hkv * kDv;
-    const uint16_t *kbase = a.k + (size_t)b * a.Tk * krow_stride + (size_t)g * kDqk;
-    const uint16_t *vbase = a.v + (size_t)b * a.Tk * vrow_stride + (size_t)g * kDv;
+    const uint16_t *kbase = a.k + k_tok0 * krow_stride + (size_t)g * kDqk;
+    const uint16_t *vbase = a.v + k_tok0 * vrow_stride + (size_t)g * kDv;
 
     // ---- key range of the block
-    const int t_last = min(q0 + QW, a.Tq) - 1;
-    const int64_t qp_lo = a.q_pos0 + q0;
-    const int64_t qp_hi = a.q_pos0 + t_last;
+    const int t_last = min(q0 + QW, Tq) - 1;
+    const int64_t qp_lo = q_pos0 + q0;
+    const int64_t qp_hi = q_pos0 + t_last;
     int64_t jlo = 0;
-    if (a.window > 0) jlo = qp_lo - a.window + 1 - a.k_pos0;
+    if (a.window > 0) jlo = qp_lo - a.window + 1 - k_pos0;
     if (jlo < 0) jlo = 0;
-    int64_t jhi = qp_hi - a.k_pos0;
-    if (jhi > a.Tk - 1) jhi = a.Tk - 1;
+    int64_t jhi = qp_hi - k_pos0;
+    if (jhi > Tk - 1) jhi = Tk - 1;
     const int tile_lo = (int)(jlo / NK);
     const int tile_hi = jhi >= jlo ? (int)(jhi / NK) : tile_lo - 1;
 
@@ -120,12 +161,12 @@ void prefill_kernel(PrefillArgs a) {
     u32x4 qr[12];
     {
         const int t = q0 + l32;
-        if (t < a.Tq) {
-            const uint16_t *src = a.q + (((size_t)b * a.Tq + t) * a.Hq + head) * kDqk + 96 * h2;
+        if (t < Tq) {
+            const uint16_t *src = a.q + ((q_tok0 + t) * a.Hq + head) * kDqk + 96 * h2;
 #pragma unroll
             for (int ks = 0; ks < 12; ++ks) qr[ks] = ldg128(src + 8 * ks);
             if (h2 == 0) {
-                const int64_t qp = a.q_pos0 + t;
+                const int64_t qp = q_pos0 + t;
 #pragma unroll
                 for (int cc = 0; cc < 4; ++cc) rope_rotate8(qr[cc], qr[cc + 4], a.rt, 8 * cc, qp);
             }
@@ -173,7 +214,7 @@ void prefill_kernel(PrefillArgs a) {
     auto tile_bases = [&](int jt) {
         if (tid < kPairs) {
             float sn, cs;
-            turn_sincos((uint64_t)(a.k_pos0 + (int64_t)jt * NK) * my_turn, sn, cs);
+            turn_sincos((uint64_t)(k_pos0 + (int64_t)jt * NK) * my_turn, sn, cs);
             rope_base[jt & 1][tid] = float2{cs, sn};
         }
     };
@@ -185,7 +226,7 @@ void prefill_kernel(PrefillArgs a) {
         const int j0 = jt * NK;
         const uint16_t *kt = kbase + (size_t)j0 * krow_stride;
         const uint16_t *vt = vbase + (size_t)j0 * vrow_stride;
-        if (j0 + NK <= a.Tk) {
+        if (j0 + NK <= Tk) {
 #pragma unroll
             for (int r = 0; r < ROT_PER; ++r) {
                 k_rx[r] = *reinterpret_cast<const u32x2 *>(kt + k_rot_off[r]);
@@ -199,7 +240,7 @@ void prefill_kernel(PrefillArgs a) {
                 v_st[r][1] = ldg128(vt + v_off[r] + vrow_stride);
             }
         } else {   // ragged last tile: rows past Tk are zero
-            const int nrow = a.Tk - j0;
+            const int nrow = Tk - j0;
 #pragma unroll
             for (int r = 0; r < ROT_PER; ++r) {
                 const bool ok = k_rot_row[r] < nrow;
@@ -270,7 +311,7 @@ void prefill_kernel(PrefillArgs a) {
     const float cl2 = a.scale_log2;
     // K row read order: bits 2 and 3 of the row index swapped
     const int prow = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
-    const int64_t qp = a.q_pos0 + q0 + l32;
+    const int64_t qp = q_pos0 + q0 + l32;
 
     if (tile_hi >= tile_lo) {
         tile_bases(tile_lo);
@@ -311,14 +352,14 @@ void prefill_kernel(PrefillArgs a) {
         }
 
         // ---- mask on edge tiles only (offsets are small there, so 32-bit)
-        const int64_t kp0 = a.k_pos0 + j0;
-        const bool full = (j0 + NK <= a.Tk) && (kp0 + NK - 1 <= qp_lo) &&
+        const int64_t kp0 = k_pos0 + j0;
+        const bool full = (j0 + NK <= Tk) && (kp0 + NK - 1 <= qp_lo) &&
                           (a.window == 0 || qp_hi - kp0 < a.window);
         if (!full) {
             int64_t d64 = qp - kp0;
             d64 = d64 < -(1 << 30) ? -(1 << 30) : (d64 > (1 << 30) ? (1 << 30) : d64);
             const int d = (int)d64;                 // query position - first key position
-            const int kmax = a.Tk - j0;             // keys past the end of k/v
+            const int kmax = Tk - j0;             // keys past the end of k/v
             const int win = a.window > 0 ? a.window : 0x7fffffff;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
@@ -392,9 +433,9 @@ void prefill_kernel(PrefillArgs a) {
     // ---- epilogue: o = v_scale * O / l, bf16
     const float lt = sum_xor32(l_run);
     const int t = q0 + l32;
-    if (t < a.Tq) {
+    if (t < Tq) {
         const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
-        uint16_t *dst = a.out + (((size_t)b * a.Tq + t) * a.Hq + head) * kDv;
+        uint16_t *dst = a.out + ((q_tok0 + t) * a.Hq + head) * kDv;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -405,7 +446,7 @@ void prefill_kernel(PrefillArgs a) {
                 *reinterpret_cast<u32x2 *>(dst + 32 * mb + 8 * a4 + 4 * h2) = o;
             }
         if (a.lse && h2 == 0)
-            a.lse[((size_t)b * a.Hq + head) * a.Tq + t] = lt > 0.0f ? (m_run + log2f(lt)) * kLn2 : kNegInf;
+            a.lse[lse_off + (size_t)head * a.lse_hstride + t] = lt > 0.0f ? (m_run + log2f(lt)) * kLn2 : kNegInf;
     }
 }
 
@@ -418,7 +459,7 @@ static hipError_t launch_variant(PrefillArgs a, hipStream_t stream) {
     const int64_t combos = (int64_t)a.B * a.Hkv * a.n_hgrp;
     const int64_t blocks = combos * a.n_qblk;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    a.xcd_remap = (combos % 8 == 0) ? 1 : 0;
+    a.xcd_remap = ((a.Hkv * a.n_hgrp) % 8 == 0) ? 2 : (combos % 8 == 0) ? 1 : 0;
     hipLaunchKernelGGL((prefill_kernel<NW, NK>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, a);
     return hipGetLastError();
 }

@@ -182,6 +182,27 @@ def global_prefill_chunk(T: int, n_q_heads: int, n_kv_heads: int, seed: int, t_l
             "v": v.reshape(1, t_hi, n_kv_heads, D_V)}
 
 
+def varlen_inputs(lens_q, lens_k, n_q_heads: int, n_kv_heads: int, seed: int, with_sinks: bool,
+                  k_pos0=None) -> dict:
+    """Packed (THD) sequences: sequence b has lens_q[b] query tokens and
+    lens_k[b] key tokens, stored back to back.  q [sum(lens_q),Hq,192],
+    k/v [sum(lens_k),Hkv,*] bf16 bits; cu_q / cu_k [B+1] int32 offsets;
+    k_pos0 [B] int64 (position of each sequence's first key) or None."""
+    lens_q = np.asarray(lens_q, dtype=np.int64)
+    lens_k = np.asarray(lens_k, dtype=np.int64)
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    cq, ck, cv, cs, _ = _children(seed)
+    return {
+        "q": normal_bf16(cq, (int(cu_q[-1]), n_q_heads, D_QK)),
+        "k": normal_bf16(ck, (int(cu_k[-1]), n_kv_heads, D_QK)),
+        "v": normal_bf16(cv, (int(cu_k[-1]), n_kv_heads, D_V)),
+        "cu_q": cu_q, "cu_k": cu_k,
+        "k_pos0": None if k_pos0 is None else np.asarray(k_pos0, dtype=np.int64),
+        "sinks": normal_f32(cs, (n_q_heads,)) if with_sinks else None,
+    }
+
+
 def append_inputs(S: int, n_kv_heads: int, seed: int, pos_lo: int, pos_hi: int) -> dict:
     """New-token k/v rows [S,Hkv,192|128] and their positions ~ U[pos_lo,pos_hi)."""
     cq, ck, cv, cs, cp = _children(seed)

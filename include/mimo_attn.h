@@ -116,6 +116,37 @@ mimo_status mimo_attn_prefill_global(const mimo_attn_cfg *cfg, const uint16_t *q
                                      int64_t q_pos0, uint16_t *out, float *lse, void *stream);
 
 /*
+ * Prefill of packed variable-length sequences (THD layout), which also covers
+ * continuing a sequence chunk by chunk (Gaudi recipe page, Launch and Buckets
+ * sections: prompts are prefilled in chunks of up to 8,192 tokens against the
+ * context before them; a sliding layer's chunk needs only the window - 1 keys
+ * before it, a global layer's chunk its whole prefix).
+ *   Sequence b owns query tokens cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key
+ *   tokens cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 (Tq_b and Tk_b of them).  Its
+ *   first key sits at position P_b = k_pos0[b] (0 if k_pos0 is NULL) and its
+ *   queries are its last Tq_b keys: query t is at position P_b + Tk_b - Tq_b + t.
+ *   Visibility, RoPE and the sink are as in the dense calls, with cfg->window
+ *   (0 = causal only) and sinks optional on either layer type.
+ *   q   : [total_q, num_q_heads, 192] unrotated;  k : [total_k, num_kv_heads, 192]
+ *   unrotated;  v : [total_k, num_kv_heads, 128];  out : [total_q, num_q_heads, 128];
+ *   lse : [num_q_heads, total_q] fp32 or NULL (natural-log LSE of each row,
+ *   sink included).
+ *   cu_seqlens_q / cu_seqlens_k : [B+1] int32 device arrays, non-decreasing,
+ *   starting at 0;  k_pos0 : [B] int64 device array or NULL.
+ * The caller guarantees, for every b: 0 <= Tq_b <= Tk_b, Tq_b <= max_seqlen_q,
+ * cu_seqlens_q[B] <= total_q, and positions >= 0.  These device values are not
+ * read on the host; rows of a sequence past max_seqlen_q are left unwritten.
+ * The attention runs over the keys given: a sliding chunk must carry the
+ * min(window - 1, P) keys before its first query, a global chunk its whole
+ * prefix (P_b = 0).
+ */
+mimo_status mimo_attn_prefill_varlen(const mimo_attn_cfg *cfg, const uint16_t *q, const uint16_t *k,
+                                     const uint16_t *v, const float *sinks, int32_t B,
+                                     const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                                     const int64_t *k_pos0, int32_t max_seqlen_q, int32_t total_q,
+                                     uint16_t *out, float *lse, void *stream);
+
+/*
  * One decode query per sequence over a KV cache (window-sized ring on sliding
  * layers, Gaudi recipe page, Launch section; a long cache on global layers).
  * Split-K flash decoding balanced over the batch: the visible slots of all

@@ -159,6 +159,33 @@ def prefill_global(q, k, v, *, q_pos0: int = 0, base: float = GLOBAL_BASE, rows=
     return (out, np.stack(lses)) if want_lse else out
 
 
+def prefill_varlen(q, k, v, cu_q, cu_k, *, k_pos0=None, sinks=None, window: int, base: float,
+                   want_lse: bool = False, n_threads: int = 0):
+    """Packed sequences: sequence b owns query tokens cu_q[b]..cu_q[b+1]-1 and key
+    tokens cu_k[b]..cu_k[b+1]-1; its first key sits at position k_pos0[b] (0 if
+    None) and its queries are its last keys (query t at k_pos0[b] + Tk - Tq + t).
+
+    Returns out [total_q,Hq,128] (and lse [Hq,total_q]); rows outside every
+    sequence are NaN."""
+    total_q, hq = q.shape[:2]
+    out = np.full((total_q, hq, v.shape[2]), np.nan)
+    lse = np.full((hq, total_q), np.nan)
+    for b in range(len(cu_q) - 1):
+        qs, qe, ks, ke = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if qe == qs:
+            continue
+        p0 = 0 if k_pos0 is None else int(k_pos0[b])
+        kpos = p0 + np.arange(ke - ks, dtype=np.int64)
+        qpos = kpos[ke - ks - (qe - qs):]
+        r = attention(q[qs:qe], qpos, k[ks:ke], kpos, v[ks:ke], sinks=sinks, window=window, base=base,
+                      want_lse=want_lse, n_threads=n_threads)
+        if want_lse:
+            out[qs:qe], lse[:, qs:qe] = r[0], r[1].T
+        else:
+            out[qs:qe] = r
+    return (out, lse) if want_lse else out
+
+
 def cache_slots(p: int, cap: int, window: int):
     """Cache rule: the token at position t lives in slot t mod cap.  A query at
     position p sees positions max(0, p-window+1)..p (window > 0) or 0..p."""

@@ -111,6 +111,24 @@ def test_global_prefill_contract(lib):
     assert glob(lib, cfg_glob(), Tq=0, Tk=0, q=None, out=None) == OK
 
 
+def varlen(lib, cfg, Bn=2, max_q=64, total_q=128, q=FAKE, cu_q=FAKE, cu_k=FAKE):
+    return lib.mimo_attn_prefill_varlen(ctypes.byref(cfg), q, FAKE, FAKE, None, Bn, cu_q, cu_k, None, max_q,
+                                        total_q, FAKE, None, None)
+
+
+def test_varlen_prefill_contract(lib):
+    assert varlen(lib, cfg_swa(), Bn=-1) == INVAL
+    assert varlen(lib, cfg_swa(), max_q=-1) == INVAL
+    assert varlen(lib, cfg_swa(), max_q=200, total_q=100) == INVAL   # a sequence longer than the pack
+    assert "total_q" in err(lib)
+    assert varlen(lib, cfg_swa(), cu_q=None) == INVAL
+    assert varlen(lib, cfg_glob(), q=None) == INVAL
+    assert varlen(lib, cfg_swa(num_q_heads=8, num_kv_heads=4)) == UNSUP     # group of 2
+    # nothing to do is valid with NULL data
+    assert varlen(lib, cfg_swa(), Bn=0, q=None, cu_q=None, cu_k=None) == OK
+    assert varlen(lib, cfg_glob(), max_q=0, total_q=0, q=None) == OK
+
+
 def dec(lib, cfg, S=4, cap=128, ws=FAKE, ws_bytes=1 << 30, q=FAKE):
     return lib.mimo_attn_decode(ctypes.byref(cfg), S, q, FAKE, FAKE, FAKE, cap, None, FAKE, ws, ws_bytes, None)
 

@@ -8,6 +8,9 @@ computes rows one by one); every output is also checked to be finite.
     sequences (KV lengths ~U[32768, 131072], cap 131072), NaN in unused slots
   * long global prefill T=524288 in query chunks of 65536: the first, a middle
     and the last chunk, each against its whole prefix
+  * serving chunks of 8192 tokens, packed: four sliding-window chunks that
+    continue sequences (127 earlier keys each) and four global chunks against
+    prefixes of up to 57344 tokens
 """
 import numpy as np
 import pytest
@@ -90,3 +93,36 @@ def test_long_global_prefill_chunk(chunk):
     got = host_f64(out[:, torch.from_numpy(rows).cuda()])
     ref = oracle.prefill_global(d["q"], d["k"], d["v"], q_pos0=lo, base=1e7, rows=rows)
     assert_parity(got, ref, f"chunk {chunk}, {len(rows)} rows")
+
+
+def test_packed_serving_chunks():
+    chunk = 8192
+    for layer, seed in (("sliding", 1005), ("global", 1006)):
+        if layer == "sliding":
+            starts = [8192, 65536, 131072, 262144]
+            lens_k = [chunk + 127] * 4
+            kpos = [st - 127 for st in starts]
+            d = gen.varlen_inputs([chunk] * 4, lens_k, 64, 8, seed=seed, with_sinks=True, k_pos0=kpos)
+            cfg = Bd.swa_cfg()
+        else:
+            prefix = [0, 8192, 24576, 57344]
+            d = gen.varlen_inputs([chunk] * 4, [chunk + p for p in prefix], 64, 4, seed=seed, with_sinks=False)
+            cfg = Bd.global_cfg()
+        say(f"full-size packed serving chunks: {layer}")
+        out = torch.empty((4 * chunk, 64, 128), dtype=torch.bfloat16, device="cuda")
+        Bd.mimo_attn_prefill_varlen(cfg, dev_bf16(d["q"]), dev_bf16(d["k"]), dev_bf16(d["v"]),
+                                    None if d["sinks"] is None else dev(d["sinks"]), dev(d["cu_q"]),
+                                    dev(d["cu_k"]), chunk, out,
+                                    k_pos0=None if d["k_pos0"] is None else dev(d["k_pos0"]))
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(out).all())
+        got_all = host_f64(out)
+        for b in range(4):
+            rows = sample_rows(chunk, 6, 10 + b)
+            q0, k0 = int(d["cu_q"][b]), int(d["cu_k"][b])
+            lq, lk = chunk, int(d["cu_k"][b + 1]) - k0
+            p0 = 0 if d["k_pos0"] is None else int(d["k_pos0"][b])
+            kp = p0 + np.arange(lk, dtype=np.int64)
+            ref = oracle.attention(d["q"][q0 + rows], kp[lk - lq + rows], d["k"][k0:k0 + lk], kp,
+                                   d["v"][k0:k0 + lk], sinks=d["sinks"], window=cfg.window, base=cfg.rope_base)
+            assert_parity(got_all[q0 + rows], ref, f"{layer} chunk {b}, {len(rows)} rows")

@@ -321,6 +321,50 @@ def test_chunked_global_prefill_equals_whole():
     assert np.array_equal(np.concatenate(parts, axis=1), whole)
 
 
+def test_varlen_chunk_continuation_equals_whole_sequence():
+    """A chunk that continues a sequence, given only the window-1 keys before it
+    (sliding) or its whole prefix (global), reproduces the whole prefill's rows."""
+    T, lo = 300, 200
+    d = gen.prefill_inputs(1, T, 8, 2, seed=21, with_sinks=True)
+    whole_s = oracle.prefill_swa(d["q"], d["k"], d["v"], d["sinks"], window=128, base=1e4)[0]
+    whole_g = oracle.prefill_global(d["q"], d["k"], d["v"], base=1e7)[0]
+    k0 = lo - 127
+    cu_q = np.array([0, T - lo], np.int32)
+    got_s = oracle.prefill_varlen(d["q"][0, lo:], d["k"][0, k0:], d["v"][0, k0:], cu_q,
+                                  np.array([0, T - k0], np.int32), k_pos0=np.array([k0]), sinks=d["sinks"],
+                                  window=128, base=1e4)
+    assert np.array_equal(got_s, whole_s[lo:])
+    got_g = oracle.prefill_varlen(d["q"][0, lo:], d["k"][0], d["v"][0], cu_q, np.array([0, T], np.int32),
+                                  window=0, base=1e7)
+    assert np.array_equal(got_g, whole_g[lo:])
+    # one key fewer than the window needs changes the first row of the chunk
+    short = oracle.prefill_varlen(d["q"][0, lo:], d["k"][0, k0 + 1:], d["v"][0, k0 + 1:], cu_q,
+                                  np.array([0, T - k0 - 1], np.int32), k_pos0=np.array([k0 + 1]),
+                                  sinks=d["sinks"], window=128, base=1e4)
+    assert np.max(np.abs(short[0] - whole_s[lo])) > 1e-6
+    assert np.array_equal(short[1:], whole_s[lo + 1:])
+
+
+def test_varlen_packing_equals_separate_sequences():
+    lens = [37, 1, 0, 130]
+    seqs = [gen.prefill_inputs(1, L, 8, 1, seed=30 + i, with_sinks=False) for i, L in enumerate(lens)]
+    sinks = np.linspace(-2, 2, 8).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q = np.concatenate([s["q"][0] for s in seqs])
+    k = np.concatenate([s["k"][0] for s in seqs])
+    v = np.concatenate([s["v"][0] for s in seqs])
+    pos0 = np.array([0, 5, 9, 1000], np.int64)
+    out, lse = oracle.prefill_varlen(q, k, v, cu, cu, k_pos0=pos0, sinks=sinks, window=128, base=1e4,
+                                     want_lse=True)
+    for i, s in enumerate(seqs):
+        if lens[i] == 0:
+            continue
+        ref, rl = oracle.prefill_swa(s["q"], s["k"], s["v"], sinks, pos0=int(pos0[i]), window=128, base=1e4,
+                                     want_lse=True)
+        assert np.array_equal(out[cu[i]:cu[i + 1]], ref[0])
+        assert np.array_equal(lse[:, cu[i]:cu[i + 1]], rl[0].T)
+
+
 def test_decode_cache_rule_matches_prefill_rows():
     """A decode query over a ring cache that holds the rotated keys sees exactly
     the keys the prefill row sees: checked on exactly representable values."""
