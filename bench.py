@@ -15,6 +15,10 @@ on the stream the kernels are launched on (torch's current stream).
 --workload long_prefill instead times the 524288-token global prefill run as 8
 query chunks of 65536, each against its full causal prefix.
 
+--workload spec_decode times multi-query decode (speculative verification) at
+the mixed-decode sizes: 64 sliding sequences (ring of 128 + n_q - 1) and 16
+global sequences, with n_q = 4 (EAGLE) and n_q = 8 (DFlash) draft tokens.
+
 --workload serving_chunks times packed (THD) serving chunks of 8192 tokens:
 four sliding-window chunks that continue sequences at positions 8192, 65536,
 131072 and 262144 (each with the 127 keys before it) and four global chunks
@@ -246,7 +250,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["layer_step", "long_prefill", "serving_chunks"], default="layer_step")
+    ap.add_argument("--workload", choices=["layer_step", "long_prefill", "serving_chunks", "spec_decode"], default="layer_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -281,6 +285,8 @@ def main():
         return main_long_prefill(args, torch, gen, Bd)
     if args.workload == "serving_chunks":
         return main_serving_chunks(args, torch, gen, Bd)
+    if args.workload == "spec_decode":
+        return main_spec_decode(args, torch, gen, Bd)
 
     ph = setup_layer_step(torch, gen, Bd)
     names = ["swa_prefill", "global_prefill", "append_swa", "append_global", "decode_swa", "decode_global"]
@@ -471,6 +477,83 @@ def main_serving_chunks(args, torch, gen, Bd):
                                     "packed global chunks 4x8192 (prefixes 0..57344)"},
              "roofline": {"bound": "mfma", "kernel": "prefill_kernel (packed global chunks)", "achieved": g["tflops"],
                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": g["frac_mfma_peak"],
+                          "traffic": None},
+             "cpu_baseline": None, "phases": phases}
+    print(json.dumps(out_j))
+
+
+def main_spec_decode(args, torch, gen, Bd):
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+    cases = {}
+    for nq in (4, 8):
+        for name, S, hkv, window, seed in (("swa", 64, 8, 128, 1003), ("global", 16, 4, 0, 2003)):
+            rng = np.random.Generator(np.random.PCG64(seed))
+            if window:
+                pos = rng.integers(128, 131072, size=S)
+                cap = window + nq - 1
+            else:
+                pos = rng.integers(32768, 131072, size=S, endpoint=True) - 1
+                cap = 131072
+            log(f"setup: multi-query decode {name} S={S} n_q={nq} cap={cap}")
+            d = gen.decode_multi_inputs(S, nq, cap, 64, hkv, seed=seed, window=window, pos=pos,
+                                        with_sinks=window > 0)
+            cfg = Bd.swa_cfg() if window else Bd.global_cfg()
+            # keys any draft token sees, and the visible (query, key) pairs
+            if window:
+                seen = np.minimum(pos + 1, window + nq - 1)
+                pairs = sum(min(max(int(p) - (nq - 1 - i) + 1, 0), window) for p in pos for i in range(nq))
+            else:
+                seen = pos + 1
+                pairs = sum(max(int(p) - (nq - 1 - i) + 1, 0) for p in pos for i in range(nq))
+            cases[f"{name}_nq{nq}"] = dict(
+                cfg=cfg, q=_dev_bf16(torch, d["q"]), pos=dev(d["pos"]), kc=_dev_bf16(torch, d["k_cache"]),
+                vc=_dev_bf16(torch, d["v_cache"]), sinks=None if d["sinks"] is None else dev(d["sinks"]),
+                out=torch.empty((S, nq, 64, 128), dtype=torch.bfloat16, device="cuda"),
+                ws=torch.empty(Bd.mimo_attn_decode_multi_workspace_size(cfg, S, nq, cap), dtype=torch.uint8,
+                               device="cuda"),
+                bytes=int(seen.sum()) * hkv * 320 * 2 + S * nq * 64 * (192 + 128) * 2,
+                flops=FLOP_PER_PAIR_HEAD * 64 * pairs)
+            del d
+    names = list(cases)
+
+    def step(ev=None):
+        for n in names:
+            c = cases[n]
+            if ev is not None:
+                ev[n][0].record()
+            Bd.mimo_attn_decode_multi(c["cfg"], c["q"], c["pos"], c["kc"], c["vc"], c["sinks"], c["out"], ws=c["ws"])
+            if ev is not None:
+                ev[n][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    ms = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in evs])) for n in names}
+    phases = {}
+    for n, c in cases.items():
+        t = ms[n] * 1e-3
+        phases[n] = {"ms": ms[n], "gbs": c["bytes"] / t / 1e9, "frac_hbm_peak": c["bytes"] / t / 1e9 / PEAK_HBM_GBS,
+                     "tflops": c["flops"] / t / 1e12}
+    total_bytes = sum(c["bytes"] for c in cases.values())
+    value = total_bytes / (ms_step * 1e-3) / 1e9
+    g = phases["global_nq8"]
+    out_j = {"metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+             "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+             "vs_baseline": None, "dtype": "bf16", "data": "synthetic: seeded N(0,1) bf16 q and caches, N(0,1) fp32 sinks",
+             "config": {"workload": "spec_decode = multi-query decode, 64 sliding + 16 global sequences, "
+                                    "n_q = 4 and n_q = 8"},
+             "roofline": {"bound": "hbm", "kernel": "decode_partial_kernel (global, 8 draft tokens)",
+                          "achieved": g["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": g["frac_hbm_peak"],
                           "traffic": None},
              "cpu_baseline": None, "phases": phases}
     print(json.dumps(out_j))

@@ -66,10 +66,14 @@ def load_library(path: str = LIB_PATH):
     lib.mimo_attn_decode.argtypes = [C, I32, P, P, P, P, I32, P, P, P, ctypes.c_size_t, P]
     lib.mimo_attn_decode_workspace_size.argtypes = [C, I32, I32]
     lib.mimo_attn_decode_workspace_size.restype = ctypes.c_size_t
+    lib.mimo_attn_decode_multi.argtypes = [C, I32, I32, P, P, P, P, I32, P, P, P, ctypes.c_size_t, P]
+    lib.mimo_attn_decode_multi_workspace_size.argtypes = [C, I32, I32, I32]
+    lib.mimo_attn_decode_multi_workspace_size.restype = ctypes.c_size_t
     lib.mimo_kv_ring_append.argtypes = [C, I32, P, P, P, P, P, I32, P]
     lib.mimo_last_error.restype = ctypes.c_char_p
     for fn in ("mimo_rope_partial", "mimo_attn_prefill_swa", "mimo_attn_prefill_global",
-               "mimo_attn_prefill_varlen", "mimo_attn_decode", "mimo_kv_ring_append"):
+               "mimo_attn_prefill_varlen", "mimo_attn_decode", "mimo_attn_decode_multi",
+               "mimo_kv_ring_append"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -173,6 +177,25 @@ def mimo_attn_decode(cfg: MimoAttnCfg, q, q_pos, k_cache, v_cache, sinks, out, w
     _check("mimo_attn_decode",
            lib.mimo_attn_decode(ctypes.byref(cfg), S, _p(q), _p(q_pos), _p(k_cache), _p(v_cache), cap,
                                 _p(sinks), _p(out), _p(ws), ws_bytes, _stream(stream)))
+    return out
+
+
+def mimo_attn_decode_multi_workspace_size(cfg: MimoAttnCfg, S: int, n_q: int, cap: int) -> int:
+    return int(load_library().mimo_attn_decode_multi_workspace_size(ctypes.byref(cfg), S, n_q, cap))
+
+
+def mimo_attn_decode_multi(cfg: MimoAttnCfg, q, q_pos, k_cache, v_cache, sinks, out, ws=None, stream=None):
+    """q [S,n_q,Hq,192], q_pos [S] int64 (newest token), caches [S,cap,Hkv,192|128], out [S,n_q,Hq,128]."""
+    lib = load_library()
+    _need(q, torch.bfloat16, "q", 4); _need(out, torch.bfloat16, "out", 4)
+    _need(k_cache, torch.bfloat16, "k_cache", 4); _need(v_cache, torch.bfloat16, "v_cache", 4)
+    _need(q_pos, torch.int64, "q_pos", 1); _need(sinks, torch.float32, "sinks", 1)
+    S, n_q = q.shape[:2]
+    cap = k_cache.shape[1]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("mimo_attn_decode_multi",
+           lib.mimo_attn_decode_multi(ctypes.byref(cfg), S, n_q, _p(q), _p(q_pos), _p(k_cache), _p(v_cache), cap,
+                                      _p(sinks), _p(out), _p(ws), ws_bytes, _stream(stream)))
     return out
 
 

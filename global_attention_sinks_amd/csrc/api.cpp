@@ -178,23 +178,21 @@ mimo_status mimo_attn_prefill_varlen(const mimo_attn_cfg *cfg, const uint16_t *q
     return from_hip(launch_prefill(a, (hipStream_t)stream), "prefill_varlen launch");
 }
 
-size_t mimo_attn_decode_workspace_size(const mimo_attn_cfg *cfg, int32_t S, int32_t cap) {
-    if (!cfg || S <= 0 || cap <= 0 || cfg->num_q_heads <= 0) return 0;
-    if (cfg->num_kv_heads <= 0 || cfg->num_kv_heads > 8) return 0;
-    return decode_workspace_bytes(S, cfg->num_q_heads, cfg->num_kv_heads);
-}
-
-mimo_status mimo_attn_decode(const mimo_attn_cfg *cfg, int32_t S, const uint16_t *q,
-                             const int64_t *q_pos, const uint16_t *k_cache, const uint16_t *v_cache,
-                             int32_t cap, const float *sinks, uint16_t *out, void *ws,
-                             size_t ws_bytes, void *stream) {
+static mimo_status decode_common(const mimo_attn_cfg *cfg, int32_t S, int32_t n_q, const uint16_t *q,
+                                 const int64_t *q_pos, const uint16_t *k_cache, const uint16_t *v_cache,
+                                 int32_t cap, const float *sinks, uint16_t *out, void *ws, size_t ws_bytes,
+                                 void *stream) {
     mimo_status st = check_cfg(cfg);
     if (st != MIMO_OK) return st;
     if (S < 0 || cap < 1) return fail(MIMO_ERR_INVALID_ARGUMENT, "S must be >= 0 and cap >= 1");
+    if (n_q < 1) return fail(MIMO_ERR_INVALID_ARGUMENT, "n_q must be >= 1");
     const int G = cfg->num_q_heads / cfg->num_kv_heads;
     if (G > 16) return fail(MIMO_ERR_UNSUPPORTED, "decode needs a GQA group size <= 16 (got %d)", G);
-    if (cfg->window > 0 && cap < cfg->window)
-        return fail(MIMO_ERR_INVALID_ARGUMENT, "a ring cache needs cap (%d) >= window (%d)", cap, cfg->window);
+    if (G * n_q > 128)
+        return fail(MIMO_ERR_UNSUPPORTED, "decode needs group size x n_q <= 128 (got %d x %d)", G, n_q);
+    if (cfg->window > 0 && (int64_t)cap < (int64_t)cfg->window + n_q - 1)
+        return fail(MIMO_ERR_INVALID_ARGUMENT, "a ring cache needs cap (%d) >= window + n_q - 1 (%d)", cap,
+                    cfg->window + n_q - 1);
     if (cfg->num_kv_heads > 8)
         return fail(MIMO_ERR_UNSUPPORTED, "decode needs num_kv_heads <= 8 (got %d)", cfg->num_kv_heads);
     if (S > 65535) return fail(MIMO_ERR_UNSUPPORTED, "decode needs S <= 65535");
@@ -202,7 +200,7 @@ mimo_status mimo_attn_decode(const mimo_attn_cfg *cfg, int32_t S, const uint16_t
     if (S == 0) return ok();
     if (!q || !q_pos || !k_cache || !v_cache || !out)
         return fail(MIMO_ERR_INVALID_ARGUMENT, "q, q_pos, k_cache, v_cache and out must be non-NULL");
-    const size_t need = decode_workspace_bytes(S, cfg->num_q_heads, cfg->num_kv_heads);
+    const size_t need = decode_workspace_bytes(S, cfg->num_q_heads, cfg->num_kv_heads, n_q);
     if (!ws || ws_bytes < need)
         return fail(MIMO_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu)", need,
                     ws ? ws_bytes : (size_t)0);
@@ -210,9 +208,43 @@ mimo_status mimo_attn_decode(const mimo_attn_cfg *cfg, int32_t S, const uint16_t
     a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.pos = q_pos; a.sinks = sinks; a.out = out;
     a.ws_o = (float *)ws;
     a.S = S; a.Hq = cfg->num_q_heads; a.Hkv = cfg->num_kv_heads; a.cap = cap; a.window = cfg->window;
+    a.n_q = n_q;
     a.scale_log2 = scale_log2(cfg); a.v_scale = cfg->v_scale;
     a.rt = rope_turns(cfg->rope_base);
     return from_hip(launch_decode(a, (hipStream_t)stream), "decode launch");
+}
+
+static size_t decode_ws_size(const mimo_attn_cfg *cfg, int32_t S, int32_t n_q) {
+    if (!cfg || S <= 0 || n_q < 1 || cfg->num_q_heads <= 0 || cfg->num_kv_heads <= 0 ||
+        cfg->num_kv_heads > 8 || cfg->num_q_heads % cfg->num_kv_heads != 0)
+        return 0;
+    const int G = cfg->num_q_heads / cfg->num_kv_heads;
+    if (G > 16 || G * n_q > 128) return 0;
+    return decode_workspace_bytes(S, cfg->num_q_heads, cfg->num_kv_heads, n_q);
+}
+
+size_t mimo_attn_decode_workspace_size(const mimo_attn_cfg *cfg, int32_t S, int32_t cap) {
+    (void)cap;
+    return decode_ws_size(cfg, S, 1);
+}
+
+mimo_status mimo_attn_decode(const mimo_attn_cfg *cfg, int32_t S, const uint16_t *q,
+                             const int64_t *q_pos, const uint16_t *k_cache, const uint16_t *v_cache,
+                             int32_t cap, const float *sinks, uint16_t *out, void *ws,
+                             size_t ws_bytes, void *stream) {
+    return decode_common(cfg, S, 1, q, q_pos, k_cache, v_cache, cap, sinks, out, ws, ws_bytes, stream);
+}
+
+size_t mimo_attn_decode_multi_workspace_size(const mimo_attn_cfg *cfg, int32_t S, int32_t n_q, int32_t cap) {
+    (void)cap;
+    return decode_ws_size(cfg, S, n_q);
+}
+
+mimo_status mimo_attn_decode_multi(const mimo_attn_cfg *cfg, int32_t S, int32_t n_q, const uint16_t *q,
+                                   const int64_t *q_pos, const uint16_t *k_cache, const uint16_t *v_cache,
+                                   int32_t cap, const float *sinks, uint16_t *out, void *ws,
+                                   size_t ws_bytes, void *stream) {
+    return decode_common(cfg, S, n_q, q, q_pos, k_cache, v_cache, cap, sinks, out, ws, ws_bytes, stream);
 }
 
 mimo_status mimo_kv_ring_append(const mimo_attn_cfg *cfg, int32_t S, const uint16_t *k_new,

@@ -155,7 +155,14 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
     }
 }
 
-__global__ __launch_bounds__(512) void decode_partial_kernel(DecodeArgs a) {
+// NC column tiles of 16 (query token, query head) pairs per wave, which all
+// use the K/V rows the wave loads once per step; more tiles go to more waves
+// of the same KV head.  MAXT: workgroup size bound (512: eight KV-head waves,
+// two per SIMD; 256: up to four waves, one per SIMD with the whole register
+// file, for the tiles of multi-query decode).
+template <int NC, int MAXT>
+__global__ __attribute__((amdgpu_flat_work_group_size(64, MAXT), amdgpu_waves_per_eu(MAXT / 256, MAXT / 256)))
+void decode_partial_kernel(DecodeArgs a) {
     const int64_t wg = blockIdx.x;
     const int64_t Ts = a.plan_start[a.S];
     const int lo = a.plan_wg_seq[wg];   // meaningful only below the groups used
@@ -163,14 +170,26 @@ __global__ __launch_bounds__(512) void decode_partial_kernel(DecodeArgs a) {
     if (wg >= ng) return;
     const int64_t r_lo = wg * Ts / ng, r_hi = (wg + 1) * Ts / ng;
 
-    const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;   // one wave per KV head
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int gl = w / a.wph, sub = w - gl * a.wph;
+    const int g = blockIdx.y * a.kvpw + gl;            // this wave's KV head
     const int lg = lane >> 4, r16 = lane & 15;
     const int G = a.Hq / a.Hkv;
-    const int head = g * G + r16;
-    const bool head_ok = r16 < G;
+    const int nq = a.n_q;
+    // column r16 of tile t is (query token tok, query head hd): col = G * tok + head in group
+    int tok[NC], hd[NC];
+    bool ok[NC];
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+        const int col = 16 * (NC * sub + t) + r16;
+        tok[t] = col / G;
+        hd[t] = g * G + (col - tok[t] * G);
+        ok[t] = tok[t] < nq;
+    }
     const float cl2 = a.scale_log2;
     const size_t krs = (size_t)a.Hkv * kDqk, vrs = (size_t)a.Hkv * kDv;
     const int win = a.window > 0 ? a.window : 0x7fffffff;
+    const bool always_mask = a.window > 0 || nq > 1;
 
     for (int s = lo; s < a.S; ++s) {
         const int64_t st0 = a.plan_start[s];
@@ -180,12 +199,12 @@ __global__ __launch_bounds__(512) void decode_partial_kernel(DecodeArgs a) {
         const int64_t seg_hi = st1 < r_hi ? st1 : r_hi;
         if (seg_lo >= seg_hi) continue;
 
-        const int64_t p = a.pos[s];   // >= 0: the sequence has steps
+        const int64_t p = a.pos[s];   // newest query's position (>= 0: the sequence has steps)
         const int n = live_slots(p, a.cap);
 
-        u32x4 qf[6];
-        float m_run, l_run;
-        f32x4 O[8];
+        u32x4 qf[NC][6];
+        float m_run[NC], l_run[NC];
+        f32x4 O[NC][8];
 
         const uint16_t *kbase = a.k_cache + (size_t)s * a.cap * krs + (size_t)g * kDqk + 8 * lg;
         const uint16_t *vbase = a.v_cache + (size_t)s * a.cap * vrs + (size_t)g * kDv + 8 * r16;
@@ -212,74 +231,73 @@ __global__ __launch_bounds__(512) void decode_partial_kernel(DecodeArgs a) {
             }
         };
 
-        auto visible = [&](int j) -> bool {
-            if (j >= n) return false;
-            if (a.window > 0) {
-                int d = pm - j;
-                if (d < 0) d += a.cap;
-                return d < win && (int64_t)d <= p;
-            }
-            return true;
-        };
-
         auto compute = [&](StepBuf &bf, int j0) {
-            f32x4 S[2];
+            // the lane's 8 keys are j0 + 16*sb + 4*lg + i (rows of its S^T registers and
+            // of its V loads); d = how many positions each lies before the newest query
+            const bool masked = always_mask || j0 + kStep > kend;
+            u32x4 pf[NC];
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-                S[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < NC; ++t) {
+                f32x4 S[2];
 #pragma unroll
-                for (int ch = 0; ch < 6; ++ch) S[sb] = mfma16(bf.k[sb][ch], qf[ch], S[sb]);
-            }
-            // lane's keys: j0 + 16*sb + 4*lg + i  (rows of its S^T registers and of its V loads)
-            if (j0 + kStep > kend || a.window > 0) {
+                for (int sb = 0; sb < 2; ++sb) {
+                    S[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ch = 0; ch < 6; ++ch) S[sb] = mfma16(bf.k[sb][ch], qf[t][ch], S[sb]);
+                }
+                if (masked) {
+                    const int delta = nq - 1 - tok[t];   // the column's query lies delta before the newest
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int j = j0 + 16 * (e >> 2) + 4 * lg + (e & 3);
+                        int d = pm - j;
+                        if (d < 0) d += a.cap;
+                        const bool live = j < n && (int64_t)d <= p;
+                        const int dd = d - delta;
+                        if (!(live && dd >= 0 && dd < win)) S[e >> 2][e & 3] = kNegInf;
+                        // no query of the sequence sees it: drop its value row (it may hold NaN)
+                        if (t == 0 && !(live && d - (nq - 1) < win)) bf.v[e] = u32x4{0, 0, 0, 0};
+                    }
+                }
+                float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
+                                 fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
+                mx = max_xor16(mx);
+                mx = max_xor32(mx);
+                const float mc = mx * cl2;
+                const bool need = mc > m_run[t] + 8.0f;
+                if (__any(need)) {
+                    const float alpha = need ? __builtin_amdgcn_exp2f(m_run[t] - mc) : 1.0f;
+                    if (need) m_run[t] = mc;
+                    l_run[t] *= alpha;
+#pragma unroll
+                    for (int tt = 0; tt < 8; ++tt) O[t][tt] *= alpha;
+                }
+                const float mu = (m_run[t] == kNegInf) ? 0.0f : m_run[t];
+                float ls = 0.0f;
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        if (!visible(j0 + 16 * sb + 4 * lg + i)) {
-                            S[sb][i] = kNegInf;
-                            bf.v[4 * sb + i] = u32x4{0, 0, 0, 0};
-                        }
+                        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[sb][i], cl2, -mu));
+                        S[sb][i] = pv;
+                        ls += pv;
                     }
+                l_run[t] += ls;
+                pf[t][0] = pack_bf16(S[0][0], S[0][1]);
+                pf[t][1] = pack_bf16(S[0][2], S[0][3]);
+                pf[t][2] = pack_bf16(S[1][0], S[1][1]);
+                pf[t][3] = pack_bf16(S[1][2], S[1][3]);
             }
-            float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
-                             fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
-            mx = max_xor16(mx);
-            mx = max_xor32(mx);
-            const float mc = mx * cl2;
-            const bool need = mc > m_run + 8.0f;
-            if (__any(need)) {
-                const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mc) : 1.0f;
-                if (need) m_run = mc;
-                l_run *= alpha;
+            // O^T tile tt covers dv = 8*r + tt (r = 0..15): lane's V chunk is dv 8*r16..8*r16+7
 #pragma unroll
-                for (int t = 0; t < 8; ++t) O[t] *= alpha;
-            }
-            const float mu = (m_run == kNegInf) ? 0.0f : m_run;
-            float ls = 0.0f;
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[sb][i], cl2, -mu));
-                    S[sb][i] = pv;
-                    ls += pv;
-                }
-            l_run += ls;
-            u32x4 pf;
-            pf[0] = pack_bf16(S[0][0], S[0][1]);
-            pf[1] = pack_bf16(S[0][2], S[0][3]);
-            pf[2] = pack_bf16(S[1][0], S[1][1]);
-            pf[3] = pack_bf16(S[1][2], S[1][3]);
-            // O^T tile t covers dv = 8*r + t (r = 0..15): lane's V chunk is dv 8*r16..8*r16+7
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+            for (int tt = 0; tt < 8; ++tt) {
+                const uint32_t sel = (tt & 1) ? 0x07060302u : 0x05040100u;
                 u32x4 vt;
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    vt[u] = __builtin_amdgcn_perm(bf.v[2 * u + 1][t >> 1], bf.v[2 * u][t >> 1], sel);
-                O[t] = mfma16(vt, pf, O[t]);
+                    vt[u] = __builtin_amdgcn_perm(bf.v[2 * u + 1][tt >> 1], bf.v[2 * u][tt >> 1], sel);
+#pragma unroll
+                for (int t = 0; t < NC; ++t) O[t][tt] = mfma16(vt, pf[t], O[t][tt]);
             }
         };
 
@@ -287,27 +305,29 @@ __global__ __launch_bounds__(512) void decode_partial_kernel(DecodeArgs a) {
             StepBuf A, B;
             int j0 = kbeg;
             if (j0 < kend) load(A, j0);   // first step's loads go out before q's
-            // ---- q (B operand): head r16; contraction slot (ch, lg, e) is dim 32*ch + 8*lg + e.
-            // Chunks 0 and 1 of a lane are rotate-half partners (dims i and i+32).
-            if (head_ok) {
-                const uint16_t *qrow = a.q + ((size_t)s * a.Hq + head) * kDqk + 8 * lg;
+            // ---- q (B operand) of each tile: contraction slot (ch, lg, e) is dim
+            // 32*ch + 8*lg + e; chunks 0 and 1 of a lane are rotate-half partners
 #pragma unroll
-                for (int ch = 0; ch < 6; ++ch) qf[ch] = ldg128(qrow + 32 * ch);
-                rope_rotate8(qf[0], qf[1], a.rt, 8 * lg, p);
-            } else {
+            for (int t = 0; t < NC; ++t) {
+                if (ok[t]) {
+                    const uint16_t *qrow = a.q + (((size_t)s * nq + tok[t]) * a.Hq + hd[t]) * kDqk + 8 * lg;
 #pragma unroll
-                for (int ch = 0; ch < 6; ++ch) qf[ch] = u32x4{0, 0, 0, 0};
+                    for (int ch = 0; ch < 6; ++ch) qf[t][ch] = ldg128(qrow + 32 * ch);
+                    rope_rotate8(qf[t][0], qf[t][1], a.rt, 8 * lg, p - (nq - 1 - tok[t]));
+                } else {
+#pragma unroll
+                    for (int ch = 0; ch < 6; ++ch) qf[t][ch] = u32x4{0, 0, 0, 0};
+                }
+                if (seg_lo == st0 && a.sinks && ok[t]) {
+                    m_run[t] = a.sinks[hd[t]] * kLog2e;
+                    l_run[t] = (lg == 0) ? 1.0f : 0.0f;
+                } else {
+                    m_run[t] = kNegInf;
+                    l_run[t] = 0.0f;
+                }
+#pragma unroll
+                for (int tt = 0; tt < 8; ++tt) O[t][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-
-            if (seg_lo == st0 && a.sinks && head_ok) {
-                m_run = a.sinks[head] * kLog2e;
-                l_run = (lg == 0) ? 1.0f : 0.0f;
-            } else {
-                m_run = kNegInf;
-                l_run = 0.0f;
-            }
-#pragma unroll
-            for (int t = 0; t < 8; ++t) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
             while (j0 < kend) {
                 int j1 = j0 + kStep;
                 if (j1 < kend) load(B, j1);
@@ -321,49 +341,55 @@ __global__ __launch_bounds__(512) void decode_partial_kernel(DecodeArgs a) {
             }
         }
 
-        // ---- this piece for the wave's heads: lane (lg, r16) holds, for each i,
-        // dv [32*lg + 8*i, +8) of head r16 in O[0..7][i]
-        l_run = sum_xor16(l_run);
-        l_run = sum_xor32(l_run);
-        if (!head_ok) continue;
+        // ---- this piece: lane (lg, r16) holds, for each i, dv [32*lg + 8*i, +8) of
+        // its column in O[t][0..7][i]
         const int cover = a.plan_cover[s];
-        if (cover == 1) {
-            const float inv = l_run > 0.0f ? a.v_scale / l_run : 0.0f;
-            uint16_t *dst = a.out + ((size_t)s * a.Hq + head) * kDv + 32 * lg;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                u32x4 r;
+        for (int t = 0; t < NC; ++t) {
+            float lt = sum_xor16(l_run[t]);
+            lt = sum_xor32(lt);
+            if (!ok[t]) continue;
+            const size_t row = ((size_t)s * nq + tok[t]) * a.Hq + hd[t];
+            if (cover == 1) {
+                const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
+                uint16_t *dst = a.out + row * kDv + 32 * lg;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) r[e] = pack_bf16(O[2 * e][i] * inv, O[2 * e + 1][i] * inv);
-                stg128(dst + 8 * i, r);
-            }
-        } else {
-            const size_t part = (size_t)(a.plan_part[s] + (int32_t)(wg - a.plan_first[s])) * a.Hq + head;
-            float *dst = a.ws_o + part * kDv + 32 * lg;
+                for (int i = 0; i < 4; ++i) {
+                    u32x4 r;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const f32x4 lo4 = {O[0][i], O[1][i], O[2][i], O[3][i]};
-                const f32x4 hi4 = {O[4][i], O[5][i], O[6][i], O[7][i]};
-                *reinterpret_cast<f32x4 *>(dst + 8 * i) = lo4;
-                *reinterpret_cast<f32x4 *>(dst + 8 * i + 4) = hi4;
-            }
-            if (lg == 0) {
-                a.ws_ml[2 * part] = m_run;
-                a.ws_ml[2 * part + 1] = l_run;
+                    for (int e = 0; e < 4; ++e) r[e] = pack_bf16(O[t][2 * e][i] * inv, O[t][2 * e + 1][i] * inv);
+                    stg128(dst + 8 * i, r);
+                }
+            } else {
+                const size_t part = (size_t)(a.plan_part[s] + (int32_t)(wg - a.plan_first[s]));
+                const size_t idx = (part * nq + tok[t]) * a.Hq + hd[t];
+                float *dst = a.ws_o + idx * kDv + 32 * lg;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4 lo4 = {O[t][0][i], O[t][1][i], O[t][2][i], O[t][3][i]};
+                    const f32x4 hi4 = {O[t][4][i], O[t][5][i], O[t][6][i], O[t][7][i]};
+                    *reinterpret_cast<f32x4 *>(dst + 8 * i) = lo4;
+                    *reinterpret_cast<f32x4 *>(dst + 8 * i + 4) = hi4;
+                }
+                if (lg == 0) {
+                    a.ws_ml[2 * idx] = m_run[t];
+                    a.ws_ml[2 * idx + 1] = lt;
+                }
             }
         }
     }
 }
 
-// One workgroup of 128 threads (one per dv) per (sequence, query head).
+// One workgroup of 128 threads (one per dv) per (sequence, query token, query head).
 __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
     __shared__ float wsc[kMaxGroups];
     __shared__ float red[2][2];
-    const int s = blockIdx.x / a.Hq;
-    const int qh = blockIdx.x - s * a.Hq;
+    const int rows = a.n_q * a.Hq;                  // output rows of one sequence
+    const int s = blockIdx.x / rows;
+    const int rr = blockIdx.x - s * rows;           // token * Hq + head
     const int cover = a.plan_cover[s];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    uint16_t *dst = a.out + ((size_t)s * a.Hq + qh) * kDv + tid;
+    uint16_t *dst = a.out + (size_t)blockIdx.x * kDv + tid;
     if (cover == 0) {   // no visible slot: zero output (the sink carries no value)
         *dst = 0;
         return;
@@ -372,7 +398,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
     const size_t part0 = (size_t)a.plan_part[s];
     // 1) max over the pieces' maxima
     float M = kNegInf;
-    for (int i = tid; i < cover; i += 128) M = fmaxf(M, a.ws_ml[2 * ((part0 + i) * a.Hq + qh)]);
+    for (int i = tid; i < cover; i += 128) M = fmaxf(M, a.ws_ml[2 * ((part0 + i) * rows + rr)]);
     for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     if (lane == 0) red[0][w] = M;
     __syncthreads();
@@ -380,7 +406,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
     // 2) piece weights and the total sum
     float L = 0.0f;
     for (int i = tid; i < cover; i += 128) {
-        const size_t pi = (part0 + i) * a.Hq + qh;
+        const size_t pi = (part0 + i) * rows + rr;
         const float mi = a.ws_ml[2 * pi];
         const float sc = (mi == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(mi - M);
         wsc[i] = sc;
@@ -391,8 +417,8 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
     __syncthreads();
     L = red[1][0] + red[1][1];
     // 3) weighted sum of the partial outputs
-    const float *src = a.ws_o + (part0 * a.Hq + qh) * kDv + tid;
-    const size_t stride = (size_t)a.Hq * kDv;
+    const float *src = a.ws_o + (part0 * rows + rr) * kDv + tid;
+    const size_t stride = (size_t)rows * kDv;
     float o = 0.0f;
 #pragma unroll 8
     for (int i = 0; i < cover; ++i) o += src[i * stride] * wsc[i];
@@ -400,28 +426,55 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
     *dst = (uint16_t)(pack_bf16(r, 0.0f) & 0xffffu);
 }
 
-namespace {
+DecodeGeom decode_geometry(int32_t Hq, int32_t Hkv, int32_t n_q) {
+    DecodeGeom m{};
+    const int G = Hq / Hkv;
+    const int tiles = (G * n_q + 15) / 16;
+    if (n_q == 1) {   // one tile per wave, one wave per KV head, every KV head in the workgroup
+        m.nc = 1; m.wph = 1; m.kvpw = Hkv;
+    } else {          // up to 2 tiles per wave, at most four waves per workgroup
+        m.wph = (tiles + 1) / 2;
+        m.nc = (tiles + m.wph - 1) / m.wph;
+        m.kvpw = m.wph >= 4 ? 1 : 4 / m.wph;
+        while (Hkv % m.kvpw) --m.kvpw;
+    }
+    m.n_hsub = Hkv / m.kvpw;
+    m.threads = 64 * m.kvpw * m.wph;
+    m.n_groups = kDecodeWaves / (Hkv * m.wph);
+    if (m.n_groups < 1) m.n_groups = 1;
+    return m;
+}
 
-int32_t decode_groups(int32_t Hkv) { return kDecodeWaves / Hkv; }
+namespace {
 
 // partials: every sequence shared by several workgroups has one piece per
 // workgroup on it, and the pieces of all sequences number < groups + S
-size_t decode_partial_slots(int32_t S, int32_t Hkv) { return (size_t)decode_groups(Hkv) + (size_t)S; }
+size_t decode_partial_slots(int32_t S, const DecodeGeom &m) { return (size_t)m.n_groups + (size_t)S; }
+
+template <int NC, int MAXT>
+void launch_partial(const DecodeArgs &a, const DecodeGeom &m, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_partial_kernel<NC, MAXT>), dim3(m.n_groups, m.n_hsub), dim3(m.threads), 0, stream, a);
+}
 
 }  // namespace
 
-size_t decode_workspace_bytes(int32_t S, int32_t Hq, int32_t Hkv) {
-    const size_t parts = decode_partial_slots(S, Hkv) * (size_t)Hq * (kDv + 2) * sizeof(float);
-    const size_t plan = (size_t)(S + 1) * sizeof(int64_t) + ((size_t)3 * S + decode_groups(Hkv)) * sizeof(int32_t);
+size_t decode_workspace_bytes(int32_t S, int32_t Hq, int32_t Hkv, int32_t n_q) {
+    const DecodeGeom m = decode_geometry(Hq, Hkv, n_q);
+    const size_t parts = decode_partial_slots(S, m) * (size_t)n_q * Hq * (kDv + 2) * sizeof(float);
+    const size_t plan = (size_t)(S + 1) * sizeof(int64_t) + ((size_t)3 * S + m.n_groups) * sizeof(int32_t);
     return parts + plan;
 }
 
 hipError_t launch_decode(DecodeArgs a, hipStream_t stream) {
-    if (a.Hkv < 1 || a.Hkv > 8) return hipErrorInvalidValue;
-    a.n_groups = decode_groups(a.Hkv);
-    const size_t parts = decode_partial_slots(a.S, a.Hkv);
-    a.ws_ml = a.ws_o + parts * a.Hq * kDv;
-    a.plan_start = reinterpret_cast<int64_t *>(a.ws_ml + parts * a.Hq * 2);
+    if (a.Hkv < 1 || a.Hkv > 8 || a.n_q < 1 || a.Hq / a.Hkv * a.n_q > 128) return hipErrorInvalidValue;
+    const DecodeGeom m = decode_geometry(a.Hq, a.Hkv, a.n_q);
+    a.n_groups = m.n_groups;
+    a.wph = m.wph;
+    a.kvpw = m.kvpw;
+    const size_t parts = decode_partial_slots(a.S, m);
+    const size_t rows = (size_t)a.n_q * a.Hq;
+    a.ws_ml = a.ws_o + parts * rows * kDv;
+    a.plan_start = reinterpret_cast<int64_t *>(a.ws_ml + parts * rows * 2);
     a.plan_first = reinterpret_cast<int32_t *>(a.plan_start + a.S + 1);
     a.plan_cover = a.plan_first + a.S;
     a.plan_part = a.plan_cover + a.S;
@@ -429,10 +482,12 @@ hipError_t launch_decode(DecodeArgs a, hipStream_t stream) {
     hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_partial_kernel, dim3(a.n_groups), dim3(64 * a.Hkv), 0, stream, a);
+    if (a.n_q == 1) launch_partial<1, 512>(a, m, stream);
+    else if (m.nc == 1) launch_partial<1, 256>(a, m, stream);
+    else launch_partial<2, 256>(a, m, stream);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3(a.S * a.Hq), dim3(kDv), 0, stream, a);
+    hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(a.S * rows)), dim3(kDv), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -48,28 +48,39 @@ hipError_t launch_prefill(PrefillArgs a, hipStream_t stream);
 #ifndef MIMO_DECODE_MIN_STEPS
 #define MIMO_DECODE_MIN_STEPS 1
 #endif
-// The batch's 32-slot steps are split evenly over kDecodeWaves / Hkv workgroups
-// (one wave per KV head), each taking at least kDecodeMinSteps steps.
+// The batch's 32-slot steps are split evenly over step ranges, each taking at
+// least kDecodeMinSteps steps; the partial pass runs kDecodeWaves waves in all.
 constexpr int kDecodeWaves = MIMO_DECODE_WAVES;
 constexpr int kDecodeMinSteps = MIMO_DECODE_MIN_STEPS;
 constexpr int kDecodeMaxCap = 1 << 30;
 struct DecodeArgs {
     const uint16_t *q, *k_cache, *v_cache;
-    const int64_t *pos;
+    const int64_t *pos;   // newest query's position per sequence
     const float *sinks;   // nullable
     uint16_t *out;
-    float *ws_o;          // [n_groups + S, Hq, 128] partial outputs
-    float *ws_ml;         // [n_groups + S, Hq, 2] partial (max, sum)
+    float *ws_o;          // [n_groups + S, n_q, Hq, 128] partial outputs
+    float *ws_ml;         // [n_groups + S, n_q, Hq, 2] partial (max, sum)
     int64_t *plan_start;  // [S + 1] first step of each sequence; [S] = total steps
     int32_t *plan_first;  // [S] first workgroup on the sequence
     int32_t *plan_cover;  // [S] workgroups on the sequence (0: nothing visible)
     int32_t *plan_part;   // [S] first partial slot of the sequence
     int32_t *plan_wg_seq; // [n_groups] sequence holding each workgroup's first step
-    int32_t S, Hq, Hkv, cap, window, n_groups;
+    int32_t S, Hq, Hkv, cap, window, n_q;
+    int32_t n_groups, wph, kvpw;   // filled by the launcher
     float scale_log2, v_scale;
     RopeTurns rt;
 };
-size_t decode_workspace_bytes(int32_t S, int32_t Hq, int32_t Hkv);
+// Launch shape of the decode partial pass for a head geometry and query count.
+struct DecodeGeom {
+    int nc;        // 16-column (query token, head) tiles per wave
+    int wph;       // waves per KV head
+    int kvpw;      // KV heads per workgroup
+    int n_hsub;    // workgroups side by side on one step range (KV head subsets)
+    int threads;   // workgroup size
+    int n_groups;  // step ranges
+};
+DecodeGeom decode_geometry(int32_t Hq, int32_t Hkv, int32_t n_q);
+size_t decode_workspace_bytes(int32_t S, int32_t Hq, int32_t Hkv, int32_t n_q);
 hipError_t launch_decode(DecodeArgs a, hipStream_t stream);
 
 }  // namespace mimo

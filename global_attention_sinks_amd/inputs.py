@@ -169,6 +169,30 @@ def decode_inputs(S: int, cap: int, n_q_heads: int, n_kv_heads: int, seed: int,
     }
 
 
+def decode_multi_inputs(S: int, n_q: int, cap: int, n_q_heads: int, n_kv_heads: int, seed: int,
+                        window: int, pos: np.ndarray, with_sinks: bool) -> dict:
+    """n_q query tokens per sequence [S,n_q,Hq,192], the newest at pos[s], over a
+    cache [S,cap,Hkv,D] in which the slots of the positions some token can see
+    (pos - n_q + 1 - window + 1 .. pos for a ring, 0 .. pos otherwise) hold draws
+    and every other slot holds bf16 NaN."""
+    cq, ck, cv, cs, _ = _children(seed)
+    pos = np.asarray(pos, dtype=np.int64)
+    q = normal_bf16(cq, (S, n_q, n_q_heads, D_QK))
+    kc = np.full((S, cap, n_kv_heads, D_QK), BF16_NAN, dtype=np.uint16)
+    vc = np.full((S, cap, n_kv_heads, D_V), BF16_NAN, dtype=np.uint16)
+    kseeds, vseeds = ck.spawn(S), cv.spawn(S)
+    for s in range(S):
+        p = int(pos[s])
+        if p < 0:
+            continue
+        lo = max(0, p - (n_q - 1) - window + 1) if window > 0 else 0
+        slots = np.arange(lo, p + 1) % cap
+        kc[s, slots] = normal_bf16(kseeds[s], (len(slots), n_kv_heads, D_QK))
+        vc[s, slots] = normal_bf16(vseeds[s], (len(slots), n_kv_heads, D_V))
+    return {"q": q, "pos": pos, "k_cache": kc, "v_cache": vc,
+            "sinks": normal_f32(cs, (n_q_heads,)) if with_sinks else None}
+
+
 def global_prefill_chunk(T: int, n_q_heads: int, n_kv_heads: int, seed: int, t_lo: int, t_hi: int) -> dict:
     """Query rows [t_lo, t_hi) of a B=1 prefill of T tokens and the keys/values
     0..t_hi-1, drawn exactly as prefill_inputs(1, T, ...) would draw them."""

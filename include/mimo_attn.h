@@ -174,6 +174,31 @@ mimo_status mimo_attn_decode(const mimo_attn_cfg *cfg, int32_t S, const uint16_t
 size_t mimo_attn_decode_workspace_size(const mimo_attn_cfg *cfg, int32_t S, int32_t cap);
 
 /*
+ * Multi-query decode for speculative verification: n_q query tokens per
+ * sequence, the newest at q_pos[s] and token i at q_pos[s] - (n_q - 1 - i),
+ * each attending causally to the cache (a draft token sees the tokens before
+ * it, the earlier drafts included, and itself).  The pages' engines verify 4
+ * draft tokens (EAGLE through the MTP layers: miles MiMo-V2.6-Flash page,
+ * section 4.2) or 7 to 8 (DFlash: vLLM recipe page, DFlash launch; SGLang
+ * cookbook page, DFlash and caching section).
+ *   q   : [S, n_q, num_q_heads, 192] unrotated;  out : [S, n_q, num_q_heads, 128].
+ *   The cache holds every token up to q_pos[s] (the drafts appended first), with
+ *   the cache rule of mimo_attn_decode; a ring needs cap >= window + n_q - 1 so
+ *   that the oldest draft's window is still in it.  A token at a negative
+ *   position sees nothing and gets a zero row.
+ *   Needs (num_q_heads / num_kv_heads) * n_q <= 128.  n_q = 1 is mimo_attn_decode.
+ *   ws  : device workspace of at least mimo_attn_decode_multi_workspace_size() bytes.
+ */
+mimo_status mimo_attn_decode_multi(const mimo_attn_cfg *cfg, int32_t S, int32_t n_q, const uint16_t *q,
+                                   const int64_t *q_pos, const uint16_t *k_cache, const uint16_t *v_cache,
+                                   int32_t cap, const float *sinks, uint16_t *out, void *ws,
+                                   size_t ws_bytes, void *stream);
+
+/* Workspace bytes mimo_attn_decode_multi needs (independent of cap; 0 for an
+ * unsupported cfg or n_q). */
+size_t mimo_attn_decode_multi_workspace_size(const mimo_attn_cfg *cfg, int32_t S, int32_t n_q, int32_t cap);
+
+/*
  * Append one new token per sequence: rotate k_new at pos (partial RoPE) and
  * write it and v_new into slot pos mod cap (the window-sized KV of the Gaudi
  * recipe page keeps only the window; a global cache with cap above every

@@ -212,6 +212,27 @@ def decode(q, q_pos, k_cache, v_cache, *, sinks=None, window: int, base: float,
     return np.stack(outs)
 
 
+def decode_multi(q, q_pos, k_cache, v_cache, *, sinks=None, window: int, base: float, seqs=None,
+                 n_threads: int = 0):
+    """n_q query tokens per sequence, the newest at q_pos[s], token i at
+    q_pos[s] - (n_q - 1 - i); each sees the cache tokens its own position sees.
+    q [S,n_q,Hq,192] unrotated.  Returns out [len(seqs),n_q,Hq,128] fp64
+    (a token at a negative position gets zeros)."""
+    S, nq, hq = q.shape[:3]
+    cap = k_cache.shape[1]
+    seqs = range(S) if seqs is None else seqs
+    outs = np.zeros((len(seqs), nq, hq, v_cache.shape[3]))
+    for r, s in enumerate(seqs):
+        for i in range(nq):
+            p = int(q_pos[s]) - (nq - 1 - i)
+            if p < 0:
+                continue
+            slots, tpos = cache_slots(p, cap, window)
+            outs[r, i] = attention(q[s, i][None], np.array([p]), k_cache[s, slots], tpos, v_cache[s, slots],
+                                   sinks=sinks, window=window, base=base, k_rotated=True, n_threads=n_threads)[0]
+    return outs
+
+
 def kv_ring_append_rows(k_new, v_new, pos, base: float):
     """What the append writes: rope(k_new) at pos and v_new unchanged, fp64."""
     return rope_partial(k_new, pos, base), v_new

@@ -162,6 +162,36 @@ def test_decode_workspace(lib):
     assert dec(lib, cfg_swa(), S=4, cap=128, ws=None, ws_bytes=0) == WS
 
 
+def decm(lib, cfg, S=4, nq=4, cap=256, ws=FAKE, ws_bytes=1 << 30, q=FAKE):
+    return lib.mimo_attn_decode_multi(ctypes.byref(cfg), S, nq, q, FAKE, FAKE, FAKE, cap, None, FAKE, ws,
+                                      ws_bytes, None)
+
+
+def test_decode_multi_contract(lib):
+    assert decm(lib, cfg_swa(), nq=0) == INVAL
+    assert decm(lib, cfg_swa(), nq=8, cap=134) == INVAL            # ring shorter than window + n_q - 1
+    assert "window + n_q - 1" in err(lib)
+    assert decm(lib, cfg_glob(), nq=9) == UNSUP                    # 16 heads x 9 tokens > 128 columns
+    assert decm(lib, cfg_swa(), nq=17) == UNSUP                    # 8 heads x 17 tokens
+    assert decm(lib, cfg_glob(), S=0, q=None) == OK
+    assert decm(lib, cfg_glob(), q=None) == INVAL
+
+
+def test_decode_multi_workspace(lib):
+    def size(cfg, S, nq):
+        return lib.mimo_attn_decode_multi_workspace_size(ctypes.byref(cfg), S, nq, 4096)
+
+    def expect(S, nq, groups):
+        return (groups + S) * nq * 64 * (128 + 2) * 4 + (S + 1) * 8 + 3 * S * 4 + groups * 4
+    # step ranges: 1024 waves over the KV heads and the waves each KV head's columns need
+    assert size(cfg_glob(), 16, 1) == lib.mimo_attn_decode_workspace_size(ctypes.byref(cfg_glob()), 16, 4096)
+    assert size(cfg_swa(), 64, 8) == expect(64, 8, 1024 // (8 * 2))
+    assert size(cfg_glob(), 16, 4) == expect(16, 4, 1024 // (4 * 2))
+    assert size(cfg_glob(), 16, 8) == expect(16, 8, 1024 // (4 * 4))
+    assert size(cfg_glob(), 16, 9) == 0
+    assert decm(lib, cfg_glob(), S=16, nq=4, ws_bytes=expect(16, 4, 128) - 1) == WS
+
+
 def test_rope_and_append_contract(lib):
     c = cfg_swa()
     assert lib.mimo_rope_partial(ctypes.byref(c), FAKE, None, 4, 8, FAKE, None) == INVAL

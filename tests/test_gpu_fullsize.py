@@ -8,6 +8,7 @@ computes rows one by one); every output is also checked to be finite.
     sequences (KV lengths ~U[32768, 131072], cap 131072), NaN in unused slots
   * long global prefill T=524288 in query chunks of 65536: the first, a middle
     and the last chunk, each against its whole prefix
+  * multi-query decode: 64 sliding sequences x 8 draft tokens, 16 global x 4
   * serving chunks of 8192 tokens, packed: four sliding-window chunks that
     continue sequences (127 earlier keys each) and four global chunks against
     prefixes of up to 57344 tokens
@@ -126,3 +127,29 @@ def test_packed_serving_chunks():
             ref = oracle.attention(d["q"][q0 + rows], kp[lk - lq + rows], d["k"][k0:k0 + lk], kp,
                                    d["v"][k0:k0 + lk], sinks=d["sinks"], window=cfg.window, base=cfg.rope_base)
             assert_parity(got_all[q0 + rows], ref, f"{layer} chunk {b}, {len(rows)} rows")
+
+
+def test_multi_query_decode_full():
+    """Speculative verification at the mixed-decode sizes: 64 sliding sequences
+    with 8 draft tokens (ring of 135) and 16 global sequences with 4."""
+    for name, S, nq, cap, hkv, window, base, sinks, seed, check in (
+            ("sliding", 64, 8, 135, 8, 128, 1e4, True, 1007, list(range(0, 64, 4))),
+            ("global", 16, 4, 131072, 4, 0, 1e7, False, 1008, [0, 7, 15])):
+        rng = np.random.Generator(np.random.PCG64(seed))
+        if window:
+            pos = rng.integers(128, 131072, size=S)
+        else:
+            pos = rng.integers(32768, 131072, size=S, endpoint=True) - 1
+        say(f"full-size multi-query decode: {name}, {S} sequences x {nq} tokens")
+        dd = gen.decode_multi_inputs(S, nq, cap, 64, hkv, seed=seed, window=window, pos=pos, with_sinks=sinks)
+        cfg = Bd.swa_cfg() if window else Bd.global_cfg()
+        ws = torch.empty(Bd.mimo_attn_decode_multi_workspace_size(cfg, S, nq, cap), dtype=torch.uint8, device="cuda")
+        out = torch.empty((S, nq, 64, 128), dtype=torch.bfloat16, device="cuda")
+        Bd.mimo_attn_decode_multi(cfg, dev_bf16(dd["q"]), dev(dd["pos"]), dev_bf16(dd["k_cache"]),
+                                  dev_bf16(dd["v_cache"]), dev(dd["sinks"]) if sinks else None, out, ws=ws)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(out).all())
+        got = host_f64(out)[check]
+        ref = oracle.decode_multi(dd["q"], dd["pos"], dd["k_cache"], dd["v_cache"], sinks=dd["sinks"],
+                                  window=window, base=base, seqs=check)
+        assert_parity(got, ref, f"{name}, {len(check)} of {S} sequences")

@@ -384,6 +384,38 @@ def test_decode_cache_rule_matches_prefill_rows():
         assert np.max(np.abs(o[0] - pref[0, p])) < 1e-13
 
 
+@pytest.mark.parametrize("window,cap", [(128, 135), (0, 400)])
+def test_decode_multi_matches_prefill_rows(window, cap):
+    """n_q draft tokens verified together over a cache that holds them see exactly
+    what their prefill rows see (exactly representable keys, as above); a token
+    at a negative position gets zeros."""
+    T, nq = 300, 8
+    d = gen.prefill_inputs(1, T, 8, 1, seed=10, with_sinks=window > 0)
+    k = d["k"].copy()
+    k[..., :64] = 0
+    if window:
+        pref = oracle.prefill_swa(d["q"], k, d["v"], d["sinks"], window=window, base=1e4)[0]
+    else:
+        pref = oracle.prefill_global(d["q"], k, d["v"], base=1e7)[0]
+    for p in (3, 7, 130, 299):
+        kc = np.full((1, cap, 1, 192), gen.BF16_NAN, np.uint16)
+        vc = np.full((1, cap, 1, 128), gen.BF16_NAN, np.uint16)
+        for t in range(max(0, p - cap + 1), p + 1):
+            kc[0, t % cap] = k[0, t]
+            vc[0, t % cap] = d["v"][0, t]
+        q = np.zeros((1, nq, 8, 192), np.uint16)
+        for i in range(nq):
+            q[0, i] = d["q"][0, max(0, p - nq + 1 + i)]
+        o = oracle.decode_multi(q, np.array([p]), kc, vc, sinks=d["sinks"], window=window,
+                                base=1e4 if window else 1e7)[0]
+        for i in range(nq):
+            t = p - nq + 1 + i
+            if t < 0:
+                assert np.all(o[i] == 0.0)
+            else:
+                assert np.max(np.abs(o[i] - pref[t])) < 1e-13
+
+
 def test_input_rounding_is_round_to_nearest_even():
     x = np.array([1.0, 1.00390625, 1.01171875, -2.5, 3.0e-3, 65504.0], np.float32)
     b = gen.f32_to_bf16_bits(x)
