@@ -19,6 +19,10 @@ query chunks of 65536, each against its full causal prefix.
 the mixed-decode sizes: 64 sliding sequences (ring of 128 + n_q - 1) and 16
 global sequences, with n_q = 4 (EAGLE) and n_q = 8 (DFlash) draft tokens.
 
+--workload paged_decode times decode over paged caches (128-slot blocks in
+shuffled pools) at the mixed-decode sizes: the 16 global sequences with bf16
+and with fp8 e4m3 pools, and the 64 sliding sequences with fp8 pools.
+
 --workload serving_chunks times packed (THD) serving chunks of 8192 tokens:
 four sliding-window chunks that continue sequences at positions 8192, 65536,
 131072 and 262144 (each with the 127 keys before it) and four global chunks
@@ -250,7 +254,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["layer_step", "long_prefill", "serving_chunks", "spec_decode"], default="layer_step")
+    ap.add_argument("--workload", choices=["layer_step", "long_prefill", "serving_chunks", "spec_decode", "paged_decode"], default="layer_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -287,6 +291,8 @@ def main():
         return main_serving_chunks(args, torch, gen, Bd)
     if args.workload == "spec_decode":
         return main_spec_decode(args, torch, gen, Bd)
+    if args.workload == "paged_decode":
+        return main_paged_decode(args, torch, gen, Bd)
 
     ph = setup_layer_step(torch, gen, Bd)
     names = ["swa_prefill", "global_prefill", "append_swa", "append_global", "decode_swa", "decode_global"]
@@ -553,6 +559,78 @@ def main_spec_decode(args, torch, gen, Bd):
              "config": {"workload": "spec_decode = multi-query decode, 64 sliding + 16 global sequences, "
                                     "n_q = 4 and n_q = 8"},
              "roofline": {"bound": "hbm", "kernel": "decode_partial_kernel (global, 8 draft tokens)",
+                          "achieved": g["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": g["frac_hbm_peak"],
+                          "traffic": None},
+             "cpu_baseline": None, "phases": phases}
+    print(json.dumps(out_j))
+
+
+def main_paged_decode(args, torch, gen, Bd):
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+    cases = {}
+    for name, S, hkv, window, seed, kv in (("global_bf16", 16, 4, 0, 2003, "bf16"),
+                                           ("global_fp8", 16, 4, 0, 2003, "fp8"),
+                                           ("swa_fp8", 64, 8, 128, 1003, "fp8")):
+        rng = np.random.Generator(np.random.PCG64(seed))
+        if window:
+            pos = rng.integers(128, 131072, size=S)
+        else:
+            pos = rng.integers(32768, 131072, size=S, endpoint=True) - 1
+        log(f"setup: paged decode {name} S={S}")
+        d = gen.paged_decode_inputs(S, 1, 128, 64, hkv, seed=seed, window=window, pos=pos, with_sinks=window > 0,
+                                    kv_dtype=kv, k_scale=0.02, v_scale=0.03)
+        cfg = Bd.swa_cfg() if window else Bd.global_cfg()
+        seen = np.minimum(pos + 1, window) if window else pos + 1
+        elem = 1 if kv == "fp8" else 2
+        pool = (lambda a: dev(a)) if kv == "fp8" else (lambda a: _dev_bf16(torch, a))
+        cases[name] = dict(
+            cfg=cfg, q=_dev_bf16(torch, d["q"]), pos=dev(d["pos"]), kp=pool(d["k_pool"]), vp=pool(d["v_pool"]),
+            table=dev(d["table"]), sinks=None if d["sinks"] is None else dev(d["sinks"]),
+            out=torch.empty((S, 1, 64, 128), dtype=torch.bfloat16, device="cuda"),
+            ws=torch.empty(Bd.mimo_attn_decode_multi_workspace_size(cfg, S, 1, 0), dtype=torch.uint8, device="cuda"),
+            bytes=int(seen.sum()) * hkv * 320 * elem + S * 64 * (192 + 128) * 2,
+            bf16_bytes=int(seen.sum()) * hkv * 320 * 2 + S * 64 * (192 + 128) * 2)
+        del d
+    names = list(cases)
+
+    def step(ev=None):
+        for n in names:
+            c = cases[n]
+            if ev is not None:
+                ev[n][0].record()
+            Bd.mimo_attn_decode_paged(c["cfg"], c["q"], c["pos"], c["kp"], c["vp"], c["table"], c["sinks"], c["out"],
+                                      ws=c["ws"], k_scale=0.02, v_scale=0.03)
+            if ev is not None:
+                ev[n][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    ms = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in evs])) for n in names}
+    phases = {}
+    for n, c in cases.items():
+        t = ms[n] * 1e-3
+        phases[n] = {"ms": ms[n], "gbs": c["bytes"] / t / 1e9, "frac_hbm_peak": c["bytes"] / t / 1e9 / PEAK_HBM_GBS,
+                     "bf16_equivalent_gbs": c["bf16_bytes"] / t / 1e9}
+    value = sum(c["bytes"] for c in cases.values()) / (ms_step * 1e-3) / 1e9
+    g = phases["global_fp8"]
+    out_j = {"metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+             "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+             "vs_baseline": None, "dtype": "bf16 compute; bf16 and fp8 e4m3 KV",
+             "data": "synthetic: seeded N(0,1) bf16 q, N(0,1) KV as bf16 or e4m3 codes of x / scale",
+             "config": {"workload": "paged_decode = 16 global sequences (bf16 and fp8 pools) + 64 sliding "
+                                    "sequences (fp8 pools), 128-slot blocks"},
+             "roofline": {"bound": "hbm", "kernel": "decode_partial_kernel (paged fp8, global)",
                           "achieved": g["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": g["frac_hbm_peak"],
                           "traffic": None},
              "cpu_baseline": None, "phases": phases}

@@ -67,13 +67,17 @@ def load_library(path: str = LIB_PATH):
     lib.mimo_attn_decode_workspace_size.argtypes = [C, I32, I32]
     lib.mimo_attn_decode_workspace_size.restype = ctypes.c_size_t
     lib.mimo_attn_decode_multi.argtypes = [C, I32, I32, P, P, P, P, I32, P, P, P, ctypes.c_size_t, P]
+    F = ctypes.c_float
+    lib.mimo_attn_decode_paged.argtypes = [C, I32, I32, P, P, P, P, I32, I32, ctypes.c_int, F, F, P, I32, P, P, P,
+                                           ctypes.c_size_t, P]
+    lib.mimo_kv_paged_append.argtypes = [C, I32, P, P, P, P, P, I32, I32, ctypes.c_int, F, F, P, I32, P]
     lib.mimo_attn_decode_multi_workspace_size.argtypes = [C, I32, I32, I32]
     lib.mimo_attn_decode_multi_workspace_size.restype = ctypes.c_size_t
     lib.mimo_kv_ring_append.argtypes = [C, I32, P, P, P, P, P, I32, P]
     lib.mimo_last_error.restype = ctypes.c_char_p
     for fn in ("mimo_rope_partial", "mimo_attn_prefill_swa", "mimo_attn_prefill_global",
                "mimo_attn_prefill_varlen", "mimo_attn_decode", "mimo_attn_decode_multi",
-               "mimo_kv_ring_append"):
+               "mimo_attn_decode_paged", "mimo_kv_paged_append", "mimo_kv_ring_append"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -197,6 +201,53 @@ def mimo_attn_decode_multi(cfg: MimoAttnCfg, q, q_pos, k_cache, v_cache, sinks, 
            lib.mimo_attn_decode_multi(ctypes.byref(cfg), S, n_q, _p(q), _p(q_pos), _p(k_cache), _p(v_cache), cap,
                                       _p(sinks), _p(out), _p(ws), ws_bytes, _stream(stream)))
     return out
+
+
+KV_DTYPE = {"bf16": 0, "fp8": 1}
+
+
+def _pool(t, name):
+    if t is None or not t.is_cuda or not t.is_contiguous() or t.dim() != 4 or t.dtype not in (torch.bfloat16,
+                                                                                            torch.uint8):
+        raise ValueError(f"{name} must be a contiguous 4-d CUDA tensor of bfloat16 or uint8 (fp8 codes)")
+    return "fp8" if t.dtype == torch.uint8 else "bf16"
+
+
+def mimo_attn_decode_paged(cfg: MimoAttnCfg, q, q_pos, k_pool, v_pool, block_table, sinks, out, ws=None,
+                           k_scale: float = 1.0, v_scale: float = 1.0, stream=None):
+    """q [S,n_q,Hq,192], q_pos [S] int64 (newest token), pools [n_blocks,block_size,Hkv,192|128] of bf16 or
+    uint8 fp8 e4m3 codes, block_table [S,max_blocks] int32, out [S,n_q,Hq,128]."""
+    lib = load_library()
+    _need(q, torch.bfloat16, "q", 4); _need(out, torch.bfloat16, "out", 4)
+    _need(q_pos, torch.int64, "q_pos", 1); _need(sinks, torch.float32, "sinks", 1)
+    _need(block_table, torch.int32, "block_table", 2)
+    kd, vd = _pool(k_pool, "k_pool"), _pool(v_pool, "v_pool")
+    if kd != vd:
+        raise ValueError("k_pool and v_pool must have the same element type")
+    S, n_q = q.shape[:2]
+    n_blocks, block_size = k_pool.shape[:2]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("mimo_attn_decode_paged",
+           lib.mimo_attn_decode_paged(ctypes.byref(cfg), S, n_q, _p(q), _p(q_pos), _p(k_pool), _p(v_pool), n_blocks,
+                                      block_size, KV_DTYPE[kd], k_scale, v_scale, _p(block_table),
+                                      block_table.shape[1], _p(sinks), _p(out), _p(ws), ws_bytes, _stream(stream)))
+    return out
+
+
+def mimo_kv_paged_append(cfg: MimoAttnCfg, k_new, v_new, pos, k_pool, v_pool, block_table,
+                         k_scale: float = 1.0, v_scale: float = 1.0, stream=None):
+    """k_new [S,Hkv,192], v_new [S,Hkv,128] unrotated; writes position pos[s] of each sequence's pages."""
+    lib = load_library()
+    _need(k_new, torch.bfloat16, "k_new", 3); _need(v_new, torch.bfloat16, "v_new", 3)
+    _need(pos, torch.int64, "pos", 1); _need(block_table, torch.int32, "block_table", 2)
+    kd, vd = _pool(k_pool, "k_pool"), _pool(v_pool, "v_pool")
+    if kd != vd:
+        raise ValueError("k_pool and v_pool must have the same element type")
+    n_blocks, block_size = k_pool.shape[:2]
+    _check("mimo_kv_paged_append",
+           lib.mimo_kv_paged_append(ctypes.byref(cfg), k_new.shape[0], _p(k_new), _p(v_new), _p(pos), _p(k_pool),
+                                    _p(v_pool), n_blocks, block_size, KV_DTYPE[kd], k_scale, v_scale,
+                                    _p(block_table), block_table.shape[1], _stream(stream)))
 
 
 def mimo_kv_ring_append(cfg: MimoAttnCfg, k_new, v_new, pos, k_cache, v_cache, stream=None):

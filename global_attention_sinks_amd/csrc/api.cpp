@@ -178,10 +178,17 @@ mimo_status mimo_attn_prefill_varlen(const mimo_attn_cfg *cfg, const uint16_t *q
     return from_hip(launch_prefill(a, (hipStream_t)stream), "prefill_varlen launch");
 }
 
+// Paged layout of a decode call (table == NULL: per-sequence caches).
+struct PagedLayout {
+    const int32_t *table = nullptr;
+    int32_t max_blocks = 0, block_shift = 0, n_blocks = 0, fp8 = 0;
+    float k_scale = 1.0f, v_scale = 1.0f;
+};
+
 static mimo_status decode_common(const mimo_attn_cfg *cfg, int32_t S, int32_t n_q, const uint16_t *q,
-                                 const int64_t *q_pos, const uint16_t *k_cache, const uint16_t *v_cache,
+                                 const int64_t *q_pos, const void *k_cache, const void *v_cache,
                                  int32_t cap, const float *sinks, uint16_t *out, void *ws, size_t ws_bytes,
-                                 void *stream) {
+                                 void *stream, const PagedLayout &pl = PagedLayout()) {
     mimo_status st = check_cfg(cfg);
     if (st != MIMO_OK) return st;
     if (S < 0 || cap < 1) return fail(MIMO_ERR_INVALID_ARGUMENT, "S must be >= 0 and cap >= 1");
@@ -190,7 +197,7 @@ static mimo_status decode_common(const mimo_attn_cfg *cfg, int32_t S, int32_t n_
     if (G > 16) return fail(MIMO_ERR_UNSUPPORTED, "decode needs a GQA group size <= 16 (got %d)", G);
     if (G * n_q > 128)
         return fail(MIMO_ERR_UNSUPPORTED, "decode needs group size x n_q <= 128 (got %d x %d)", G, n_q);
-    if (cfg->window > 0 && (int64_t)cap < (int64_t)cfg->window + n_q - 1)
+    if (!pl.table && cfg->window > 0 && (int64_t)cap < (int64_t)cfg->window + n_q - 1)
         return fail(MIMO_ERR_INVALID_ARGUMENT, "a ring cache needs cap (%d) >= window + n_q - 1 (%d)", cap,
                     cfg->window + n_q - 1);
     if (cfg->num_kv_heads > 8)
@@ -199,7 +206,7 @@ static mimo_status decode_common(const mimo_attn_cfg *cfg, int32_t S, int32_t n_
     if (cap > kDecodeMaxCap) return fail(MIMO_ERR_UNSUPPORTED, "decode needs cap <= %d", kDecodeMaxCap);
     if (S == 0) return ok();
     if (!q || !q_pos || !k_cache || !v_cache || !out)
-        return fail(MIMO_ERR_INVALID_ARGUMENT, "q, q_pos, k_cache, v_cache and out must be non-NULL");
+        return fail(MIMO_ERR_INVALID_ARGUMENT, "q, q_pos, the caches and out must be non-NULL");
     const size_t need = decode_workspace_bytes(S, cfg->num_q_heads, cfg->num_kv_heads, n_q);
     if (!ws || ws_bytes < need)
         return fail(MIMO_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu)", need,
@@ -210,6 +217,12 @@ static mimo_status decode_common(const mimo_attn_cfg *cfg, int32_t S, int32_t n_
     a.S = S; a.Hq = cfg->num_q_heads; a.Hkv = cfg->num_kv_heads; a.cap = cap; a.window = cfg->window;
     a.n_q = n_q;
     a.scale_log2 = scale_log2(cfg); a.v_scale = cfg->v_scale;
+    a.table = pl.table; a.max_blocks = pl.max_blocks; a.block_shift = pl.block_shift; a.n_blocks = pl.n_blocks;
+    a.fp8 = pl.fp8;
+    if (pl.fp8) {   // scores and outputs of the codes, scaled back
+        a.scale_log2 *= pl.k_scale;
+        a.v_scale *= pl.v_scale;
+    }
     a.rt = rope_turns(cfg->rope_base);
     return from_hip(launch_decode(a, (hipStream_t)stream), "decode launch");
 }
@@ -245,6 +258,72 @@ mimo_status mimo_attn_decode_multi(const mimo_attn_cfg *cfg, int32_t S, int32_t 
                                    int32_t cap, const float *sinks, uint16_t *out, void *ws,
                                    size_t ws_bytes, void *stream) {
     return decode_common(cfg, S, n_q, q, q_pos, k_cache, v_cache, cap, sinks, out, ws, ws_bytes, stream);
+}
+
+// Checks of a paged layout shared by decode and append.
+static mimo_status check_paged(int32_t n_blocks, int32_t block_size, mimo_kv_dtype kv_dtype, float k_scale,
+                               float v_scale, int32_t max_blocks, PagedLayout &pl) {
+    if (kv_dtype != MIMO_KV_BF16 && kv_dtype != MIMO_KV_FP8_E4M3)
+        return fail(MIMO_ERR_INVALID_ARGUMENT, "kv_dtype must be MIMO_KV_BF16 or MIMO_KV_FP8_E4M3");
+    if (block_size < 32 || (block_size & (block_size - 1)) != 0 || block_size > (1 << 16))
+        return fail(MIMO_ERR_UNSUPPORTED, "block_size must be a power of two in [32, 65536] (got %d)", block_size);
+    if (n_blocks < 1 || max_blocks < 1)
+        return fail(MIMO_ERR_INVALID_ARGUMENT, "n_blocks and max_blocks must be >= 1");
+    if ((int64_t)max_blocks * block_size > (1 << 30))
+        return fail(MIMO_ERR_UNSUPPORTED, "max_blocks * block_size must be <= 2^30");
+    if (kv_dtype == MIMO_KV_FP8_E4M3 &&
+        (!(k_scale > 0.0f) || !(v_scale > 0.0f) || !isfinite(k_scale) || !isfinite(v_scale)))
+        return fail(MIMO_ERR_INVALID_ARGUMENT, "fp8 scales must be finite and > 0");
+    int shift = 0;
+    while ((1 << shift) < block_size) ++shift;
+    pl.max_blocks = max_blocks;
+    pl.block_shift = shift;
+    pl.n_blocks = n_blocks;
+    pl.fp8 = kv_dtype == MIMO_KV_FP8_E4M3;
+    pl.k_scale = pl.fp8 ? k_scale : 1.0f;
+    pl.v_scale = pl.fp8 ? v_scale : 1.0f;
+    return ok();
+}
+
+mimo_status mimo_attn_decode_paged(const mimo_attn_cfg *cfg, int32_t S, int32_t n_q, const uint16_t *q,
+                                   const int64_t *q_pos, const void *k_pool, const void *v_pool,
+                                   int32_t n_blocks, int32_t block_size, mimo_kv_dtype kv_dtype,
+                                   float k_scale, float v_scale, const int32_t *block_table,
+                                   int32_t max_blocks, const float *sinks, uint16_t *out, void *ws,
+                                   size_t ws_bytes, void *stream) {
+    mimo_status st = check_cfg(cfg);
+    if (st != MIMO_OK) return st;
+    PagedLayout pl;
+    st = check_paged(n_blocks, block_size, kv_dtype, k_scale, v_scale, max_blocks, pl);
+    if (st != MIMO_OK) return st;
+    if (S > 0 && !block_table) return fail(MIMO_ERR_INVALID_ARGUMENT, "block_table must be non-NULL");
+    pl.table = block_table;
+    return decode_common(cfg, S, n_q, q, q_pos, k_pool, v_pool, max_blocks * block_size, sinks, out, ws,
+                         ws_bytes, stream, pl);
+}
+
+mimo_status mimo_kv_paged_append(const mimo_attn_cfg *cfg, int32_t S, const uint16_t *k_new,
+                                 const uint16_t *v_new, const int64_t *pos, void *k_pool, void *v_pool,
+                                 int32_t n_blocks, int32_t block_size, mimo_kv_dtype kv_dtype,
+                                 float k_scale, float v_scale, const int32_t *block_table,
+                                 int32_t max_blocks, void *stream) {
+    mimo_status st = check_cfg(cfg);
+    if (st != MIMO_OK) return st;
+    PagedLayout pl;
+    st = check_paged(n_blocks, block_size, kv_dtype, k_scale, v_scale, max_blocks, pl);
+    if (st != MIMO_OK) return st;
+    if (S < 0) return fail(MIMO_ERR_INVALID_ARGUMENT, "S must be >= 0");
+    if ((int64_t)S * cfg->num_kv_heads > 0x7fffffff)
+        return fail(MIMO_ERR_UNSUPPORTED, "S * num_kv_heads is too large");
+    if (S == 0) return ok();
+    if (!k_new || !v_new || !pos || !k_pool || !v_pool || !block_table)
+        return fail(MIMO_ERR_INVALID_ARGUMENT, "k_new, v_new, pos, the pools and block_table must be non-NULL");
+    PagedAppendArgs a{};
+    a.k_new = k_new; a.v_new = v_new; a.pos = pos; a.k_pool = k_pool; a.v_pool = v_pool; a.table = block_table;
+    a.S = S; a.Hkv = cfg->num_kv_heads; a.n_blocks = n_blocks; a.block_shift = pl.block_shift;
+    a.max_blocks = max_blocks; a.fp8 = pl.fp8; a.k_scale = pl.k_scale; a.v_scale = pl.v_scale;
+    return from_hip(launch_kv_paged_append(rope_turns(cfg->rope_base), a, (hipStream_t)stream),
+                    "kv_paged_append launch");
 }
 
 mimo_status mimo_kv_ring_append(const mimo_attn_cfg *cfg, int32_t S, const uint16_t *k_new,

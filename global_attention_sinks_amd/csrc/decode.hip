@@ -41,14 +41,45 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
-// Number of cache slots a query at position p can see (slots >= this hold nothing).
-__device__ __forceinline__ int live_slots(int64_t p, int32_t cap) {
-    if (p < 0) return 0;
-    return p + 1 < cap ? (int)(p + 1) : cap;
+// The logical key slots [lo, hi) a sequence whose newest query sits at p reads.
+// Per-sequence caches: slot = position mod cap, slots 0 .. min(p+1, cap) - 1.
+// Paged caches: slot = position; with a window only the 32-aligned range from
+// the oldest query's window start on (earlier blocks may be released).
+__device__ __forceinline__ void key_range(const DecodeArgs &a, int64_t p, int &lo, int &hi) {
+    lo = 0;
+    hi = 0;
+    if (p < 0) return;
+    if (a.table) {
+        const int64_t end = (int64_t)a.max_blocks << a.block_shift;
+        hi = (int)(p + 1 < end ? p + 1 : end);
+        if (a.window > 0) {
+            const int64_t first = p - (a.n_q - 1) - a.window + 1;
+            lo = first > 0 ? (int)(first & ~(int64_t)(kStep - 1)) : 0;
+        }
+    } else {
+        hi = p + 1 < a.cap ? (int)(p + 1) : a.cap;
+    }
 }
 
-__device__ __forceinline__ int64_t steps_of(int64_t p, int32_t cap) {
-    return (live_slots(p, cap) + kStep - 1) / kStep;
+__device__ __forceinline__ int64_t steps_of(const DecodeArgs &a, int64_t p) {
+    int lo, hi;
+    key_range(a, p, lo, hi);
+    return (hi - lo + kStep - 1) / kStep;
+}
+
+// 8 fp8 e4m3 codes (two dwords, code e in byte e) -> 8 bf16 (exact: every e4m3
+// value is a bf16 value)
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+    u32x4 r;
+    const auto a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
+    const auto a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+    const auto b0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
+    const auto b1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+    r[0] = pack_bf16(a0[0], a0[1]);
+    r[1] = pack_bf16(a1[0], a1[1]);
+    r[2] = pack_bf16(b0[0], b0[1]);
+    r[3] = pack_bf16(b1[0], b1[1]);
+    return r;
 }
 
 // Workgroups used for Ts steps: at most n_groups, each with >= kDecodeMinSteps
@@ -87,9 +118,17 @@ __device__ T block_scan(T v, T *wsum, T &total) {
     return v + before;
 }
 
-struct StepBuf {
-    u32x4 k[2][6];   // [16-key sub-block][chunk]: dims 32*ch + 8*lg .. +8 of one key row
-    u32x4 v[8];      // 8 key rows x 8 dv
+// One step's K/V registers of a lane.  bf16: k[sb][ch] holds dims 32*ch + 8*lg
+// .. +8 of key row 16*sb + r16; v[jj] 8 dv of a key row.  fp8: k[sb][c] holds
+// 16 codes, dims 16*(lg + 4*c) .. +16 (two MFMA chunks); v[jj] 8 codes.
+template <bool FP8> struct StepBuf;
+template <> struct StepBuf<false> {
+    u32x4 k[2][6];
+    u32x4 v[8];
+};
+template <> struct StepBuf<true> {
+    u32x4 k[2][3];
+    u32x2 v[8];
 };
 
 }  // namespace
@@ -104,7 +143,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
     const int per = (a.S + kPlanThreads - 1) / kPlanThreads;
     const int s0 = min(a.S, t * per), s1 = min(a.S, s0 + per);
     int64_t mine = 0;
-    for (int s = s0; s < s1; ++s) mine += steps_of(a.pos[s], a.cap);
+    for (int s = s0; s < s1; ++s) mine += steps_of(a, a.pos[s]);
     int64_t Ts;
     const int64_t incl = block_scan<int64_t>(mine, wsum64, Ts);
     run_end[t] = incl;
@@ -112,7 +151,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
     int64_t start = incl - mine;
     int32_t parts = 0;
     for (int s = s0; s < s1; ++s) {
-        const int64_t steps = steps_of(a.pos[s], a.cap);
+        const int64_t steps = steps_of(a, a.pos[s]);
         int32_t first = 0, cover = 0;
         if (steps > 0) {
             first = (int32_t)step_owner(start, Ts, ng);
@@ -160,7 +199,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
 // of the same KV head.  MAXT: workgroup size bound (512: eight KV-head waves,
 // two per SIMD; 256: up to four waves, one per SIMD with the whole register
 // file, for the tiles of multi-query decode).
-template <int NC, int MAXT>
+template <int NC, int MAXT, bool FP8, bool PAGED>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, MAXT), amdgpu_waves_per_eu(MAXT / 256, MAXT / 256)))
 void decode_partial_kernel(DecodeArgs a) {
     const int64_t wg = blockIdx.x;
@@ -187,9 +226,18 @@ void decode_partial_kernel(DecodeArgs a) {
         ok[t] = tok[t] < nq;
     }
     const float cl2 = a.scale_log2;
+    // row strides of the caches in elements (bf16) or bytes (fp8): one element each
     const size_t krs = (size_t)a.Hkv * kDqk, vrs = (size_t)a.Hkv * kDv;
     const int win = a.window > 0 ? a.window : 0x7fffffff;
     const bool always_mask = a.window > 0 || nq > 1;
+    constexpr bool paged = PAGED;
+    const int bmask = (1 << a.block_shift) - 1;
+    using Buf = StepBuf<FP8>;
+    // per-lane bases: K dims of the contraction slots, V dv chunk of the lane
+    const uint16_t *k16 = static_cast<const uint16_t *>(a.k_cache) + (size_t)g * kDqk + 8 * lg;
+    const uint16_t *v16 = static_cast<const uint16_t *>(a.v_cache) + (size_t)g * kDv + 8 * r16;
+    const uint8_t *k8 = static_cast<const uint8_t *>(a.k_cache) + (size_t)g * kDqk + 16 * lg;
+    const uint8_t *v8 = static_cast<const uint8_t *>(a.v_cache) + (size_t)g * kDv + 8 * r16;
 
     for (int s = lo; s < a.S; ++s) {
         const int64_t st0 = a.plan_start[s];
@@ -200,41 +248,73 @@ void decode_partial_kernel(DecodeArgs a) {
         if (seg_lo >= seg_hi) continue;
 
         const int64_t p = a.pos[s];   // newest query's position (>= 0: the sequence has steps)
-        const int n = live_slots(p, a.cap);
+        int jlo, n;
+        key_range(a, p, jlo, n);      // logical slots [jlo, n)
 
         u32x4 qf[NC][6];
         float m_run[NC], l_run[NC];
         f32x4 O[NC][8];
 
-        const uint16_t *kbase = a.k_cache + (size_t)s * a.cap * krs + (size_t)g * kDqk + 8 * lg;
-        const uint16_t *vbase = a.v_cache + (size_t)s * a.cap * vrs + (size_t)g * kDv + 8 * r16;
-        const int kbeg = (int)(seg_lo - st0) * kStep;
-        const int kseg = (int)(seg_hi - st0) * kStep;
+        const int kbeg = jlo + (int)(seg_lo - st0) * kStep;
+        const int kseg = jlo + (int)(seg_hi - st0) * kStep;
         const int kend = kseg < n ? kseg : n;
         // ring rule: slot j holds position p - ((p - j) mod cap); with pm = p mod cap
-        // that distance is pm - j, or pm - j + cap when j > pm
-        const int pm = (int)(p % a.cap);
+        // that distance is pm - j, or pm - j + cap when j > pm.  Paged: slot j is position j.
+        const int pm = paged ? 0 : (int)(p % a.cap);
+        const size_t seq_rows = paged ? 0 : (size_t)s * a.cap;
+        const int32_t *btab = paged ? a.table + (size_t)s * a.max_blocks : nullptr;
 
-        // rows past the cache end (last step of a full cache) re-read the last
-        // row; every key at or past n is masked out of the step anyway
-        auto load = [&](StepBuf &bf, int j0) {
+        // physical cache row of slot j: per-sequence caches re-read their last row
+        // for slots past the end (last step of a full cache); a paged step lies in
+        // one block.  Every slot at or past n is masked out of the step anyway.
+        auto load = [&](Buf &bf, int j0) {
+            size_t blk_row = 0;
+            if constexpr (PAGED) {
+                int blk = btab[j0 >> a.block_shift];
+                blk = blk < 0 ? 0 : (blk >= a.n_blocks ? a.n_blocks - 1 : blk);
+                blk_row = (size_t)blk << a.block_shift;
+            }
+            auto row = [&](int j) -> size_t {
+                return paged ? blk_row + (size_t)(j & bmask) : seq_rows + (size_t)min(j, a.cap - 1);
+            };
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb) {
-                const int j = min(j0 + 16 * sb + r16, a.cap - 1);
+                const size_t r = row(j0 + 16 * sb + r16);
+                if constexpr (FP8) {
 #pragma unroll
-                for (int ch = 0; ch < 6; ++ch) bf.k[sb][ch] = ldg128(kbase + (size_t)j * krs + 32 * ch);
+                    for (int c = 0; c < 3; ++c) bf.k[sb][c] = *reinterpret_cast<const u32x4 *>(k8 + r * krs + 64 * c);
+                } else {
+#pragma unroll
+                    for (int ch = 0; ch < 6; ++ch) bf.k[sb][ch] = ldg128(k16 + r * krs + 32 * ch);
+                }
             }
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
-                const int j = min(j0 + 16 * (jj >> 2) + 4 * lg + (jj & 3), a.cap - 1);
-                bf.v[jj] = ldg128(vbase + (size_t)j * vrs);
+                const size_t r = row(j0 + 16 * (jj >> 2) + 4 * lg + (jj & 3));
+                if constexpr (FP8) bf.v[jj] = *reinterpret_cast<const u32x2 *>(v8 + r * vrs);
+                else bf.v[jj] = ldg128(v16 + r * vrs);
             }
         };
 
-        auto compute = [&](StepBuf &bf, int j0) {
+        auto compute = [&](Buf &bf, int j0) {
             // the lane's 8 keys are j0 + 16*sb + 4*lg + i (rows of its S^T registers and
             // of its V loads); d = how many positions each lies before the newest query
             const bool masked = always_mask || j0 + kStep > kend;
+            // K operands in bf16 (fp8 codes widened once per step)
+            u32x4 kop8[2][FP8 ? 6 : 1];
+            if constexpr (FP8) {
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                    for (int ch = 0; ch < 6; ++ch) {
+                        const u32x4 wv = bf.k[sb][ch >> 1];
+                        kop8[sb][ch] = (ch & 1) ? fp8x8_to_bf16(wv[2], wv[3]) : fp8x8_to_bf16(wv[0], wv[1]);
+                    }
+            }
+            auto kop = [&](int sb, int ch) -> u32x4 {
+                if constexpr (FP8) return kop8[sb][ch];
+                else return bf.k[sb][ch];
+            };
             u32x4 pf[NC];
 #pragma unroll
             for (int t = 0; t < NC; ++t) {
@@ -243,20 +323,28 @@ void decode_partial_kernel(DecodeArgs a) {
                 for (int sb = 0; sb < 2; ++sb) {
                     S[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ch = 0; ch < 6; ++ch) S[sb] = mfma16(bf.k[sb][ch], qf[t][ch], S[sb]);
+                    for (int ch = 0; ch < 6; ++ch) S[sb] = mfma16(kop(sb, ch), qf[t][ch], S[sb]);
                 }
                 if (masked) {
                     const int delta = nq - 1 - tok[t];   // the column's query lies delta before the newest
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const int j = j0 + 16 * (e >> 2) + 4 * lg + (e & 3);
-                        int d = pm - j;
-                        if (d < 0) d += a.cap;
+                        int d;
+                        if constexpr (PAGED) {
+                            d = (int)(p - j);
+                        } else {
+                            d = pm - j;
+                            if (d < 0) d += a.cap;
+                        }
                         const bool live = j < n && (int64_t)d <= p;
                         const int dd = d - delta;
                         if (!(live && dd >= 0 && dd < win)) S[e >> 2][e & 3] = kNegInf;
                         // no query of the sequence sees it: drop its value row (it may hold NaN)
-                        if (t == 0 && !(live && d - (nq - 1) < win)) bf.v[e] = u32x4{0, 0, 0, 0};
+                        if (t == 0 && !(live && d - (nq - 1) < win)) {
+                            if constexpr (FP8) bf.v[e] = u32x2{0, 0};
+                            else bf.v[e] = u32x4{0, 0, 0, 0};
+                        }
                     }
                 }
                 float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
@@ -288,6 +376,15 @@ void decode_partial_kernel(DecodeArgs a) {
                 pf[t][2] = pack_bf16(S[1][0], S[1][1]);
                 pf[t][3] = pack_bf16(S[1][2], S[1][3]);
             }
+            u32x4 vr8[FP8 ? 8 : 1];
+            if constexpr (FP8) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vr8[e] = fp8x8_to_bf16(bf.v[e][0], bf.v[e][1]);
+            }
+            auto vr = [&](int e) -> u32x4 {
+                if constexpr (FP8) return vr8[e];
+                else return bf.v[e];
+            };
             // O^T tile tt covers dv = 8*r + tt (r = 0..15): lane's V chunk is dv 8*r16..8*r16+7
 #pragma unroll
             for (int tt = 0; tt < 8; ++tt) {
@@ -295,25 +392,44 @@ void decode_partial_kernel(DecodeArgs a) {
                 u32x4 vt;
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    vt[u] = __builtin_amdgcn_perm(bf.v[2 * u + 1][tt >> 1], bf.v[2 * u][tt >> 1], sel);
+                    vt[u] = __builtin_amdgcn_perm(vr(2 * u + 1)[tt >> 1], vr(2 * u)[tt >> 1], sel);
 #pragma unroll
                 for (int t = 0; t < NC; ++t) O[t][tt] = mfma16(vt, pf[t], O[t][tt]);
             }
         };
 
         {
-            StepBuf A, B;
+            Buf A, B;
             int j0 = kbeg;
             if (j0 < kend) load(A, j0);   // first step's loads go out before q's
-            // ---- q (B operand) of each tile: contraction slot (ch, lg, e) is dim
-            // 32*ch + 8*lg + e; chunks 0 and 1 of a lane are rotate-half partners
+            // ---- q (B operand) of each tile, in the contraction order of the K operand:
+            // bf16: slot (ch, lg, e) is dim 32*ch + 8*lg + e, so chunks 0 and 1 of a lane
+            // are rotate-half partners (dims i and i+32); fp8: slot (ch = 2c+h, lg, e) is
+            // dim 16*(lg + 4*c) + 8*h + e, and the partner of chunk h of c = 0 sits two
+            // lanes over, so it is read from memory as well
 #pragma unroll
             for (int t = 0; t < NC; ++t) {
                 if (ok[t]) {
-                    const uint16_t *qrow = a.q + (((size_t)s * nq + tok[t]) * a.Hq + hd[t]) * kDqk + 8 * lg;
+                    const int64_t qp = p - (nq - 1 - tok[t]);
+                    const uint16_t *qrow = a.q + (((size_t)s * nq + tok[t]) * a.Hq + hd[t]) * kDqk;
+                    if constexpr (FP8) {
 #pragma unroll
-                    for (int ch = 0; ch < 6; ++ch) qf[t][ch] = ldg128(qrow + 32 * ch);
-                    rope_rotate8(qf[t][0], qf[t][1], a.rt, 8 * lg, p - (nq - 1 - tok[t]));
+                        for (int c = 0; c < 3; ++c)
+#pragma unroll
+                            for (int h = 0; h < 2; ++h) qf[t][2 * c + h] = ldg128(qrow + 16 * (lg + 4 * c) + 8 * h);
+                        const int pl = lg < 2 ? lg + 2 : lg - 2;
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const u32x4 own = qf[t][h], partner = ldg128(qrow + 16 * pl + 8 * h);
+                            u32x4 x = lg < 2 ? own : partner, y = lg < 2 ? partner : own;
+                            rope_rotate8(x, y, a.rt, 16 * (lg & 1) + 8 * h, qp);
+                            qf[t][h] = lg < 2 ? x : y;
+                        }
+                    } else {
+#pragma unroll
+                        for (int ch = 0; ch < 6; ++ch) qf[t][ch] = ldg128(qrow + 8 * lg + 32 * ch);
+                        rope_rotate8(qf[t][0], qf[t][1], a.rt, 8 * lg, qp);
+                    }
                 } else {
 #pragma unroll
                     for (int ch = 0; ch < 6; ++ch) qf[t][ch] = u32x4{0, 0, 0, 0};
@@ -453,7 +569,13 @@ size_t decode_partial_slots(int32_t S, const DecodeGeom &m) { return (size_t)m.n
 
 template <int NC, int MAXT>
 void launch_partial(const DecodeArgs &a, const DecodeGeom &m, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_partial_kernel<NC, MAXT>), dim3(m.n_groups, m.n_hsub), dim3(m.threads), 0, stream, a);
+    const dim3 grid(m.n_groups, m.n_hsub), block(m.threads);
+    if (!a.table)
+        hipLaunchKernelGGL((decode_partial_kernel<NC, MAXT, false, false>), grid, block, 0, stream, a);
+    else if (a.fp8)
+        hipLaunchKernelGGL((decode_partial_kernel<NC, MAXT, true, true>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((decode_partial_kernel<NC, MAXT, false, true>), grid, block, 0, stream, a);
 }
 
 }  // namespace

@@ -15,6 +15,16 @@ hipError_t launch_rope_partial(const RopeTurns &rt, const uint16_t *x_in, uint16
 hipError_t launch_kv_ring_append(const RopeTurns &rt, int32_t S, int32_t Hkv, const uint16_t *k_new,
                                  const uint16_t *v_new, const int64_t *pos, uint16_t *k_cache,
                                  uint16_t *v_cache, int32_t cap, hipStream_t stream);
+// Paged pools [n_blocks, 1 << block_shift, Hkv, D] of bf16 (fp8 == 0) or fp8 e4m3 codes.
+struct PagedAppendArgs {
+    const uint16_t *k_new, *v_new;
+    const int64_t *pos;
+    void *k_pool, *v_pool;
+    const int32_t *table;
+    int32_t S, Hkv, n_blocks, block_shift, max_blocks, fp8;
+    float k_scale, v_scale;
+};
+hipError_t launch_kv_paged_append(const RopeTurns &rt, const PagedAppendArgs &a, hipStream_t stream);
 
 // ---- prefill (prefill.hip)
 struct PrefillArgs {
@@ -54,7 +64,8 @@ constexpr int kDecodeWaves = MIMO_DECODE_WAVES;
 constexpr int kDecodeMinSteps = MIMO_DECODE_MIN_STEPS;
 constexpr int kDecodeMaxCap = 1 << 30;
 struct DecodeArgs {
-    const uint16_t *q, *k_cache, *v_cache;
+    const uint16_t *q;
+    const void *k_cache, *v_cache;   // per-sequence caches [S, cap, Hkv, D], or paged pools
     const int64_t *pos;   // newest query's position per sequence
     const float *sinks;   // nullable
     uint16_t *out;
@@ -66,6 +77,11 @@ struct DecodeArgs {
     int32_t *plan_part;   // [S] first partial slot of the sequence
     int32_t *plan_wg_seq; // [n_groups] sequence holding each workgroup's first step
     int32_t S, Hq, Hkv, cap, window, n_q;
+    // paged caches (table == NULL: per-sequence caches of cap slots): position t of
+    // sequence s is in pool block table[s * max_blocks + (t >> block_shift)]
+    const int32_t *table;
+    int32_t max_blocks, block_shift, n_blocks;
+    int32_t fp8;                   // pools hold fp8 e4m3 codes (scales folded into scale_log2, v_scale)
     int32_t n_groups, wph, kvpw;   // filled by the launcher
     float scale_log2, v_scale;
     RopeTurns rt;

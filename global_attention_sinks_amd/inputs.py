@@ -193,6 +193,74 @@ def decode_multi_inputs(S: int, n_q: int, cap: int, n_q_heads: int, n_kv_heads: 
             "sinks": normal_f32(cs, (n_q_heads,)) if with_sinks else None}
 
 
+FP8_NAN = np.uint8(0x7F)
+
+
+def f32_to_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """Round float32 draws to OCP fp8 e4m3 codes (round to nearest even, via
+    torch's float8_e4m3fn cast), after clipping them to the format's +-448."""
+    import torch
+    t = torch.from_numpy(np.clip(np.ascontiguousarray(x, dtype=np.float32), -448.0, 448.0))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def paged_decode_inputs(S: int, n_q: int, block_size: int, n_q_heads: int, n_kv_heads: int, seed: int,
+                        window: int, pos: np.ndarray, with_sinks: bool, kv_dtype: str = "bf16",
+                        k_scale: float = 1.0, v_scale: float = 1.0, spare_blocks: int = 3) -> dict:
+    """n_q query tokens per sequence (newest at pos[s]) over a paged cache.
+
+    Sequence s holds positions 0..pos[s] in blocks of block_size slots; with a
+    window only the blocks that hold some token's window get a pool block (the
+    table entry of the others is -1).  Pool blocks are handed out in a seeded
+    random order, plus spare_blocks unused ones.  Slots of the positions some
+    token can see hold draws: bf16 N(0,1), or fp8 e4m3 codes of N(0,1) / scale;
+    every other slot holds NaN (bf16 0x7FC0, fp8 0x7F)."""
+    cq, ck, cv, cs, cp = _children(seed)
+    pos = np.asarray(pos, dtype=np.int64)
+    fp8 = kv_dtype == "fp8"
+    q = normal_bf16(cq, (S, n_q, n_q_heads, D_QK))
+    max_blocks = int(max(1, max((int(p) + block_size) // block_size for p in pos))) + 1
+    table = np.full((S, max_blocks), -1, dtype=np.int32)
+    need = []
+    for s in range(S):
+        p = int(pos[s])
+        if p < 0:
+            continue
+        lo = max(0, p - (n_q - 1) - window + 1) if window > 0 else 0
+        for b in range(lo // block_size, p // block_size + 1):
+            need.append((s, b))
+    n_blocks = len(need) + spare_blocks
+    perm = np.random.Generator(np.random.PCG64(cp)).permutation(n_blocks)
+    for i, (s, b) in enumerate(need):
+        table[s, b] = perm[i]
+    nan = FP8_NAN if fp8 else BF16_NAN
+    dt = np.uint8 if fp8 else np.uint16
+    kp = np.full((n_blocks, block_size, n_kv_heads, D_QK), nan, dtype=dt)
+    vp = np.full((n_blocks, block_size, n_kv_heads, D_V), nan, dtype=dt)
+    kseeds, vseeds = ck.spawn(S), cv.spawn(S)
+    for s in range(S):
+        p = int(pos[s])
+        if p < 0:
+            continue
+        lo = max(0, p - (n_q - 1) - window + 1) if window > 0 else 0
+        tpos = np.arange(lo, p + 1)
+        blk = table[s, tpos // block_size]
+        slot = tpos % block_size
+        if fp8:
+            kd = np.random.Generator(np.random.PCG64(kseeds[s])).standard_normal(
+                (len(tpos), n_kv_heads, D_QK), dtype=np.float32)
+            vd = np.random.Generator(np.random.PCG64(vseeds[s])).standard_normal(
+                (len(tpos), n_kv_heads, D_V), dtype=np.float32)
+            kp[blk, slot] = f32_to_e4m3_codes(kd / np.float32(k_scale))
+            vp[blk, slot] = f32_to_e4m3_codes(vd / np.float32(v_scale))
+        else:
+            kp[blk, slot] = normal_bf16(kseeds[s], (len(tpos), n_kv_heads, D_QK))
+            vp[blk, slot] = normal_bf16(vseeds[s], (len(tpos), n_kv_heads, D_V))
+    return {"q": q, "pos": pos, "k_pool": kp, "v_pool": vp, "table": table, "block_size": block_size,
+            "kv_dtype": kv_dtype, "k_scale": float(k_scale), "v_scale": float(v_scale),
+            "sinks": normal_f32(cs, (n_q_heads,)) if with_sinks else None}
+
+
 def global_prefill_chunk(T: int, n_q_heads: int, n_kv_heads: int, seed: int, t_lo: int, t_hi: int) -> dict:
     """Query rows [t_lo, t_hi) of a B=1 prefill of T tokens and the keys/values
     0..t_hi-1, drawn exactly as prefill_inputs(1, T, ...) would draw them."""

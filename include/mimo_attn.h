@@ -198,6 +198,53 @@ mimo_status mimo_attn_decode_multi(const mimo_attn_cfg *cfg, int32_t S, int32_t 
  * unsupported cfg or n_q). */
 size_t mimo_attn_decode_multi_workspace_size(const mimo_attn_cfg *cfg, int32_t S, int32_t n_q, int32_t cap);
 
+/* Element type of a paged KV cache. */
+typedef enum mimo_kv_dtype {
+    MIMO_KV_BF16 = 0,      /* bf16 bit patterns */
+    MIMO_KV_FP8_E4M3 = 1   /* OCP fp8 e4m3 (e4m3fn) codes; value = code * scale */
+} mimo_kv_dtype;
+
+/*
+ * Decode over a paged KV cache: the cache of every sequence is a list of
+ * blocks of block_size token slots taken from shared pools, and a block table
+ * maps a sequence's logical block to its pool block (vLLM recipe page,
+ * Launch command for AMD MI355X: --block-size 128 and --kv-cache-dtype fp8;
+ * Gaudi recipe page, Launch: --block-size 128).  Position t of sequence s
+ * lives in pool block block_table[s * max_blocks + t / block_size], slot
+ * t % block_size.  Queries as in mimo_attn_decode_multi (n_q >= 1 tokens, the
+ * newest at q_pos[s]); a sequence holds positions 0..q_pos[s], and with a
+ * window only the blocks that hold some query's window are read (blocks
+ * before them may have been released).
+ *   k_pool  : [n_blocks, block_size, num_kv_heads, 192] rotated keys;
+ *   v_pool  : [n_blocks, block_size, num_kv_heads, 128];  elements of kv_dtype.
+ *   k_scale, v_scale : dequantisation scales of fp8 pools (ignored for bf16).
+ *   block_table : [S, max_blocks] int32 device array; entries outside
+ *   [0, n_blocks) are clamped into it (never read outside the pools).
+ *   block_size : a multiple of 32;  q_pos[s] < max_blocks * block_size.
+ *   out : [S, n_q, num_q_heads, 128] bf16;  ws as for mimo_attn_decode_multi
+ *   (mimo_attn_decode_multi_workspace_size with the same S and n_q).
+ */
+mimo_status mimo_attn_decode_paged(const mimo_attn_cfg *cfg, int32_t S, int32_t n_q, const uint16_t *q,
+                                   const int64_t *q_pos, const void *k_pool, const void *v_pool,
+                                   int32_t n_blocks, int32_t block_size, mimo_kv_dtype kv_dtype,
+                                   float k_scale, float v_scale, const int32_t *block_table,
+                                   int32_t max_blocks, const float *sinks, uint16_t *out, void *ws,
+                                   size_t ws_bytes, void *stream);
+
+/*
+ * Append one new token per sequence to a paged cache: k_new is rotated at
+ * pos[s] (partial RoPE) and written with v_new into the slot of position
+ * pos[s] (layout as in mimo_attn_decode_paged).  fp8 pools store
+ * code = round-to-nearest-even(x / scale), saturated to +-448, where x is the
+ * fp32 rotated key (or the bf16 value); bf16 pools store the bf16-rounded
+ * rotation, as mimo_kv_ring_append does.  A negative position writes nothing.
+ */
+mimo_status mimo_kv_paged_append(const mimo_attn_cfg *cfg, int32_t S, const uint16_t *k_new,
+                                 const uint16_t *v_new, const int64_t *pos, void *k_pool, void *v_pool,
+                                 int32_t n_blocks, int32_t block_size, mimo_kv_dtype kv_dtype,
+                                 float k_scale, float v_scale, const int32_t *block_table,
+                                 int32_t max_blocks, void *stream);
+
 /*
  * Append one new token per sequence: rotate k_new at pos (partial RoPE) and
  * write it and v_new into slot pos mod cap (the window-sized KV of the Gaudi

@@ -233,6 +233,92 @@ def decode_multi(q, q_pos, k_cache, v_cache, *, sinks=None, window: int, base: f
     return outs
 
 
+# ---------------------------------------------------------------- fp8 e4m3 (OCP) and paged caches
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """OCP fp8 e4m3 (e4m3fn) codes to their values: sign bit 7, exponent bits 6..3
+    with bias 7, mantissa bits 2..0; exponent 0 is subnormal (m/8 * 2^-6); the
+    all-ones exponent with all-ones mantissa is NaN (no infinities)."""
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.power(2.0, e - 7.0))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return sign * val
+
+
+_E4M3_POS = None
+
+
+def e4m3_round(x) -> np.ndarray:
+    """Values to e4m3 codes: nearest representable value, ties to the even code
+    (the one with an even mantissa), magnitudes beyond 448 saturated to 448."""
+    global _E4M3_POS
+    if _E4M3_POS is None:
+        _E4M3_POS = e4m3_to_f64(np.arange(0x7F))          # codes 0..126: 0 .. 448, increasing
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    d_lo, d_hi = a - _E4M3_POS[lo], _E4M3_POS[hi] - a
+    pick = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(a == _E4M3_POS[hi], hi, pick)
+    return (pick | np.where(x < 0, 0x80, 0)).astype(np.uint8)
+
+
+def _bf16_bits_exact(x: np.ndarray) -> np.ndarray:
+    """fp64 values that bf16 represents exactly, as bf16 bit patterns."""
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    assert np.array_equal(f.astype(np.float64), np.asarray(x, np.float64), equal_nan=True)
+    u = f.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0)
+    return (u >> 16).astype(np.uint16)
+
+
+def decode_paged(q, q_pos, k_pool, v_pool, table, *, block_size: int, kv_dtype: str = "bf16",
+                 k_scale: float = 1.0, v_scale: float = 1.0, sinks=None, window: int, base: float,
+                 seqs=None, n_threads: int = 0):
+    """decode_multi over a paged cache: position t of sequence s sits in pool
+    block table[s, t // block_size], slot t % block_size.  fp8 pools hold e4m3
+    codes of value code * scale: the codes' values are exact in bf16, and the
+    scales multiply the scores (k) and the output (v)."""
+    S, nq, hq = q.shape[:3]
+    seqs = range(S) if seqs is None else seqs
+    outs = np.zeros((len(seqs), nq, hq, v_pool.shape[3]))
+    fp8 = kv_dtype == "fp8"
+    for r, s in enumerate(seqs):
+        for i in range(nq):
+            p = int(q_pos[s]) - (nq - 1 - i)
+            if p < 0:
+                continue
+            tpos = np.arange(max(0, p - window + 1) if window > 0 else 0, p + 1, dtype=np.int64)
+            blk = table[s, tpos // block_size]
+            assert np.all(blk >= 0)
+            kr, vr = k_pool[blk, tpos % block_size], v_pool[blk, tpos % block_size]
+            if fp8:
+                kr, vr = _bf16_bits_exact(e4m3_to_f64(kr)), _bf16_bits_exact(e4m3_to_f64(vr))
+            outs[r, i] = attention(q[s, i][None], np.array([p]), kr, tpos, vr, sinks=sinks, window=window,
+                                   base=base, k_rotated=True, n_threads=n_threads,
+                                   softmax_scale=SOFTMAX_SCALE * (k_scale if fp8 else 1.0),
+                                   v_scale=V_SCALE * (v_scale if fp8 else 1.0))[0]
+    return outs
+
+
+def kv_paged_append_fp8(k_new, v_new, pos, base: float, k_scale: float, v_scale: float):
+    """What an fp8 paged append stores: codes of rope(k_new at pos) / k_scale and
+    of v_new / v_scale, each rounded once from its fp64 value."""
+    kr = rope_partial(k_new, pos, base)
+    v = bf16_to_f64(v_new)
+    return e4m3_round(kr / k_scale), e4m3_round(v / v_scale), kr / k_scale, v / v_scale
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns to their fp64 values."""
+    u = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
 def kv_ring_append_rows(k_new, v_new, pos, base: float):
     """What the append writes: rope(k_new) at pos and v_new unchanged, fp64."""
     return rope_partial(k_new, pos, base), v_new

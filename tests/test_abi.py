@@ -192,6 +192,32 @@ def test_decode_multi_workspace(lib):
     assert decm(lib, cfg_glob(), S=16, nq=4, ws_bytes=expect(16, 4, 128) - 1) == WS
 
 
+def paged(lib, cfg, S=4, nq=1, block_size=128, dtype=0, ks=1.0, vs=1.0, table=FAKE, max_blocks=8, n_blocks=64,
+          ws_bytes=1 << 30):
+    return lib.mimo_attn_decode_paged(ctypes.byref(cfg), S, nq, FAKE, FAKE, FAKE, FAKE, n_blocks, block_size,
+                                      dtype, ctypes.c_float(ks), ctypes.c_float(vs), table, max_blocks, None, FAKE,
+                                      FAKE, ws_bytes, None)
+
+
+def test_paged_decode_contract(lib):
+    assert paged(lib, cfg_glob(), block_size=96) == UNSUP      # not a power of two
+    assert paged(lib, cfg_glob(), block_size=16) == UNSUP      # below one 32-slot step
+    assert paged(lib, cfg_glob(), dtype=7) == INVAL
+    assert paged(lib, cfg_glob(), dtype=1, ks=0.0) == INVAL
+    assert paged(lib, cfg_glob(), table=None) == INVAL
+    assert paged(lib, cfg_glob(), n_blocks=0) == INVAL
+    assert paged(lib, cfg_glob(), max_blocks=1 << 24) == UNSUP   # more than 2^30 slots per sequence
+    assert paged(lib, cfg_glob(), ws_bytes=16) == WS
+    assert paged(lib, cfg_glob(), S=0, table=None) == OK
+    c = cfg_glob()
+    assert lib.mimo_kv_paged_append(ctypes.byref(c), 4, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 100, 0,
+                                    ctypes.c_float(1.0), ctypes.c_float(1.0), FAKE, 8, None) == UNSUP
+    assert lib.mimo_kv_paged_append(ctypes.byref(c), 4, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 128, 0,
+                                    ctypes.c_float(1.0), ctypes.c_float(1.0), None, 8, None) == INVAL
+    assert lib.mimo_kv_paged_append(ctypes.byref(c), 0, None, None, None, None, None, 64, 128, 1,
+                                    ctypes.c_float(1.0), ctypes.c_float(1.0), None, 8, None) == OK
+
+
 def test_rope_and_append_contract(lib):
     c = cfg_swa()
     assert lib.mimo_rope_partial(ctypes.byref(c), FAKE, None, 4, 8, FAKE, None) == INVAL

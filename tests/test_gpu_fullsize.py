@@ -9,6 +9,8 @@ computes rows one by one); every output is also checked to be finite.
   * long global prefill T=524288 in query chunks of 65536: the first, a middle
     and the last chunk, each against its whole prefix
   * multi-query decode: 64 sliding sequences x 8 draft tokens, 16 global x 4
+  * paged fp8 decode (128-slot blocks in shuffled pools): the 16 global
+    sequences of the mixed decode and 64 sliding sequences
   * serving chunks of 8192 tokens, packed: four sliding-window chunks that
     continue sequences (127 earlier keys each) and four global chunks against
     prefixes of up to 57344 tokens
@@ -152,4 +154,31 @@ def test_multi_query_decode_full():
         got = host_f64(out)[check]
         ref = oracle.decode_multi(dd["q"], dd["pos"], dd["k_cache"], dd["v_cache"], sinks=dd["sinks"],
                                   window=window, base=base, seqs=check)
+        assert_parity(got, ref, f"{name}, {len(check)} of {S} sequences")
+
+
+def test_paged_fp8_decode_full():
+    for name, S, hkv, window, base, sinks, seed, check in (
+            ("global", 16, 4, 0, 1e7, False, 1009, [0, 6, 11, 15]),
+            ("sliding", 64, 8, 128, 1e4, True, 1010, list(range(0, 64, 8)))):
+        rng = np.random.Generator(np.random.PCG64(seed))
+        if window:
+            pos = rng.integers(128, 131072, size=S)
+        else:
+            pos = rng.integers(32768, 131072, size=S, endpoint=True) - 1
+        say(f"full-size paged fp8 decode: {name}, {S} sequences")
+        d = gen.paged_decode_inputs(S, 1, 128, 64, hkv, seed=seed, window=window, pos=pos, with_sinks=sinks,
+                                    kv_dtype="fp8", k_scale=0.02, v_scale=0.03)
+        cfg = Bd.swa_cfg() if window else Bd.global_cfg()
+        out = torch.empty((S, 1, 64, 128), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(Bd.mimo_attn_decode_multi_workspace_size(cfg, S, 1, 0), dtype=torch.uint8, device="cuda")
+        Bd.mimo_attn_decode_paged(cfg, dev_bf16(d["q"]), dev(d["pos"]), dev(d["k_pool"]), dev(d["v_pool"]),
+                                  dev(d["table"]), dev(d["sinks"]) if sinks else None, out, ws=ws,
+                                  k_scale=0.02, v_scale=0.03)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(out).all())
+        got = host_f64(out)[check]
+        ref = oracle.decode_paged(d["q"], d["pos"], d["k_pool"], d["v_pool"], d["table"], block_size=128,
+                                  kv_dtype="fp8", k_scale=0.02, v_scale=0.03, sinks=d["sinks"], window=window,
+                                  base=base, seqs=check)
         assert_parity(got, ref, f"{name}, {len(check)} of {S} sequences")

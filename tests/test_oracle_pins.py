@@ -416,6 +416,73 @@ def test_decode_multi_matches_prefill_rows(window, cap):
                 assert np.max(np.abs(o[i] - pref[t])) < 1e-13
 
 
+# ---------------------------------------------------------------- fp8 e4m3 and paged caches
+
+def test_e4m3_decode_closed_forms_and_library():
+    """OCP e4m3: exponent bias 7, 3 mantissa bits, subnormals below 2^-6, 448 the
+    largest value, 0x7F NaN; and every code against torch's float8_e4m3fn."""
+    known = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x3F: 1.875,
+             0x40: 2.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, v in known.items():
+        assert oracle.e4m3_to_f64([c])[0] == v, hex(c)
+    assert np.isnan(oracle.e4m3_to_f64([0x7F, 0xFF])).all()
+    codes = np.arange(256, dtype=np.uint8)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(oracle.e4m3_to_f64(codes), lib, equal_nan=True)
+
+
+def test_e4m3_round_nearest_even_saturating():
+    # midpoints go to the even code; beyond 448 saturates; subnormal midpoints too
+    assert list(oracle.e4m3_round([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10, 500.0, -1000.0])) == \
+        [0x38, 0x3A, 0x00, 0x02, 0x7E, 0xFE]
+    x = np.random.default_rng(1).standard_normal(200000) * 60
+    x = x[np.abs(x) < 448]
+    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(oracle.e4m3_to_f64(oracle.e4m3_round(x)), lib)
+
+
+@pytest.mark.parametrize("window,nq", [(0, 1), (0, 4), (128, 8)])
+def test_paged_decode_equals_contiguous_cache(window, nq):
+    """The same tokens in shuffled pool blocks or in a per-sequence cache give the
+    same result (bf16 pools)."""
+    S, bs = 3, 32
+    pos = np.array([40, 150, 5], np.int64)
+    d = gen.paged_decode_inputs(S, nq, bs, 8, 2, seed=40, window=window, pos=pos, with_sinks=window > 0)
+    cap = 160 if window == 0 else window + nq - 1
+    kc = np.full((S, cap, 2, 192), gen.BF16_NAN, np.uint16)
+    vc = np.full((S, cap, 2, 128), gen.BF16_NAN, np.uint16)
+    for s in range(S):
+        p = int(pos[s])
+        lo = max(0, p - (nq - 1) - window + 1) if window else 0
+        for t in range(lo, p + 1):
+            kc[s, t % cap] = d["k_pool"][d["table"][s, t // bs], t % bs]
+            vc[s, t % cap] = d["v_pool"][d["table"][s, t // bs], t % bs]
+    base = 1e4 if window else 1e7
+    a = oracle.decode_paged(d["q"], pos, d["k_pool"], d["v_pool"], d["table"], block_size=bs, sinks=d["sinks"],
+                            window=window, base=base)
+    b = oracle.decode_multi(d["q"], pos, kc, vc, sinks=d["sinks"], window=window, base=base)
+    assert np.array_equal(a, b)
+
+
+def test_fp8_paged_decode_equals_bf16_of_the_values():
+    """fp8 codes with power-of-two scales hold values bf16 represents exactly:
+    the fp8 paged decode equals the bf16 paged decode of those values."""
+    S, bs, nq = 2, 32, 2
+    pos = np.array([70, 33], np.int64)
+    ks, vs = 2.0 ** -3, 2.0 ** 2
+    d = gen.paged_decode_inputs(S, nq, bs, 8, 2, seed=41, window=0, pos=pos, with_sinks=False,
+                                kv_dtype="fp8", k_scale=ks, v_scale=vs)
+    kval = oracle.e4m3_to_f64(d["k_pool"]) * ks
+    vval = oracle.e4m3_to_f64(d["v_pool"]) * vs
+    kb = gen.f32_to_bf16_bits(kval.astype(np.float32))
+    vb = gen.f32_to_bf16_bits(vval.astype(np.float32))
+    assert np.array_equal(gen.bf16_bits_to_f32(kb).astype(np.float64), kval, equal_nan=True)
+    a = oracle.decode_paged(d["q"], pos, d["k_pool"], d["v_pool"], d["table"], block_size=bs, kv_dtype="fp8",
+                            k_scale=ks, v_scale=vs, window=0, base=1e7)
+    b = oracle.decode_paged(d["q"], pos, kb, vb, d["table"], block_size=bs, window=0, base=1e7)
+    assert np.max(np.abs(a - b)) < 1e-12
+
+
 def test_input_rounding_is_round_to_nearest_even():
     x = np.array([1.0, 1.00390625, 1.01171875, -2.5, 3.0e-3, 65504.0], np.float32)
     b = gen.f32_to_bf16_bits(x)
