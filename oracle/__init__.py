@@ -65,6 +65,12 @@ def _load():
             ctypes.c_double, P, ctypes.c_int64, ctypes.c_double, ctypes.c_double,
             P, P, P, ctypes.c_int]
         lib.oracle_attention.restype = None
+        lib.oracle_attention_backward.argtypes = [
+            P, P, ctypes.c_int64, P, P, ctypes.c_int64, P,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_double, P, ctypes.c_int64, ctypes.c_double, ctypes.c_double,
+            P, P, P, P, P, ctypes.c_int]
+        lib.oracle_attention_backward.restype = None
         _lib = lib
     return _lib
 
@@ -114,6 +120,48 @@ def attention(q, q_pos, k, k_pos, v, *, sinks=None, window: int = 0, base: float
     if want_psink:
         res.append(psink)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+def attention_backward(q, q_pos, k, k_pos, v, dout, *, sinks=None, window: int = 0, base: float,
+                       softmax_scale: float = SOFTMAX_SCALE, v_scale: float = V_SCALE,
+                       rope_dim: int = ROPE_DIM, n_threads: int = 0):
+    """Gradients of attention() for one sequence (k unrotated): returns dq [nq,Hq,Dqk],
+    dk [nk,Hkv,Dqk], dv [nk,Hkv,Dv] and dsinks [Hq] (None without sinks), fp64."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    dout = np.ascontiguousarray(dout, dtype=np.uint16)
+    q_pos = np.ascontiguousarray(q_pos, dtype=np.int64)
+    k_pos = np.ascontiguousarray(k_pos, dtype=np.int64)
+    nq, hq, dqk = q.shape
+    nk, hkv, _ = k.shape
+    dv_ = v.shape[2]
+    assert dout.shape == (nq, hq, dv_)
+    s = None if sinks is None else np.ascontiguousarray(sinks, dtype=np.float64)
+    dq = np.empty((nq, hq, dqk))
+    dk = np.empty((nk, hkv, dqk))
+    dv = np.empty((nk, hkv, dv_))
+    ds = np.empty(hq) if sinks is not None else None
+    _load().oracle_attention_backward(_ptr(q), _ptr(q_pos), nq, _ptr(k), _ptr(k_pos), nk, _ptr(v), hq, hkv, dqk,
+                                      dv_, rope_dim, float(base), _ptr(s), int(window), float(softmax_scale),
+                                      float(v_scale), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ds),
+                                      int(n_threads))
+    return dq, dk, dv, ds
+
+
+def prefill_backward(q, k, v, dout, *, sinks=None, pos0: int = 0, window: int, base: float, n_threads: int = 0):
+    """Gradients of a dense prefill batch (q [B,T,Hq,192], k/v [B,T,Hkv,*], token t at
+    pos0 + t, dout [B,T,Hq,128]): dq, dk, dv per batch entry and dsinks summed over
+    the batch."""
+    B, T = q.shape[:2]
+    pos = pos0 + np.arange(T, dtype=np.int64)
+    outs = [attention_backward(q[b], pos, k[b], pos, v[b], dout[b], sinks=sinks, window=window, base=base,
+                               n_threads=n_threads) for b in range(B)]
+    dq = np.stack([o[0] for o in outs])
+    dk = np.stack([o[1] for o in outs])
+    dv = np.stack([o[2] for o in outs])
+    ds = None if sinks is None else np.sum([o[3] for o in outs], axis=0)
+    return dq, dk, dv, ds
 
 
 def prefill_swa(q, k, v, sinks, *, pos0: int = 0, window: int = SWA_WINDOW, base: float = SWA_BASE,

@@ -36,6 +36,17 @@
  *
  * bf16 inputs are taken as exact values (bf16 -> fp64 is exact); nothing is
  * rounded in between.
+ *
+ * The backward (oracle_attention_backward) differentiates exactly that map,
+ * written out by the chain rule for the trainer's path (miles recipe page,
+ * section 5.4: the sink is trained through the fused attention).  With
+ * p_j = exp(s_j)/Z, p_sink = exp(sink)/Z and an upstream gradient dO of the
+ * output row: dp_j = v_scale <dO, v_j>; D = sum_j p_j dp_j (the sink column
+ * has no value, so its dp is 0); ds_j = p_j (dp_j - D); d rope(q) = scale *
+ * sum_j ds_j rope(k_j); d rope(k_j) += scale * ds_j rope(q); dv_j += v_scale
+ * p_j dO; d sink = -p_sink * D summed over every row of the head; and the
+ * gradients of q and k are the rotated gradients turned back by the transpose
+ * of the rotation (the same angle, negated).
  */
 #include <math.h>
 #include <stdint.h>
@@ -62,6 +73,19 @@ static void rope_one(const double *x, double *y, int D, int R, double base, int6
         double c = cos(angle), s = sin(angle);
         y[i] = x[i] * c - x[i + half] * s;
         y[i + half] = x[i + half] * c + x[i] * s;
+    }
+}
+
+/* y = R(pos)^T x: the transpose of rope_one's rotation (angle negated). */
+static void rope_one_transpose(const double *x, double *y, int D, int R, double base, int64_t pos) {
+    int half = R / 2;
+    for (int d = 0; d < D; ++d) y[d] = x[d];
+    for (int i = 0; i < half; ++i) {
+        double inv_freq = pow(base, -(double)(2 * i) / (double)R);
+        double angle = (double)pos * inv_freq;
+        double c = cos(angle), s = sin(angle);
+        y[i] = x[i] * c + x[i + half] * s;
+        y[i + half] = x[i + half] * c - x[i] * s;
     }
 }
 
@@ -181,4 +205,112 @@ void oracle_attention(const uint16_t *q, const int64_t *q_pos, int64_t nq,
         free(keys);
     }
     free(kr);
+}
+
+/*
+ * Gradients of the attention rows above (same arguments, k unrotated).
+ *   dout   [nq, Hq, Dv] bf16 bits: the upstream gradient of out
+ * Outputs (fp64, overwritten): dq [nq, Hq, Dqk], dk [nk, Hkv, Dqk],
+ * dv [nk, Hkv, Dv], dsinks [Hq] (NULL when sinks is NULL).  Work is split over
+ * KV heads, so each thread owns the dk / dv rows it accumulates.
+ */
+void oracle_attention_backward(const uint16_t *q, const int64_t *q_pos, int64_t nq,
+                               const uint16_t *k, const int64_t *k_pos, int64_t nk,
+                               const uint16_t *v, int Hq, int Hkv, int Dqk, int Dv, int R,
+                               double base, const double *sinks, int64_t window,
+                               double softmax_scale, double v_scale, const uint16_t *dout,
+                               double *dq, double *dk, double *dv, double *dsinks, int n_threads) {
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+    int group = Hq / Hkv;
+    double *kr = (double *)malloc((size_t)(nk > 0 ? nk : 1) * Hkv * Dqk * sizeof(double));
+    double *dkr = (double *)calloc((size_t)(nk > 0 ? nk : 1) * Hkv * Dqk, sizeof(double));
+    for (int64_t j = 0; j < nk; ++j) {
+        double buf[1024];
+        for (int g = 0; g < Hkv; ++g) {
+            const uint16_t *src = k + ((size_t)j * Hkv + g) * Dqk;
+            for (int d = 0; d < Dqk; ++d) buf[d] = bf16_value(src[d]);
+            rope_one(buf, kr + ((size_t)j * Hkv + g) * Dqk, Dqk, R, base, k_pos[j]);
+        }
+    }
+    memset(dv, 0, (size_t)nk * Hkv * Dv * sizeof(double));
+    if (dsinks) memset(dsinks, 0, (size_t)Hq * sizeof(double));
+
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int g = 0; g < Hkv; ++g) {
+        double *scores = (double *)malloc((size_t)(nk > 0 ? nk : 1) * sizeof(double));
+        double *dp = (double *)malloc((size_t)(nk > 0 ? nk : 1) * sizeof(double));
+        int64_t *keys = (int64_t *)malloc((size_t)(nk > 0 ? nk : 1) * sizeof(int64_t));
+        double qraw[1024], qrot[1024], dqrot[1024], dor[1024];
+        for (int h = g * group; h < (g + 1) * group; ++h) {
+            double dsink = 0.0;
+            for (int64_t r = 0; r < nq; ++r) {
+                const uint16_t *qs = q + ((size_t)r * Hq + h) * Dqk;
+                for (int d = 0; d < Dqk; ++d) qraw[d] = bf16_value(qs[d]);
+                rope_one(qraw, qrot, Dqk, R, base, q_pos[r]);
+                const uint16_t *ds = dout + ((size_t)r * Hq + h) * Dv;
+                for (int d = 0; d < Dv; ++d) dor[d] = bf16_value(ds[d]);
+
+                int64_t n = 0;
+                for (int64_t j = 0; j < nk; ++j) {
+                    if (!visible(q_pos[r], k_pos[j], window)) continue;
+                    const double *kj = kr + ((size_t)j * Hkv + g) * Dqk;
+                    double dot = 0.0;
+                    for (int d = 0; d < Dqk; ++d) dot += qrot[d] * kj[d];
+                    scores[n] = softmax_scale * dot;
+                    keys[n] = j;
+                    ++n;
+                }
+                double m = -INFINITY;
+                for (int64_t t = 0; t < n; ++t) if (scores[t] > m) m = scores[t];
+                if (sinks && sinks[h] > m) m = sinks[h];
+                double *dqr = dq + ((size_t)r * Hq + h) * Dqk;
+                if (m == -INFINITY) {
+                    for (int d = 0; d < Dqk; ++d) dqr[d] = 0.0;
+                    continue;
+                }
+                double z = 0.0;
+                for (int64_t t = 0; t < n; ++t) z += exp(scores[t] - m);
+                double zsink = sinks ? exp(sinks[h] - m) : 0.0;
+                z += zsink;
+                /* dp_j and D = sum_j p_j dp_j */
+                double D = 0.0;
+                for (int64_t t = 0; t < n; ++t) {
+                    const uint16_t *vj = v + ((size_t)keys[t] * Hkv + g) * Dv;
+                    double dot = 0.0;
+                    for (int d = 0; d < Dv; ++d) dot += dor[d] * bf16_value(vj[d]);
+                    dp[t] = v_scale * dot;
+                    scores[t] = exp(scores[t] - m) / z;      /* now p_j */
+                    D += scores[t] * dp[t];
+                }
+                if (sinks) dsink -= (zsink / z) * D;
+                for (int d = 0; d < Dqk; ++d) dqrot[d] = 0.0;
+                for (int64_t t = 0; t < n; ++t) {
+                    double dsj = scores[t] * (dp[t] - D);
+                    const double *kj = kr + ((size_t)keys[t] * Hkv + g) * Dqk;
+                    double *dkj = dkr + ((size_t)keys[t] * Hkv + g) * Dqk;
+                    for (int d = 0; d < Dqk; ++d) {
+                        dqrot[d] += softmax_scale * dsj * kj[d];
+                        dkj[d] += softmax_scale * dsj * qrot[d];
+                    }
+                    double *dvj = dv + ((size_t)keys[t] * Hkv + g) * Dv;
+                    for (int d = 0; d < Dv; ++d) dvj[d] += v_scale * scores[t] * dor[d];
+                }
+                rope_one_transpose(dqrot, dqr, Dqk, R, base, q_pos[r]);
+            }
+            if (dsinks) dsinks[h] = dsink;
+        }
+        free(scores);
+        free(dp);
+        free(keys);
+    }
+    for (int64_t j = 0; j < nk; ++j)
+        for (int g = 0; g < Hkv; ++g)
+            rope_one_transpose(dkr + ((size_t)j * Hkv + g) * Dqk, dk + ((size_t)j * Hkv + g) * Dqk, Dqk, R,
+                               base, k_pos[j]);
+    free(kr);
+    free(dkr);
 }

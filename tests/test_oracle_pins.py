@@ -416,6 +416,94 @@ def test_decode_multi_matches_prefill_rows(window, cap):
                 assert np.max(np.abs(o[i] - pref[t])) < 1e-13
 
 
+# ---------------------------------------------------------------- backward
+
+def _torch_eager_rows(q, k, v, qpos, kpos, sinks, window, base, R, scale, vscale):
+    """The eager structure in float64 torch ops (RoPE, repeat_kv, scores, mask,
+    sink column, softmax, column dropped, @ V, V scale); differentiable."""
+    half = R // 2
+    inv = torch.tensor([base ** (-(2 * i) / R) for i in range(half)], dtype=torch.float64)
+
+    def rope(x, pos):
+        ang = torch.from_numpy(pos.astype(np.float64))[:, None] * inv[None, :]
+        c, s_ = torch.cos(ang)[:, None, :], torch.sin(ang)[:, None, :]
+        a, b = x[..., :half], x[..., half:R]
+        return torch.cat([a * c - b * s_, b * c + a * s_, x[..., R:]], dim=-1)
+
+    hq, hkv = q.shape[1], k.shape[1]
+    qr, kr = rope(q, qpos), rope(k, kpos)
+    kr = kr.repeat_interleave(hq // hkv, dim=1)
+    vv = v.repeat_interleave(hq // hkv, dim=1)
+    sc = torch.einsum("ihd,jhd->hij", qr, kr) * scale
+    qp, kp = torch.from_numpy(qpos)[:, None], torch.from_numpy(kpos)[None, :]
+    vis = kp <= qp
+    if window:
+        vis &= (qp - kp) < window
+    sc = sc.masked_fill(~vis[None], -math.inf)
+    if sinks is not None:
+        sc = torch.cat([sc, sinks[:, None, None].expand(hq, q.shape[0], 1)], dim=2)
+    p = torch.softmax(sc, dim=2)[:, :, :k.shape[0]]
+    return torch.einsum("hij,jhd->ihd", p, vv) * vscale
+
+
+@pytest.mark.parametrize("window,with_sink,hkv", [(0, False, 2), (5, True, 2), (1, True, 1), (16, True, 4)])
+def test_backward_matches_autograd(window, with_sink, hkv):
+    """The oracle's chain-rule gradients against torch autograd (float64) through
+    the eager structure."""
+    n, hq, dqk, dv, R = 24, 8, 12, 8, 8
+    qb, kb, vb = rand_case(51 + window, n, n, hq, hkv, dqk, dv)
+    dob = gen.normal_bf16(np.random.SeedSequence(52 + window), (n, hq, dv))
+    pos = np.arange(500, 500 + n, dtype=np.int64)
+    sinks = np.linspace(-1.5, 2.0, hq) if with_sink else None
+    scale = 1.0 / math.sqrt(dqk)
+    got = oracle.attention_backward(qb, pos, kb, pos, vb, dob, sinks=sinks, window=window, base=1e4,
+                                    softmax_scale=scale, v_scale=0.707, rope_dim=R)
+    Q = torch.tensor(f64(qb), requires_grad=True)
+    K = torch.tensor(f64(kb), requires_grad=True)
+    V = torch.tensor(f64(vb), requires_grad=True)
+    Sk = torch.tensor(sinks, requires_grad=True) if with_sink else None
+    out = _torch_eager_rows(Q, K, V, pos, pos, Sk, window, 1e4, R, scale, 0.707)
+    out.backward(torch.tensor(f64(dob)))
+    for a, b in ((got[0], Q.grad), (got[1], K.grad), (got[2], V.grad)):
+        assert np.max(np.abs(a - b.numpy())) < 1e-12
+    if with_sink:
+        assert np.max(np.abs(got[3] - Sk.grad.numpy())) < 1e-12
+    else:
+        assert got[3] is None
+
+
+def test_backward_window_one_closed_form():
+    """W = 1: o_t = 0.707 g_t v_t with g_t = sigmoid(s_tt - sink), so
+    dv_t = 0.707 g_t dO_t and d sink = -sum_t 0.707 g_t (1 - g_t) <dO_t, v_t>."""
+    n = 40
+    qb, kb, vb = rand_case(61, n, n, 4, 1, 192, 128)
+    dob = gen.normal_bf16(np.random.SeedSequence(62), (n, 4, 128))
+    pos = np.arange(n, dtype=np.int64)
+    sinks = np.array([0.5, -0.5, 1.5, 0.0])
+    _, _, dv, ds = oracle.attention_backward(qb, pos, kb, pos, vb, dob, sinks=sinks, window=1, base=1e4)
+    qr, kr = oracle.rope_partial(qb, pos, 1e4), oracle.rope_partial(kb, pos, 1e4)
+    s_tt = np.einsum("thd,td->th", qr, kr[:, 0]) * oracle.SOFTMAX_SCALE
+    g = 1.0 / (1.0 + np.exp(-(s_tt - sinks[None, :])))
+    dO, v = f64(dob), f64(vb)[:, 0]
+    assert np.max(np.abs(dv[:, 0] - 0.707 * np.einsum("th,thd->td", g, dO))) < 1e-12
+    want = -np.sum(0.707 * g * (1 - g) * np.einsum("thd,td->th", dO, v), axis=0)
+    assert np.max(np.abs(ds - want)) < 1e-12
+
+
+def test_backward_position_shift_invariance():
+    """Shifting every position changes no score, so no gradient of the unrotated
+    inputs either."""
+    n = 60
+    qb, kb, vb = rand_case(71, n, n, 8, 1, 192, 128)
+    dob = gen.normal_bf16(np.random.SeedSequence(72), (n, 8, 128))
+    p0 = np.arange(n, dtype=np.int64)
+    sinks = np.linspace(-1, 1, 8)
+    a = oracle.attention_backward(qb, p0, kb, p0, vb, dob, sinks=sinks, window=16, base=1e4)
+    b = oracle.attention_backward(qb, p0 + 99999, kb, p0 + 99999, vb, dob, sinks=sinks, window=16, base=1e4)
+    for x, y in zip(a, b):
+        assert np.max(np.abs(x - y)) < 1e-9
+
+
 # ---------------------------------------------------------------- fp8 e4m3 and paged caches
 
 def test_e4m3_decode_closed_forms_and_library():
