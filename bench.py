@@ -23,6 +23,9 @@ global sequences, with n_q = 4 (EAGLE) and n_q = 8 (DFlash) draft tokens.
 shuffled pools) at the mixed-decode sizes: the 16 global sequences with bf16
 and with fp8 e4m3 pools, and the 64 sliding sequences with fp8 pools.
 
+--workload backward times the sliding-window + sink backward (dq, dk, dv, d sink)
+of the B=4 x T=8192 prefill, from the forward's output and LSE.
+
 --workload serving_chunks times packed (THD) serving chunks of 8192 tokens:
 four sliding-window chunks that continue sequences at positions 8192, 65536,
 131072 and 262144 (each with the 127 keys before it) and four global chunks
@@ -254,7 +257,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["layer_step", "long_prefill", "serving_chunks", "spec_decode", "paged_decode"], default="layer_step")
+    ap.add_argument("--workload", choices=["layer_step", "long_prefill", "serving_chunks", "spec_decode", "paged_decode",
+                                            "backward"], default="layer_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -293,6 +297,8 @@ def main():
         return main_spec_decode(args, torch, gen, Bd)
     if args.workload == "paged_decode":
         return main_paged_decode(args, torch, gen, Bd)
+    if args.workload == "backward":
+        return main_backward(args, torch, gen, Bd)
 
     ph = setup_layer_step(torch, gen, Bd)
     names = ["swa_prefill", "global_prefill", "append_swa", "append_global", "decode_swa", "decode_global"]
@@ -634,6 +640,59 @@ def main_paged_decode(args, torch, gen, Bd):
                           "achieved": g["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": g["frac_hbm_peak"],
                           "traffic": None},
              "cpu_baseline": None, "phases": phases}
+    print(json.dumps(out_j))
+
+
+def main_backward(args, torch, gen, Bd):
+    B, T = 4, 8192
+    log("setup: sliding-window prefill B=4 T=8192, forward once for its output and LSE")
+    d = gen.prefill_inputs(B, T, 64, 8, seed=1001, with_sinks=True)
+    cfg = Bd.swa_cfg()
+    q, k, v = _dev_bf16(torch, d["q"]), _dev_bf16(torch, d["k"]), _dev_bf16(torch, d["v"])
+    sinks = torch.from_numpy(d["sinks"]).to("cuda")
+    del d
+    dout = _dev_bf16(torch, gen.normal_bf16(np.random.SeedSequence(1012), (B, T, 64, 128)))
+    out = torch.empty((B, T, 64, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, 64, T), dtype=torch.float32, device="cuda")
+    Bd.mimo_attn_prefill_swa(cfg, q, k, v, sinks, out, lse=lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dsinks = torch.empty(64, dtype=torch.float32, device="cuda")
+    ws = torch.empty(Bd.mimo_attn_backward_workspace_size(cfg, B, T), dtype=torch.uint8, device="cuda")
+
+    def step():
+        Bd.mimo_attn_prefill_backward(cfg, q, k, v, sinks, out, lse, dout, dq, dk, dv, dsinks, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    s_ev.record()
+    for _ in range(args.steps):
+        step()
+    e_ev.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    ms_ev = s_ev.elapsed_time(e_ev) / args.steps
+    pairs = B * swa_pairs(T, 128)
+    # one recompute of S, then dP, dV, dK, dQ: 2 * (3 * 192 + 2 * 128) FLOP per visible pair and head
+    flops = 2 * (3 * 192 + 2 * 128) * 64 * pairs
+    # read q, out, dO and write dq per (token, query head); read k, v and write dk, dv per (token, KV head);
+    # read the LSE
+    nbytes = B * T * (64 * (192 + 128 + 128 + 192) * 2 + 8 * (192 + 128) * 2 * 2) + B * 64 * T * 4
+    tflops = flops / (ms_ev * 1e-3) / 1e12
+    gbs = nbytes / (ms_ev * 1e-3) / 1e9
+    out_j = {"metric": METRIC, "value": flops / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
+             "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+             "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+             "data": "synthetic: seeded N(0,1) bf16 q/k/v/dO, N(0,1) fp32 sinks",
+             "config": {"workload": "swa_backward_b4_t8192 (dq, dk, dv, d sink from the forward's output and LSE)"},
+             "roofline": {"bound": "hbm", "kernel": "bwd_prep + bwd_sink + bwd_dq + bwd_dkdv (one call)",
+                          "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                          "traffic": None, "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
+                          "tflops": tflops, "frac_mfma_peak": tflops / PEAK_BF16_TFLOPS},
+             "cpu_baseline": None, "ms_per_call_events": ms_ev}
     print(json.dumps(out_j))
 
 

@@ -64,6 +64,10 @@ def load_library(path: str = LIB_PATH):
     lib.mimo_attn_prefill_global.argtypes = [C, P, P, P, I32, I32, I32, I64, P, P, P]
     lib.mimo_attn_prefill_varlen.argtypes = [C, P, P, P, P, I32, P, P, P, I32, I32, P, P, P]
     lib.mimo_attn_decode.argtypes = [C, I32, P, P, P, P, I32, P, P, P, ctypes.c_size_t, P]
+    lib.mimo_attn_prefill_backward.argtypes = [C, P, P, P, P, I32, I32, I64, P, P, P, P, P, P, P, P,
+                                               ctypes.c_size_t, P]
+    lib.mimo_attn_backward_workspace_size.argtypes = [C, I32, I32]
+    lib.mimo_attn_backward_workspace_size.restype = ctypes.c_size_t
     lib.mimo_attn_decode_workspace_size.argtypes = [C, I32, I32]
     lib.mimo_attn_decode_workspace_size.restype = ctypes.c_size_t
     lib.mimo_attn_decode_multi.argtypes = [C, I32, I32, P, P, P, P, I32, P, P, P, ctypes.c_size_t, P]
@@ -77,7 +81,8 @@ def load_library(path: str = LIB_PATH):
     lib.mimo_last_error.restype = ctypes.c_char_p
     for fn in ("mimo_rope_partial", "mimo_attn_prefill_swa", "mimo_attn_prefill_global",
                "mimo_attn_prefill_varlen", "mimo_attn_decode", "mimo_attn_decode_multi",
-               "mimo_attn_decode_paged", "mimo_kv_paged_append", "mimo_kv_ring_append"):
+               "mimo_attn_decode_paged", "mimo_kv_paged_append", "mimo_kv_ring_append",
+               "mimo_attn_prefill_backward"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -161,6 +166,31 @@ def mimo_attn_prefill_varlen(cfg: MimoAttnCfg, q, k, v, sinks, cu_seqlens_q, cu_
                                         _p(cu_seqlens_k), _p(k_pos0), max_seqlen_q, q.shape[0], _p(out),
                                         _p(lse), _stream(stream)))
     return out
+
+
+def mimo_attn_backward_workspace_size(cfg: MimoAttnCfg, B: int, T: int) -> int:
+    return int(load_library().mimo_attn_backward_workspace_size(ctypes.byref(cfg), B, T))
+
+
+def mimo_attn_prefill_backward(cfg: MimoAttnCfg, q, k, v, sinks, out, lse, dout, dq, dk, dv, dsinks=None,
+                               pos0: int = 0, ws=None, stream=None):
+    """Gradients of a dense prefill: q/dq [B,T,Hq,192], k/dk [B,T,Hkv,192], v/dv [B,T,Hkv,128], out/dout
+    [B,T,Hq,128], lse [B,Hq,T] from the forward, dsinks [Hq] (when sinks are given).  ws is allocated
+    here when not given."""
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, torch.bfloat16, n, 4)
+    _need(lse, torch.float32, "lse", 3); _need(sinks, torch.float32, "sinks", 1)
+    _need(dsinks, torch.float32, "dsinks", 1)
+    B, T = q.shape[:2]
+    if ws is None:
+        ws = torch.empty(max(1, mimo_attn_backward_workspace_size(cfg, B, T)), dtype=torch.uint8, device=q.device)
+    ws_bytes = ws.numel() * ws.element_size()
+    _check("mimo_attn_prefill_backward",
+           lib.mimo_attn_prefill_backward(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(sinks), B, T, pos0, _p(out),
+                                          _p(lse), _p(dout), _p(dq), _p(dk), _p(dv), _p(dsinks), _p(ws), ws_bytes,
+                                          _stream(stream)))
+    return dq, dk, dv, dsinks
 
 
 def mimo_attn_decode_workspace_size(cfg: MimoAttnCfg, S: int, cap: int) -> int:

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmimo_attn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["rope.hip", "prefill.hip", "decode.hip", "api.cpp"]
+SOURCES = ["rope.hip", "prefill.hip", "decode.hip", "backward.hip", "api.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

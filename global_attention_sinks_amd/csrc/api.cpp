@@ -185,6 +185,39 @@ struct PagedLayout {
     float k_scale = 1.0f, v_scale = 1.0f;
 };
 
+size_t mimo_attn_backward_workspace_size(const mimo_attn_cfg *cfg, int32_t B, int32_t T) {
+    if (!cfg || B <= 0 || T <= 0 || cfg->num_q_heads <= 0) return 0;
+    return backward_workspace_bytes(B, T, cfg->num_q_heads);
+}
+
+mimo_status mimo_attn_prefill_backward(const mimo_attn_cfg *cfg, const uint16_t *q, const uint16_t *k,
+                                       const uint16_t *v, const float *sinks, int32_t B, int32_t T, int64_t pos0,
+                                       const uint16_t *out, const float *lse, const uint16_t *dout, uint16_t *dq,
+                                       uint16_t *dk, uint16_t *dv, float *dsinks, void *ws, size_t ws_bytes,
+                                       void *stream) {
+    mimo_status st = prefill_common(cfg, q, k, v, dq, B, T, T);
+    if (st != MIMO_OK) return st;
+    if (pos0 < 0) return fail(MIMO_ERR_INVALID_ARGUMENT, "pos0 must be >= 0");
+    if ((int64_t)B * T * cfg->num_q_heads > ((int64_t)1 << 31) / 2)
+        return fail(MIMO_ERR_UNSUPPORTED, "B * T * num_q_heads is too large");
+    if (B == 0 || T == 0) return ok();
+    if (!out || !lse || !dout || !dk || !dv)
+        return fail(MIMO_ERR_INVALID_ARGUMENT, "out, lse, dout, dq, dk and dv must be non-NULL");
+    if (sinks && !dsinks) return fail(MIMO_ERR_INVALID_ARGUMENT, "dsinks must be non-NULL when sinks are given");
+    const size_t need = backward_workspace_bytes(B, T, cfg->num_q_heads);
+    if (!ws || ws_bytes < need)
+        return fail(MIMO_ERR_WORKSPACE, "backward workspace needs %zu bytes (got %zu)", need,
+                    ws ? ws_bytes : (size_t)0);
+    BwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse; a.sinks = sinks;
+    a.D = (float *)ws; a.csink = a.D + (size_t)B * T * cfg->num_q_heads;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dsinks = sinks ? dsinks : nullptr;
+    a.B = B; a.T = T; a.Hq = cfg->num_q_heads; a.Hkv = cfg->num_kv_heads; a.window = cfg->window; a.pos0 = pos0;
+    a.scale = cfg->softmax_scale; a.scale_log2 = scale_log2(cfg); a.v_scale = cfg->v_scale;
+    a.rt = rope_turns(cfg->rope_base);
+    return from_hip(launch_backward(a, (hipStream_t)stream), "prefill_backward launch");
+}
+
 static mimo_status decode_common(const mimo_attn_cfg *cfg, int32_t S, int32_t n_q, const uint16_t *q,
                                  const int64_t *q_pos, const void *k_cache, const void *v_cache,
                                  int32_t cap, const float *sinks, uint16_t *out, void *ws, size_t ws_bytes,

@@ -51,6 +51,24 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill(PrefillArgs a, hipStream_t stream);
 
+// ---- prefill backward (backward.hip)
+struct BwdArgs {
+    const uint16_t *q, *k, *v, *out, *dout;   // [B, T, H, D] bf16, q/k unrotated
+    const float *lse;                         // [B, Hq, T] natural-log LSE of the forward
+    const float *sinks;                       // nullable
+    float *D;                                 // workspace [B, T, Hq]: rowsum(dO o O)
+    float *csink;                             // workspace [B, T, Hq]: each row's sink term
+    uint16_t *dq, *dk, *dv;
+    float *dsinks;                            // [Hq], written when sinks != NULL
+    int32_t B, T, Hq, Hkv, window;
+    int64_t pos0;
+    float scale, scale_log2, v_scale;
+    RopeTurns rt;
+    int32_t n_qblk, n_hgrp, n_kblk;           // filled by the launcher
+};
+size_t backward_workspace_bytes(int32_t B, int32_t T, int32_t Hq);
+hipError_t launch_backward(BwdArgs a, hipStream_t stream);
+
 // ---- decode (decode.hip)
 #ifndef MIMO_DECODE_WAVES
 #define MIMO_DECODE_WAVES 1024

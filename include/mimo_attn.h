@@ -198,6 +198,29 @@ mimo_status mimo_attn_decode_multi(const mimo_attn_cfg *cfg, int32_t S, int32_t 
  * unsupported cfg or n_q). */
 size_t mimo_attn_decode_multi_workspace_size(const mimo_attn_cfg *cfg, int32_t S, int32_t n_q, int32_t cap);
 
+/*
+ * Backward of dense prefill attention (both layer types; cfg->window > 0 is a
+ * sliding window, 0 causal): the trainer's path of the sliding-window layers
+ * with their learned sink (miles MiMo-V2.6-Flash page, section 5.4: the sink is
+ * trained through the fused attention).  Inputs are the forward's q, k, v (as
+ * given to mimo_attn_prefill_swa / _global with Tq = Tk = T, token t at
+ * pos0 + t), sinks or NULL, its output `out` and its `lse` ([B, num_q_heads, T],
+ * the forward's lse output), and the upstream gradient dout [B, T, num_q_heads,
+ * 128].  Outputs (overwritten): dq [B, T, num_q_heads, 192], dk [B, T,
+ * num_kv_heads, 192], dv [B, T, num_kv_heads, 128] (gradients of the unrotated
+ * inputs, bf16) and, when sinks are given, dsinks [num_q_heads] fp32 (summed
+ * over the batch).  ws: at least mimo_attn_backward_workspace_size() bytes.
+ * Deterministic: nothing is accumulated across workgroups.
+ */
+mimo_status mimo_attn_prefill_backward(const mimo_attn_cfg *cfg, const uint16_t *q, const uint16_t *k,
+                                       const uint16_t *v, const float *sinks, int32_t B, int32_t T, int64_t pos0,
+                                       const uint16_t *out, const float *lse, const uint16_t *dout, uint16_t *dq,
+                                       uint16_t *dk, uint16_t *dv, float *dsinks, void *ws, size_t ws_bytes,
+                                       void *stream);
+
+/* Workspace bytes of mimo_attn_prefill_backward (two fp32 values per row and head). */
+size_t mimo_attn_backward_workspace_size(const mimo_attn_cfg *cfg, int32_t B, int32_t T);
+
 /* Element type of a paged KV cache. */
 typedef enum mimo_kv_dtype {
     MIMO_KV_BF16 = 0,      /* bf16 bit patterns */

@@ -218,6 +218,24 @@ def test_paged_decode_contract(lib):
                                     ctypes.c_float(1.0), ctypes.c_float(1.0), None, 8, None) == OK
 
 
+def bwd(lib, cfg, Bn=2, T=64, ws=FAKE, ws_bytes=1 << 30, dsinks=FAKE, sinks=None, lse=FAKE):
+    return lib.mimo_attn_prefill_backward(ctypes.byref(cfg), FAKE, FAKE, FAKE, sinks, Bn, T, 0, FAKE, lse, FAKE,
+                                          FAKE, FAKE, FAKE, dsinks, ws, ws_bytes, None)
+
+
+def test_backward_contract(lib):
+    c = cfg_swa()
+    assert bwd(lib, c, lse=None) == INVAL
+    assert bwd(lib, c, sinks=FAKE, dsinks=None) == INVAL
+    assert "dsinks" in err(lib)
+    assert bwd(lib, c, ws=None, ws_bytes=0) == WS
+    need = lib.mimo_attn_backward_workspace_size(ctypes.byref(c), 2, 64)
+    assert need == 2 * 2 * 64 * 64 * 4          # D and the sink term per (row, head), fp32
+    assert bwd(lib, c, ws_bytes=need - 1) == WS
+    assert bwd(lib, cfg_swa(num_q_heads=16, num_kv_heads=8)) == UNSUP    # group of 2
+    assert bwd(lib, c, T=0, lse=None) == OK
+
+
 def test_rope_and_append_contract(lib):
     c = cfg_swa()
     assert lib.mimo_rope_partial(ctypes.byref(c), FAKE, None, 4, 8, FAKE, None) == INVAL

@@ -11,6 +11,8 @@ computes rows one by one); every output is also checked to be finite.
   * multi-query decode: 64 sliding sequences x 8 draft tokens, 16 global x 4
   * paged fp8 decode (128-slot blocks in shuffled pools): the 16 global
     sequences of the mixed decode and 64 sliding sequences
+  * sliding-window + sink backward, B=4 x T=8192: dq of 256-row slices and dk/dv
+    of the keys whose every query lies in the slice
   * serving chunks of 8192 tokens, packed: four sliding-window chunks that
     continue sequences (127 earlier keys each) and four global chunks against
     prefixes of up to 57344 tokens
@@ -182,3 +184,35 @@ def test_paged_fp8_decode_full():
                                   kv_dtype="fp8", k_scale=0.02, v_scale=0.03, sinks=d["sinks"], window=window,
                                   base=base, seqs=check)
         assert_parity(got, ref, f"{name}, {len(check)} of {S} sequences")
+
+
+def test_swa_backward_b4_t8192():
+    say("full-size sliding backward B=4 T=8192")
+    B, T = 4, 8192
+    d = gen.prefill_inputs(B, T, 64, 8, seed=1011, with_sinks=True)
+    dout = gen.normal_bf16(np.random.SeedSequence(1012), (B, T, 64, 128))
+    cfg = Bd.swa_cfg()
+    q, k, v = dev_bf16(d["q"]), dev_bf16(d["k"]), dev_bf16(d["v"])
+    sinks = dev(d["sinks"])
+    out = torch.empty((B, T, 64, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, 64, T), dtype=torch.float32, device="cuda")
+    Bd.mimo_attn_prefill_swa(cfg, q, k, v, sinks, out, lse=lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dsinks = torch.empty(64, dtype=torch.float32, device="cuda")
+    Bd.mimo_attn_prefill_backward(cfg, q, k, v, sinks, out, lse, dev_bf16(dout), dq, dk, dv, dsinks)
+    torch.cuda.synchronize()
+    for t_ in (dq, dk, dv, dsinks):
+        assert bool(torch.isfinite(t_).all())
+    for b, t0 in ((0, 0), (0, 4000), (3, T - 256)):
+        t1 = t0 + 256
+        k0 = max(0, t0 - 127)
+        pos = np.arange(T, dtype=np.int64)
+        rdq, rdk, rdv, _ = oracle.attention_backward(d["q"][b, t0:t1], pos[t0:t1], d["k"][b, k0:t1], pos[k0:t1],
+                                                     d["v"][b, k0:t1], dout[b, t0:t1], sinks=d["sinks"], window=128,
+                                                     base=1e4)
+        keys = slice(t0 - k0, t1 - 127 - k0)                 # keys t0 .. t1-128: every query that sees them is here
+        for name, got, ref in (("dq", host_f64(dq[b, t0:t1]), rdq),
+                               ("dk", host_f64(dk[b, t0:t1 - 127]), rdk[keys]),
+                               ("dv", host_f64(dv[b, t0:t1 - 127]), rdv[keys])):
+            scale = max(1.0, float(np.abs(ref).max()))
+            assert_parity(got, ref, f"seq {b} rows {t0}..{t1 - 1} {name}", max_abs=2e-2 * scale, mean_abs=2e-3 * scale)
