@@ -8,8 +8,9 @@
 // and dq, dk are dQ~, dK~ turned back by the transpose of the partial RoPE
 // rotation (the same angle, negated).
 //
-//   bwd_prep_kernel    D per (row, head) from O and dO; each row's sink term
-//   bwd_sink_kernel    one workgroup per head sums the sink terms (fixed order)
+//   bwd_prep_kernel    D per (row, head) from O and dO; per workgroup and head,
+//                      the sum of its rows' sink terms
+//   bwd_sink_kernel    one workgroup per head sums those partials (fixed order)
 //   bwd_dq_kernel      query-major: a workgroup owns 32 queries x 4 heads of a
 //                      GQA group; per 32-key tile (K rotated, K^T and V staged
 //                      in LDS, shared by the 4 heads) it rebuilds S^T and dP^T
@@ -35,6 +36,7 @@ constexpr float kPosInf = __builtin_inff();
 constexpr int RSTR = kDqk + 8;   // LDS row stride of a 192-dim tile (bf16)
 constexpr int VSTR = kDv + 8;    // LDS row stride of a 128-dim tile
 constexpr int TSTR = 32 + 8;     // LDS row stride of a transposed 32-column tile
+constexpr int kPrepRows = 1024;  // (row, head) pairs per workgroup of the D pass
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
@@ -92,6 +94,54 @@ __device__ __forceinline__ void transpose32(uint16_t *dst, const uint16_t *src, 
     }
 }
 
+// One 32-row stage held in registers between its global loads and its LDS
+// stores (256 threads): a 192-dim row piece that rotates (threads < 128), two
+// pass-through 192-dim chunks and two 128-dim chunks per thread.
+struct StageRegs {
+    u32x4 rx, ry;
+    u32x4 pl[2];
+    u32x4 r128[2];
+};
+
+__device__ __forceinline__ void stage_load(StageRegs &st, const uint16_t *src192, size_t s192,
+                                           const uint16_t *src128, size_t s128, int nvalid, int tid) {
+    // rows past the end re-read the last valid row: they are masked out of every
+    // product (zero probability), and finite values keep 0 * value = 0; the loads
+    // stay unconditional so that they are all in flight together
+    const int last = nvalid - 1;
+    if (tid < 128) {
+        const int row = min(tid >> 2, last), cc = tid & 3;
+        st.rx = ldg128(src192 + row * s192 + 8 * cc);
+        st.ry = ldg128(src192 + row * s192 + 8 * cc + 32);
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int u = tid + 256 * r;
+        const int row = min(u >> 4, last), c = 8 + (u & 15), c2 = u & 15;
+        st.pl[r] = ldg128(src192 + row * s192 + 8 * c);
+        st.r128[r] = ldg128(src128 + row * s128 + 8 * c2);
+    }
+}
+
+// Rotate (rows at positions pos0 + row) and store a loaded stage into LDS.
+__device__ __forceinline__ void stage_store(const StageRegs &st, uint16_t *d192, uint16_t *d128, int64_t pos0,
+                                            const RopeTurns &rt, int tid) {
+    if (tid < 128) {
+        const int row = tid >> 2, cc = tid & 3;
+        u32x4 x = st.rx, y = st.ry;
+        rope_rotate8(x, y, rt, 8 * cc, pos0 + row);
+        *reinterpret_cast<u32x4 *>(d192 + row * RSTR + 8 * cc) = x;
+        *reinterpret_cast<u32x4 *>(d192 + row * RSTR + 8 * cc + 32) = y;
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int u = tid + 256 * r;
+        const int row = u >> 4, c = 8 + (u & 15), c2 = u & 15;
+        *reinterpret_cast<u32x4 *>(d192 + row * RSTR + 8 * c) = st.pl[r];
+        *reinterpret_cast<u32x4 *>(d128 + row * VSTR + 8 * c2) = st.r128[r];
+    }
+}
+
 // Turn a rotated-space gradient held as (dims d, d + 32) pairs back: the
 // transpose of the rotation by pos * theta_d.
 __device__ __forceinline__ void rope_back(float &x, float &y, uint64_t turn, int64_t pos) {
@@ -105,38 +155,57 @@ __device__ __forceinline__ void rope_back(float &x, float &y, uint64_t turn, int
 
 }  // namespace
 
-// ---- D = rowsum(dO o O) and each row's sink term -exp(sink - L) D; one thread per (row, head)
+// ---- D = rowsum(dO o O) per (row, head); 16 lanes per row (16 bytes each), a
+// workgroup takes kPrepRows consecutive rows and leaves, per head, the sum of
+// its rows' sink terms -exp(sink - L) D (summed in a fixed order)
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
-    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // ((b * T) + t) * Hq + h
+    __shared__ float term[kPrepRows];
+    const int tid = threadIdx.x, sub = tid & 15, grp = tid >> 4;   // 16 groups of 16 lanes
     const int64_t n = (int64_t)a.B * a.T * a.Hq;
-    if (r >= n) return;
-    const uint16_t *o = a.out + r * kDv;
-    const uint16_t *g = a.dout + r * kDv;
-    float acc = 0.0f;
-#pragma unroll 4
-    for (int c = 0; c < 16; ++c) {
-        const u32x4 x = ldg128(o + 8 * c), y = ldg128(g + 8 * c);
+    const int64_t r0 = (int64_t)blockIdx.x * kPrepRows;
+#pragma unroll 8
+    for (int i = grp; i < kPrepRows; i += 16) {
+        const int64_t r = r0 + i;                                    // ((b * T) + t) * Hq + h
+        float acc = 0.0f;
+        if (r < n) {
+            const u32x4 x = ldg128(a.out + r * kDv + 8 * sub), y = ldg128(a.dout + r * kDv + 8 * sub);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) acc += bf_lo(x[w]) * bf_lo(y[w]) + bf_hi(x[w]) * bf_hi(y[w]);
+            for (int w = 0; w < 4; ++w) acc += bf_lo(x[w]) * bf_lo(y[w]) + bf_hi(x[w]) * bf_hi(y[w]);
+        }
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+        if (sub == 0) {
+            float t_ = 0.0f;
+            if (r < n) {
+                a.D[r] = acc;
+                if (a.sinks) {
+                    const int h = (int)(r % a.Hq);
+                    const int64_t bt = r / a.Hq;
+                    const int64_t b = bt / a.T, t = bt - b * a.T;
+                    t_ = -__expf(a.sinks[h] - a.lse[((size_t)b * a.Hq + h) * a.T + t]) * acc;
+                }
+            }
+            term[i] = t_;
+        }
     }
-    a.D[r] = acc;
-    if (a.sinks) {
-        const int h = (int)(r % a.Hq);
-        const int64_t bt = r / a.Hq;
-        const int64_t b = bt / a.T, t = bt - b * a.T;
-        const float L = a.lse[((size_t)b * a.Hq + h) * a.T + t];
-        a.csink[r] = -__expf(a.sinks[h] - L) * acc;
+    if (!a.sinks) return;
+    __syncthreads();
+    // rows r0 + i with (r0 + i) % Hq == h, in increasing i
+    for (int h = tid; h < a.Hq; h += 256) {
+        float s_ = 0.0f;
+        for (int i = (int)((h - r0 % a.Hq + a.Hq) % a.Hq); i < kPrepRows; i += a.Hq) s_ += term[i];
+        a.csink[(size_t)blockIdx.x * a.Hq + h] = s_;
     }
 }
 
-// ---- d sink_h: one workgroup per head, fixed-order tree sum over every row
+// ---- d sink_h: one workgroup per head, fixed-order tree sum over the workgroup partials
 __global__ __launch_bounds__(256) void bwd_sink_kernel(BwdArgs a) {
     __shared__ float red[256];
     const int h = blockIdx.x;
-    const int64_t rows = (int64_t)a.B * a.T;
-    float s = 0.0f;
-    for (int64_t i = threadIdx.x; i < rows; i += 256) s += a.csink[i * a.Hq + h];
-    red[threadIdx.x] = s;
+    const int64_t nblk = ((int64_t)a.B * a.T * a.Hq + kPrepRows - 1) / kPrepRows;
+    float s_ = 0.0f;
+    for (int64_t i = threadIdx.x; i < nblk; i += 256) s_ += a.csink[i * a.Hq + h];
+    red[threadIdx.x] = s_;
     __syncthreads();
     for (int off = 128; off > 0; off >>= 1) {
         if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
@@ -204,12 +273,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void bwd_dq_ke
     const int win = a.window > 0 ? a.window : 0x7fffffff;
     const size_t krs = (size_t)a.Hkv * kDqk, vrs = (size_t)a.Hkv * kDv;
 
-    for (int j0 = (jlo / 32) * 32; j0 <= jhi; j0 += 32) {
-        const int nvalid = min(32, a.T - j0);
+    // the next tile's K / V rows are loaded into registers while this one is computed
+    auto load_tile = [&](StageRegs &st, int j0) {
+        stage_load(st, a.k + ((size_t)b * a.T + j0) * krs + (size_t)g * kDqk, krs,
+                   a.v + ((size_t)b * a.T + j0) * vrs + (size_t)g * kDv, vrs, min(32, a.T - j0), tid);
+    };
+    StageRegs st;
+    const int j_first = (jlo / 32) * 32;
+    load_tile(st, j_first);
+    for (int j0 = j_first; j0 <= jhi; j0 += 32) {
         __syncthreads();   // the previous tile's reads are done
-        stage_rot192(Ks, a.k + ((size_t)b * a.T + j0) * krs + (size_t)g * kDqk, krs, nvalid, a.pos0 + j0, a.rt,
-                     tid, 64 * NW);
-        stage_rows128(Vs, a.v + ((size_t)b * a.T + j0) * vrs + (size_t)g * kDv, vrs, nvalid, tid, 64 * NW);
+        stage_store(st, Ks, Vs, a.pos0 + j0, a.rt, tid);
+        if (j0 + 32 <= jhi) load_tile(st, j0 + 32);
         __syncthreads();
         transpose32(KTs, Ks, RSTR, kDqk / 8, tid, 64 * NW);
         __syncthreads();
@@ -283,7 +358,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t QTs[kDqk * TSTR];
     __shared__ __attribute__((aligned(16))) uint16_t Os[32 * VSTR];
     __shared__ __attribute__((aligned(16))) uint16_t OTs[kDv * TSTR];
-    __shared__ float Ls[32], Ds[32];
+    __shared__ __attribute__((aligned(16))) float Ls[32], Ds[32];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int h2 = lane >> 5, l32 = lane & 31;
@@ -339,20 +414,35 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const int qhi = a.window > 0 ? min(a.T - 1, jb0 + 127 + a.window - 1) : a.T - 1;
     const int wq_hi = a.window > 0 ? jw0 + 31 + a.window - 1 : 0x7fffffff;
 
-    for (int hi = 0; hi < G; ++hi) {
-        const int head = g * G + hi;
-        for (int q0 = (qlo / 32) * 32; q0 <= qhi; q0 += 32) {
-            const int nvalid = min(32, a.T - q0);
+    // stages (query head, 32-query block), head-major; the next stage's rows are
+    // loaded into registers while this one is computed
+    const int q_first = (qlo / 32) * 32;
+    const int n_qb = (qhi - q_first) / 32 + 1;
+    const int n_stage = G * n_qb;
+    auto load_stage = [&](StageRegs &st, float &lv, float &dv_, int s_) {
+        const int head = g * G + s_ / n_qb, q0 = q_first + 32 * (s_ % n_qb);
+        const int nvalid = min(32, a.T - q0);
+        stage_load(st, a.q + ((size_t)b * a.T + q0) * qrs + (size_t)head * kDqk, qrs,
+                   a.dout + ((size_t)b * a.T + q0) * ors + (size_t)head * kDv, ors, nvalid, tid);
+        if (tid < 32) {
+            const bool ok = tid < nvalid;
+            lv = ok ? a.lse[((size_t)b * a.Hq + head) * a.T + q0 + tid] * kLog2e : kPosInf;
+            dv_ = ok ? a.D[((size_t)b * a.T + q0 + tid) * a.Hq + head] : 0.0f;
+        }
+    };
+    StageRegs st;
+    float st_l = 0.0f, st_d = 0.0f;
+    load_stage(st, st_l, st_d, 0);
+    for (int s_ = 0; s_ < n_stage; ++s_) {
+        const int q0 = q_first + 32 * (s_ % n_qb);
+        {
             __syncthreads();
-            stage_rot192(Qs, a.q + ((size_t)b * a.T + q0) * qrs + (size_t)head * kDqk, qrs, nvalid, a.pos0 + q0,
-                         a.rt, tid, 256);
-            stage_rows128(Os, a.dout + ((size_t)b * a.T + q0) * ors + (size_t)head * kDv, ors, nvalid, tid, 256);
+            stage_store(st, Qs, Os, a.pos0 + q0, a.rt, tid);
             if (tid < 32) {
-                const bool ok = tid < nvalid;
-                const size_t row = ((size_t)b * a.T + q0 + tid) * a.Hq + head;
-                Ls[tid] = ok ? a.lse[((size_t)b * a.Hq + head) * a.T + q0 + tid] * kLog2e : kPosInf;
-                Ds[tid] = ok ? a.D[row] : 0.0f;
+                Ls[tid] = st_l;
+                Ds[tid] = st_d;
             }
+            if (s_ + 1 < n_stage) load_stage(st, st_l, st_d, s_ + 1);
             __syncthreads();
             transpose32(QTs, Qs, RSTR, kDqk / 8, tid, 256);
             transpose32(OTs, Os, VSTR, kDv / 8, tid, 256);
@@ -376,15 +466,21 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 float p8[8], d8[8];
+                // the lane's 8 query rows are consecutive: their L and D in two 16-byte reads each
+                const float4 l0 = *reinterpret_cast<const float4 *>(Ls + 16 * s + 8 * h2);
+                const float4 l1 = *reinterpret_cast<const float4 *>(Ls + 16 * s + 8 * h2 + 4);
+                const float4 d0 = *reinterpret_cast<const float4 *>(Ds + 16 * s + 8 * h2);
+                const float4 d1 = *reinterpret_cast<const float4 *>(Ds + 16 * s + 8 * h2 + 4);
+                const float lrow[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+                const float drow[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
 #pragma unroll
                 for (int x = 0; x < 8; ++x) {
                     const int e = 8 * s + x;
-                    const int qr = 16 * s + 8 * h2 + x;
-                    const int q = q0 + qr;
+                    const int q = q0 + 16 * s + 8 * h2 + x;
                     const bool vis = jval && q < a.T && j <= q && q - j < win;
-                    const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], cl2, -Ls[qr])) : 0.0f;
+                    const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], cl2, -lrow[x])) : 0.0f;
                     p8[x] = p;
-                    d8[x] = p * (DP[e] * a.v_scale - Ds[qr]);
+                    d8[x] = p * (DP[e] * a.v_scale - drow[x]);
                 }
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
@@ -443,7 +539,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 size_t backward_workspace_bytes(int32_t B, int32_t T, int32_t Hq) {
-    return (size_t)2 * B * T * Hq * sizeof(float);
+    const size_t rows = (size_t)B * T * Hq;
+    return (rows + (rows + kPrepRows - 1) / kPrepRows * Hq) * sizeof(float);
 }
 
 hipError_t launch_backward(BwdArgs a, hipStream_t stream) {
@@ -453,7 +550,7 @@ hipError_t launch_backward(BwdArgs a, hipStream_t stream) {
     a.n_hgrp = G / 4;
     a.n_kblk = (a.T + 127) / 128;
     const int64_t rows = (int64_t)a.B * a.T * a.Hq;
-    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + kPrepRows - 1) / kPrepRows)), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.sinks) {

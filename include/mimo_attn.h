@@ -218,7 +218,8 @@ mimo_status mimo_attn_prefill_backward(const mimo_attn_cfg *cfg, const uint16_t 
                                        uint16_t *dk, uint16_t *dv, float *dsinks, void *ws, size_t ws_bytes,
                                        void *stream);
 
-/* Workspace bytes of mimo_attn_prefill_backward (two fp32 values per row and head). */
+/* Workspace bytes of mimo_attn_prefill_backward: one fp32 value per (token, query head) and
+ * one per query head for every 1024 of those. */
 size_t mimo_attn_backward_workspace_size(const mimo_attn_cfg *cfg, int32_t B, int32_t T);
 
 /* Element type of a paged KV cache. */
