@@ -27,6 +27,17 @@
 // (sink * log2 e, 1).
 #include "kernels.hpp"
 
+// One-token decode: at most 4 KV heads (waves) per workgroup, so that every
+// workgroup runs one wave per SIMD and the step ranges cover all CUs (on
+// sliding layers, 8 KV heads in one workgroup left half the CUs idle).
+#ifndef MIMO_DECODE_SPLIT_HEADS
+#define MIMO_DECODE_SPLIT_HEADS 1
+#endif
+// Steps whose loads are in flight per wave (2: the computed one and the next).
+#ifndef MIMO_DECODE_DEPTH
+#define MIMO_DECODE_DEPTH 2
+#endif
+
 namespace mimo {
 
 namespace {
@@ -199,7 +210,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
 // of the same KV head.  MAXT: workgroup size bound (512: eight KV-head waves,
 // two per SIMD; 256: up to four waves, one per SIMD with the whole register
 // file, for the tiles of multi-query decode).
-template <int NC, int MAXT, bool FP8, bool PAGED>
+template <int NC, int MAXT, bool FP8, bool PAGED, int DEPTH>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, MAXT), amdgpu_waves_per_eu(MAXT / 256, MAXT / 256)))
 void decode_partial_kernel(DecodeArgs a) {
     const int64_t wg = blockIdx.x;
@@ -444,16 +455,35 @@ void decode_partial_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int tt = 0; tt < 8; ++tt) O[t][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-            while (j0 < kend) {
-                int j1 = j0 + kStep;
-                if (j1 < kend) load(B, j1);
-                compute(A, j0);
-                j0 = j1;
-                if (j0 >= kend) break;
-                j1 = j0 + kStep;
-                if (j1 < kend) load(A, j1);
-                compute(B, j0);
-                j0 = j1;
+            if constexpr (DEPTH == 3) {
+                // three steps' loads in flight: the one computed and the next two
+                Buf C;
+                if (j0 + kStep < kend) load(B, j0 + kStep);
+                while (j0 < kend) {
+                    if (j0 + 2 * kStep < kend) load(C, j0 + 2 * kStep);
+                    compute(A, j0);
+                    j0 += kStep;
+                    if (j0 >= kend) break;
+                    if (j0 + 2 * kStep < kend) load(A, j0 + 2 * kStep);
+                    compute(B, j0);
+                    j0 += kStep;
+                    if (j0 >= kend) break;
+                    if (j0 + 2 * kStep < kend) load(B, j0 + 2 * kStep);
+                    compute(C, j0);
+                    j0 += kStep;
+                }
+            } else {
+                while (j0 < kend) {
+                    int j1 = j0 + kStep;
+                    if (j1 < kend) load(B, j1);
+                    compute(A, j0);
+                    j0 = j1;
+                    if (j0 >= kend) break;
+                    j1 = j0 + kStep;
+                    if (j1 < kend) load(A, j1);
+                    compute(B, j0);
+                    j0 = j1;
+                }
             }
         }
 
@@ -546,8 +576,9 @@ DecodeGeom decode_geometry(int32_t Hq, int32_t Hkv, int32_t n_q) {
     DecodeGeom m{};
     const int G = Hq / Hkv;
     const int tiles = (G * n_q + 15) / 16;
-    if (n_q == 1) {   // one tile per wave, one wave per KV head, every KV head in the workgroup
-        m.nc = 1; m.wph = 1; m.kvpw = Hkv;
+    if (n_q == 1) {   // one tile per wave, one wave per KV head
+        m.nc = 1; m.wph = 1; m.kvpw = MIMO_DECODE_SPLIT_HEADS ? (Hkv < 4 ? Hkv : 4) : Hkv;
+        while (Hkv % m.kvpw) --m.kvpw;
     } else {          // up to 2 tiles per wave, at most four waves per workgroup
         m.wph = (tiles + 1) / 2;
         m.nc = (tiles + m.wph - 1) / m.wph;
@@ -567,15 +598,15 @@ namespace {
 // workgroup on it, and the pieces of all sequences number < groups + S
 size_t decode_partial_slots(int32_t S, const DecodeGeom &m) { return (size_t)m.n_groups + (size_t)S; }
 
-template <int NC, int MAXT>
+template <int NC, int MAXT, int DEPTH = 2>
 void launch_partial(const DecodeArgs &a, const DecodeGeom &m, hipStream_t stream) {
     const dim3 grid(m.n_groups, m.n_hsub), block(m.threads);
     if (!a.table)
-        hipLaunchKernelGGL((decode_partial_kernel<NC, MAXT, false, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((decode_partial_kernel<NC, MAXT, false, false, DEPTH>), grid, block, 0, stream, a);
     else if (a.fp8)
-        hipLaunchKernelGGL((decode_partial_kernel<NC, MAXT, true, true>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((decode_partial_kernel<NC, MAXT, true, true, DEPTH>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((decode_partial_kernel<NC, MAXT, false, true>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((decode_partial_kernel<NC, MAXT, false, true, DEPTH>), grid, block, 0, stream, a);
 }
 
 }  // namespace
@@ -604,7 +635,10 @@ hipError_t launch_decode(DecodeArgs a, hipStream_t stream) {
     hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.n_q == 1) launch_partial<1, 512>(a, m, stream);
+    if (a.n_q == 1) {
+        if (m.threads <= 256) launch_partial<1, 256, MIMO_DECODE_DEPTH>(a, m, stream);
+        else launch_partial<1, 512>(a, m, stream);
+    }
     else if (m.nc == 1) launch_partial<1, 256>(a, m, stream);
     else launch_partial<2, 256>(a, m, stream);
     e = hipGetLastError();
