@@ -37,6 +37,11 @@
 #ifndef MIMO_DECODE_DEPTH
 #define MIMO_DECODE_DEPTH 2
 #endif
+// Multi-query decode with more than 2 column tiles per KV head: its 2 or 4
+// waves read each step from HBM once, through LDS (0: each wave reads it).
+#ifndef MIMO_DECODE_SHARED
+#define MIMO_DECODE_SHARED 1
+#endif
 
 namespace mimo {
 
@@ -210,9 +215,15 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
 // of the same KV head.  MAXT: workgroup size bound (512: eight KV-head waves,
 // two per SIMD; 256: up to four waves, one per SIMD with the whole register
 // file, for the tiles of multi-query decode).
-template <int NC, int MAXT, bool FP8, bool PAGED, int DEPTH>
+template <int NC, int MAXT, bool FP8, bool PAGED, int DEPTH, int SW = 0>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, MAXT), amdgpu_waves_per_eu(MAXT / 256, MAXT / 256)))
 void decode_partial_kernel(DecodeArgs a) {
+    // SW > 0: the workgroup is the SW waves of one KV head; each step's K/V rows
+    // are read from HBM once, by all of them, staged in LDS and read from there
+    constexpr int kKRowB = FP8 ? kDqk : 2 * kDqk;        // bytes of one K / V row
+    constexpr int kVRowB = FP8 ? kDv : 2 * kDv;
+    constexpr int kStepB = kStep * (kKRowB + kVRowB);
+    __shared__ __attribute__((aligned(16))) uint8_t sring[SW > 0 ? 2 * kStepB : 16];
     const int64_t wg = blockIdx.x;
     const int64_t Ts = a.plan_start[a.S];
     const int lo = a.plan_wg_seq[wg];   // meaningful only below the groups used
@@ -240,7 +251,6 @@ void decode_partial_kernel(DecodeArgs a) {
     // row strides of the caches in elements (bf16) or bytes (fp8): one element each
     const size_t krs = (size_t)a.Hkv * kDqk, vrs = (size_t)a.Hkv * kDv;
     const int win = a.window > 0 ? a.window : 0x7fffffff;
-    const bool always_mask = a.window > 0 || nq > 1;
     constexpr bool paged = PAGED;
     const int bmask = (1 << a.block_shift) - 1;
     using Buf = StepBuf<FP8>;
@@ -310,7 +320,10 @@ void decode_partial_kernel(DecodeArgs a) {
         auto compute = [&](Buf &bf, int j0) {
             // the lane's 8 keys are j0 + 16*sb + 4*lg + i (rows of its S^T registers and
             // of its V loads); d = how many positions each lies before the newest query
-            const bool masked = always_mask || j0 + kStep > kend;
+            // unmasked: a global layer's step wholly inside this piece, before the
+            // newest n_q - 1 positions, in a cache whose slot j holds position j
+            const bool masked = a.window > 0 || j0 + kStep > kend ||
+                                (nq > 1 && (!(paged || p < a.cap) || (int64_t)j0 + kStep > p - nq + 2));
             // K operands in bf16 (fp8 codes widened once per step)
             u32x4 kop8[2][FP8 ? 6 : 1];
             if constexpr (FP8) {
@@ -409,10 +422,7 @@ void decode_partial_kernel(DecodeArgs a) {
             }
         };
 
-        {
-            Buf A, B;
-            int j0 = kbeg;
-            if (j0 < kend) load(A, j0);   // first step's loads go out before q's
+        auto init_q = [&]() {
             // ---- q (B operand) of each tile, in the contraction order of the K operand:
             // bf16: slot (ch, lg, e) is dim 32*ch + 8*lg + e, so chunks 0 and 1 of a lane
             // are rotate-half partners (dims i and i+32); fp8: slot (ch = 2c+h, lg, e) is
@@ -455,6 +465,113 @@ void decode_partial_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int tt = 0; tt < 8; ++tt) O[t][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
+        };
+
+        if constexpr (SW > 0) {
+            // Staging: per step, 32 K rows and 32 V rows cut into 16-byte (bf16) or
+            // 8-byte (fp8) chunks, 768 of K and 512 of V, spread evenly over the
+            // workgroup; each thread holds its chunks of the next RS steps in
+            // registers, so RS steps per KV head are in flight from HBM.
+            constexpr int NT = 64 * SW;
+            constexpr int KCH = 768, TOT = 1280, PER = TOT / NT, KPER = KCH / NT;
+            static_assert(TOT % NT == 0 && KCH % NT == 0, "chunk split");
+            constexpr int CB = FP8 ? 8 : 16;
+            constexpr int RS = SW == 2 ? 2 : 3;
+            using Chunk = typename std::conditional<FP8, u32x2, u32x4>::type;
+            const int tid = threadIdx.x;
+            const uint8_t *kb8 = static_cast<const uint8_t *>(a.k_cache) + (size_t)g * kKRowB;
+            const uint8_t *vb8 = static_cast<const uint8_t *>(a.v_cache) + (size_t)g * kVRowB;
+            const size_t krb = (size_t)a.Hkv * kKRowB, vrb = (size_t)a.Hkv * kVRowB;
+            Chunk rs[RS][PER];
+            auto gload = [&](Chunk (&r)[PER], int j0) {
+                size_t blk_row = 0;
+                if constexpr (PAGED) {
+                    int blk = btab[j0 >> a.block_shift];
+                    blk = blk < 0 ? 0 : (blk >= a.n_blocks ? a.n_blocks - 1 : blk);
+                    blk_row = (size_t)blk << a.block_shift;
+                }
+                auto row = [&](int j) -> size_t {
+                    return paged ? blk_row + (size_t)(j & bmask) : seq_rows + (size_t)min(j, a.cap - 1);
+                };
+#pragma unroll
+                for (int i = 0; i < PER; ++i) {
+                    const int u = tid + i * NT;
+                    if (i < KPER) r[i] = *reinterpret_cast<const Chunk *>(kb8 + row(j0 + u / 24) * krb + CB * (u % 24));
+                    else r[i] = *reinterpret_cast<const Chunk *>(vb8 + row(j0 + (u - KCH) / 16) * vrb + CB * ((u - KCH) % 16));
+                }
+            };
+            // LDS step image: K rows of kKRowB bytes, their 16-byte chunks XOR-swizzled
+            // by row (conflict-free operand reads), then V rows of kVRowB bytes
+            auto kslot = [](int row, int c16) {
+                return FP8 ? row * kKRowB + 16 * (c16 ^ ((row >> 2) & 3)) : row * kKRowB + 16 * (c16 ^ ((row >> 1) & 7));
+            };
+            auto lstore = [&](const Chunk (&r)[PER], int buf) {
+                uint8_t *base = sring + buf * kStepB;
+#pragma unroll
+                for (int i = 0; i < PER; ++i) {
+                    const int u = tid + i * NT;
+                    if (i < KPER) {
+                        const int row = u / 24, c = u % 24;
+                        const int off = FP8 ? kslot(row, c >> 1) + 8 * (c & 1) : kslot(row, c);
+                        *reinterpret_cast<Chunk *>(base + off) = r[i];
+                    } else {
+                        const int row = (u - KCH) / 16, c = (u - KCH) % 16;
+                        *reinterpret_cast<Chunk *>(base + kStep * kKRowB + row * kVRowB + CB * c) = r[i];
+                    }
+                }
+            };
+            // the operand registers of a step, as the per-wave loads would give them
+            auto lfetch = [&](Buf &bf, int buf) {
+                const uint8_t *base = sring + buf * kStepB;
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb) {
+                    const int row = 16 * sb + r16;
+#pragma unroll
+                    for (int ch = 0; ch < (FP8 ? 3 : 6); ++ch)
+                        bf.k[sb][ch] = *reinterpret_cast<const u32x4 *>(base + kslot(row, 4 * ch + lg));
+                }
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int row = 16 * (jj >> 2) + 4 * lg + (jj & 3);
+                    bf.v[jj] = *reinterpret_cast<const std::remove_reference_t<decltype(bf.v[0])> *>(base + kStep * kKRowB + row * kVRowB + CB * r16);
+                }
+            };
+            // (loads past the last step re-read the last step, and their stores land in
+            // a buffer nobody reads: no load sits under a data-dependent branch, which
+            // keeps the compiler's memory waits per register set)
+            const int nsteps = (kend - kbeg + kStep - 1) / kStep;   // >= 1
+            auto step_j0 = [&](int i) { return kbeg + min(i, nsteps - 1) * kStep; };
+            gload(rs[0], step_j0(0));   // first step's loads go out before q's
+            init_q();
+#pragma unroll
+            for (int i = 1; i < RS; ++i) gload(rs[i], step_j0(i));
+            lstore(rs[0], 0);
+            gload(rs[0], step_j0(RS));
+            __syncthreads();
+            // step i: computed from LDS buffer i & 1; its successor is stored to the
+            // other buffer from register set (i + 1) % RS, which then loads step i + 1 + RS
+            auto phase = [&](int i, int ph) {
+                Buf bf;
+                lfetch(bf, i & 1);
+                compute(bf, kbeg + i * kStep);
+                lstore(rs[(ph + 1) % RS], (i + 1) & 1);
+                gload(rs[(ph + 1) % RS], step_j0(i + 1 + RS));
+                __syncthreads();
+            };
+            // whole rounds of RS steps without branches around the loads, then the rest
+            int i0 = 0;
+            for (; i0 + RS <= nsteps; i0 += RS) {
+#pragma unroll
+                for (int ph = 0; ph < RS; ++ph) phase(i0 + ph, ph);
+            }
+#pragma unroll
+            for (int ph = 0; ph < RS - 1; ++ph)
+                if (i0 + ph < nsteps) phase(i0 + ph, ph);
+        } else {
+            Buf A, B;
+            int j0 = kbeg;
+            if (j0 < kend) load(A, j0);   // first step's loads go out before q's
+            init_q();
             if constexpr (DEPTH == 3) {
                 // three steps' loads in flight: the one computed and the next two
                 Buf C;
@@ -579,11 +696,15 @@ DecodeGeom decode_geometry(int32_t Hq, int32_t Hkv, int32_t n_q) {
     if (n_q == 1) {   // one tile per wave, one wave per KV head
         m.nc = 1; m.wph = 1; m.kvpw = MIMO_DECODE_SPLIT_HEADS ? (Hkv < 4 ? Hkv : 4) : Hkv;
         while (Hkv % m.kvpw) --m.kvpw;
-    } else {          // up to 2 tiles per wave, at most four waves per workgroup
+    } else if (tiles <= 2 || !MIMO_DECODE_SHARED) {   // up to 2 tiles per wave, at most four waves per workgroup
         m.wph = (tiles + 1) / 2;
         m.nc = (tiles + m.wph - 1) / m.wph;
         m.kvpw = m.wph >= 4 ? 1 : 4 / m.wph;
         while (Hkv % m.kvpw) --m.kvpw;
+    } else {          // 2 tiles per wave; the 2 or 4 waves of a KV head share its steps through LDS
+        m.nc = 2;
+        m.wph = tiles <= 4 ? 2 : 4;
+        m.kvpw = 1;
     }
     m.n_hsub = Hkv / m.kvpw;
     m.threads = 64 * m.kvpw * m.wph;
@@ -597,6 +718,17 @@ namespace {
 // partials: every sequence shared by several workgroups has one piece per
 // workgroup on it, and the pieces of all sequences number < groups + S
 size_t decode_partial_slots(int32_t S, const DecodeGeom &m) { return (size_t)m.n_groups + (size_t)S; }
+
+template <int SW>
+void launch_shared(const DecodeArgs &a, const DecodeGeom &m, hipStream_t stream) {
+    const dim3 grid(m.n_groups, m.n_hsub), block(64 * SW);
+    if (!a.table)
+        hipLaunchKernelGGL((decode_partial_kernel<2, 256, false, false, 2, SW>), grid, block, 0, stream, a);
+    else if (a.fp8)
+        hipLaunchKernelGGL((decode_partial_kernel<2, 256, true, true, 2, SW>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((decode_partial_kernel<2, 256, false, true, 2, SW>), grid, block, 0, stream, a);
+}
 
 template <int NC, int MAXT, int DEPTH = 2>
 void launch_partial(const DecodeArgs &a, const DecodeGeom &m, hipStream_t stream) {
@@ -639,6 +771,8 @@ hipError_t launch_decode(DecodeArgs a, hipStream_t stream) {
         if (m.threads <= 256) launch_partial<1, 256, MIMO_DECODE_DEPTH>(a, m, stream);
         else launch_partial<1, 512>(a, m, stream);
     }
+    else if (m.wph == 2 && m.kvpw == 1) launch_shared<2>(a, m, stream);
+    else if (m.wph == 4 && m.kvpw == 1) launch_shared<4>(a, m, stream);
     else if (m.nc == 1) launch_partial<1, 256>(a, m, stream);
     else launch_partial<2, 256>(a, m, stream);
     e = hipGetLastError();
