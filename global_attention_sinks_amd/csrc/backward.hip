@@ -215,11 +215,14 @@ __global__ __launch_bounds__(256) void bwd_sink_kernel(BwdArgs a) {
 }
 
 // ---- dq: 4 heads x 32 queries per workgroup, 32-key tiles
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void bwd_dq_kernel(BwdArgs a) {
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(BwdArgs a) {
     constexpr int NW = 4;
     __shared__ __attribute__((aligned(16))) uint16_t Ks[32 * RSTR];
     __shared__ __attribute__((aligned(16))) uint16_t KTs[kDqk * TSTR];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[32 * VSTR];
+    // each wave's dO rows: the B operand of dP^T, parked in LDS (each lane reads
+    // back only what it wrote) to keep the kernel at two waves per SIMD
+    __shared__ __attribute__((aligned(16))) uint16_t DOs[NW][32 * VSTR];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int h2 = lane >> 5, l32 = lane & 31;
@@ -241,6 +244,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void bwd_dq_ke
     // per lane: Q~ (B operand of S^T = K~ Q~^T, dims 96*h2 + 8*s), dO (B operand of dP^T = V dO^T)
     const size_t qrow = ((size_t)b * a.T + t) * a.Hq + head;
     u32x4 qf[12], dof[8];
+    uint16_t *dos = DOs[w] + l32 * VSTR + 64 * h2;
     float L2 = kPosInf, Dq = 0.0f;
     if (tval) {
         const uint16_t *src = a.q + qrow * kDqk + 96 * h2;
@@ -261,6 +265,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void bwd_dq_ke
 #pragma unroll
         for (int s = 0; s < 8; ++s) dof[s] = u32x4{0, 0, 0, 0};
     }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) *reinterpret_cast<u32x4 *>(dos + 8 * s) = dof[s];
 
     f32x16 acc[6];
 #pragma unroll
@@ -278,8 +284,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void bwd_dq_ke
         stage_load(st, a.k + ((size_t)b * a.T + j0) * krs + (size_t)g * kDqk, krs,
                    a.v + ((size_t)b * a.T + j0) * vrs + (size_t)g * kDv, vrs, min(32, a.T - j0), tid);
     };
-    StageRegs st;
     const int j_first = (jlo / 32) * 32;
+    StageRegs st;
     load_tile(st, j_first);
     for (int j0 = j_first; j0 <= jhi; j0 += 32) {
         __syncthreads();   // the previous tile's reads are done
@@ -298,7 +304,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void bwd_dq_ke
 #pragma unroll
         for (int s = 0; s < 12; ++s) S = mfma32(lds128(Ks + prow * RSTR + 96 * h2 + 8 * s), qf[s], S);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) DP = mfma32(lds128(Vs + prow * VSTR + 64 * h2 + 8 * s), dof[s], DP);
+        for (int s = 0; s < 8; ++s) DP = mfma32(lds128(Vs + prow * VSTR + 64 * h2 + 8 * s), lds128(dos + 8 * s), DP);
 
         // element e: key j0 + 16*(e>>3) + 8*h2 + (e&7), query t
         u32x4 dsb[2];
@@ -354,11 +360,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void bwd_dq_ke
 // ---- dk, dv: 128 keys of one KV head per workgroup (one wave per 32 keys)
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t Qs[32 * RSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t QTs[kDqk * TSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t Os[32 * VSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t OTs[kDv * TSTR];
-    __shared__ __attribute__((aligned(16))) float Ls[32], Ds[32];
+    // two stage buffers: one is computed on while the next is written
+    __shared__ __attribute__((aligned(16))) uint16_t Qsb[2][32 * RSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t QTsb[2][kDqk * TSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t Osb[2][32 * VSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t OTsb[2][kDv * TSTR];
+    __shared__ __attribute__((aligned(16))) float Lsb[2][32], Dsb[2][32];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int h2 = lane >> 5, l32 = lane & 31;
@@ -419,36 +426,79 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const int q_first = (qlo / 32) * 32;
     const int n_qb = (qhi - q_first) / 32 + 1;
     const int n_stage = G * n_qb;
-    auto load_stage = [&](StageRegs &st, float &lv, float &dv_, int s_) {
+    // Staging of a stage (32 query rows of one head): thread u < 64 takes rows
+    // (2*(u%16), +1) x rotating chunks (u/16, u/16 + 4) of Q; every thread takes
+    // rows (2*(t%16), +1) x one pass-through Q chunk 8 + t/16 and x dO chunk t/16.
+    // Holding both rows of a pair, a thread writes its chunks row-major and, two
+    // rows per dword, transposed: no LDS-to-LDS transpose pass.
+    struct DkStage {
+        u32x4 rq[2][2];   // [row of pair][chunk c, c + 4], threads < 64
+        u32x4 pq[2];      // [row of pair] pass-through Q chunk
+        u32x4 po[2];      // [row of pair] dO chunk
+        float lv, dv;     // L and D of query row tid (threads < 32)
+    };
+    const int rp = tid & 15, rc = tid >> 4;
+    auto load_stage = [&](DkStage &st, int s_) {
+        s_ = min(s_, n_stage - 1);   // past the last stage: re-read it (unused)
         const int head = g * G + s_ / n_qb, q0 = q_first + 32 * (s_ % n_qb);
-        const int nvalid = min(32, a.T - q0);
-        stage_load(st, a.q + ((size_t)b * a.T + q0) * qrs + (size_t)head * kDqk, qrs,
-                   a.dout + ((size_t)b * a.T + q0) * ors + (size_t)head * kDv, ors, nvalid, tid);
+        const int last = min(32, a.T - q0) - 1;
+        const uint16_t *qb_ = a.q + ((size_t)b * a.T + q0) * qrs + (size_t)head * kDqk;
+        const uint16_t *ob_ = a.dout + ((size_t)b * a.T + q0) * ors + (size_t)head * kDv;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            // rows past the end re-read the last valid row: masked out of every product
+            const int row = min(2 * rp + i, last);
+            if (tid < 64) {
+                st.rq[i][0] = ldg128(qb_ + row * qrs + 8 * rc);
+                st.rq[i][1] = ldg128(qb_ + row * qrs + 8 * rc + 32);
+            }
+            st.pq[i] = ldg128(qb_ + row * qrs + 8 * (8 + rc));
+            st.po[i] = ldg128(ob_ + row * ors + 8 * rc);
+        }
         if (tid < 32) {
-            const bool ok = tid < nvalid;
-            lv = ok ? a.lse[((size_t)b * a.Hq + head) * a.T + q0 + tid] * kLog2e : kPosInf;
-            dv_ = ok ? a.D[((size_t)b * a.T + q0 + tid) * a.Hq + head] : 0.0f;
+            const bool ok = tid <= last;
+            st.lv = ok ? a.lse[((size_t)b * a.Hq + head) * a.T + q0 + tid] * kLog2e : kPosInf;
+            st.dv = ok ? a.D[((size_t)b * a.T + q0 + tid) * a.Hq + head] : 0.0f;
         }
     };
-    StageRegs st;
-    float st_l = 0.0f, st_d = 0.0f;
-    load_stage(st, st_l, st_d, 0);
+    // chunk x0 (row 2*rp) and x1 (row 2*rp + 1) of 8 columns starting at col:
+    // row-major into d (row stride sstr), transposed into dT (column-major pairs)
+    auto put2 = [&](uint16_t *d, uint16_t *dT, int sstr, int col, const u32x4 &x0, const u32x4 &x1) {
+        *reinterpret_cast<u32x4 *>(d + (2 * rp) * sstr + col) = x0;
+        *reinterpret_cast<u32x4 *>(d + (2 * rp + 1) * sstr + col) = x1;
+#pragma unroll
+        for (int dd = 0; dd < 8; ++dd) {
+            const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
+            *reinterpret_cast<uint32_t *>(dT + (col + dd) * TSTR + 2 * rp) = __builtin_amdgcn_perm(x1[dd >> 1], x0[dd >> 1], sel);
+        }
+    };
+    auto store_stage = [&](DkStage &st, int s_, int buf) {
+        const int q0 = q_first + 32 * (s_ % n_qb);
+        if (tid < 64) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) rope_rotate8(st.rq[i][0], st.rq[i][1], a.rt, 8 * rc, a.pos0 + q0 + 2 * rp + i);
+            put2(Qsb[buf], QTsb[buf], RSTR, 8 * rc, st.rq[0][0], st.rq[1][0]);
+            put2(Qsb[buf], QTsb[buf], RSTR, 8 * rc + 32, st.rq[0][1], st.rq[1][1]);
+        }
+        put2(Qsb[buf], QTsb[buf], RSTR, 8 * (8 + rc), st.pq[0], st.pq[1]);
+        put2(Osb[buf], OTsb[buf], VSTR, 8 * rc, st.po[0], st.po[1]);
+        if (tid < 32) {
+            Lsb[buf][tid] = st.lv;
+            Dsb[buf][tid] = st.dv;
+        }
+    };
+    DkStage st;
+    load_stage(st, 0);
+    store_stage(st, 0, 0);
+    load_stage(st, 1);
+    __syncthreads();
     for (int s_ = 0; s_ < n_stage; ++s_) {
         const int q0 = q_first + 32 * (s_ % n_qb);
-        {
-            __syncthreads();
-            stage_store(st, Qs, Os, a.pos0 + q0, a.rt, tid);
-            if (tid < 32) {
-                Ls[tid] = st_l;
-                Ds[tid] = st_d;
-            }
-            if (s_ + 1 < n_stage) load_stage(st, st_l, st_d, s_ + 1);
-            __syncthreads();
-            transpose32(QTs, Qs, RSTR, kDqk / 8, tid, 256);
-            transpose32(OTs, Os, VSTR, kDv / 8, tid, 256);
-            __syncthreads();
-            // does this wave's key range meet the block's queries? (wave-uniform)
-            if (jw0 > q0 + 31 || q0 > wq_hi) continue;
+        const int buf = s_ & 1;
+        const uint16_t *Qs = Qsb[buf], *QTs = QTsb[buf], *Os = Osb[buf], *OTs = OTsb[buf];
+        const float *Ls = Lsb[buf], *Ds = Dsb[buf];
+        // does this wave's key range meet the block's queries? (wave-uniform)
+        if (!(jw0 > q0 + 31 || q0 > wq_hi)) {
 
             f32x16 S, DP;
 #pragma unroll
@@ -500,6 +550,10 @@ void bwd_dkdv_kernel(BwdArgs a) {
                 for (int s = 0; s < 2; ++s)
                     dK[mb] = mfma32(lds128(QTs + (32 * mb + l32) * TSTR + 16 * s + 8 * h2), dsb[s], dK[mb]);
         }
+        // the next stage goes to the other buffer, read last in the previous stage
+        store_stage(st, s_ + 1 < n_stage ? s_ + 1 : s_, buf ^ 1);
+        load_stage(st, s_ + 2);
+        __syncthreads();
     }
 
     // ---- epilogue: dK[mb][e] / dV[mb][e] hold dim 32*mb + 8*(e/4) + 4*h2 + (e%4) of key j
