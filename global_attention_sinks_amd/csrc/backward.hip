@@ -19,10 +19,13 @@
 //                      wave per 32 keys, the keys' K~ and V held in registers);
 //                      it walks every query head of the group and every 32-query
 //                      block that sees its keys (Q~, Q~^T, dO, dO^T staged in
-//                      LDS) and accumulates dK~^T = Q~^T dS and dV^T = dO^T P
+//                      LDS, double-buffered) and accumulates dK~^T = Q~^T dS
+//                      and dV^T = dO^T P
 // Both contractions reuse the forward's layout trick: the A-operand rows of the
 // first product are read with bits 2 and 3 of the row index swapped, so each
-// lane's accumulators are directly the B operand of the second product.
+// lane's accumulators are directly the B operand of the second product.  The
+// dk/dv stages are written transposed straight from registers: a staging
+// thread holds both rows of a row pair and stores each column pair as a dword.
 // Nothing is accumulated across workgroups, so the results are deterministic.
 #include "kernels.hpp"
 
@@ -31,7 +34,6 @@ namespace mimo {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kNegInf = -__builtin_inff();
 constexpr float kPosInf = __builtin_inff();
 constexpr int RSTR = kDqk + 8;   // LDS row stride of a 192-dim tile (bf16)
 constexpr int VSTR = kDv + 8;    // LDS row stride of a 128-dim tile
@@ -43,39 +45,6 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 }
 
 __device__ __forceinline__ u32x4 lds128(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
-
-// Stage 32 rows of 192 dims (q or k, unrotated in memory) into LDS rotated at
-// positions pos0 + row: 128 rotating units (row, 4 pairs of 8-dim chunks) and
-// 512 pass-through units.  Rows >= nvalid are zero.
-__device__ __forceinline__ void stage_rot192(uint16_t *dst, const uint16_t *src, size_t row_stride, int nvalid,
-                                             int64_t pos0, const RopeTurns &rt, int tid, int nthreads) {
-    for (int u = tid; u < 32 * 4; u += nthreads) {
-        const int row = u >> 2, cc = u & 3;
-        u32x4 x = u32x4{0, 0, 0, 0}, y = u32x4{0, 0, 0, 0};
-        if (row < nvalid) {
-            x = ldg128(src + row * row_stride + 8 * cc);
-            y = ldg128(src + row * row_stride + 8 * cc + 32);
-            rope_rotate8(x, y, rt, 8 * cc, pos0 + row);
-        }
-        *reinterpret_cast<u32x4 *>(dst + row * RSTR + 8 * cc) = x;
-        *reinterpret_cast<u32x4 *>(dst + row * RSTR + 8 * cc + 32) = y;
-    }
-    for (int u = tid; u < 32 * 16; u += nthreads) {
-        const int row = u >> 4, c = 8 + (u & 15);
-        const u32x4 x = row < nvalid ? ldg128(src + row * row_stride + 8 * c) : u32x4{0, 0, 0, 0};
-        *reinterpret_cast<u32x4 *>(dst + row * RSTR + 8 * c) = x;
-    }
-}
-
-// Stage 32 rows of 128 dims (v or dO) into LDS as they are.
-__device__ __forceinline__ void stage_rows128(uint16_t *dst, const uint16_t *src, size_t row_stride, int nvalid,
-                                              int tid, int nthreads) {
-    for (int u = tid; u < 32 * 16; u += nthreads) {
-        const int row = u >> 4, c = u & 15;
-        const u32x4 x = row < nvalid ? ldg128(src + row * row_stride + 8 * c) : u32x4{0, 0, 0, 0};
-        *reinterpret_cast<u32x4 *>(dst + row * VSTR + 8 * c) = x;
-    }
-}
 
 // Transpose a staged 32-row tile (row stride sstr, nch chunks of 8 columns) into
 // dst[col][row] (row stride TSTR): each unit takes two rows x 8 columns and
@@ -163,7 +132,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
     const int tid = threadIdx.x, sub = tid & 15, grp = tid >> 4;   // 16 groups of 16 lanes
     const int64_t n = (int64_t)a.B * a.T * a.Hq;
     const int64_t r0 = (int64_t)blockIdx.x * kPrepRows;
-#pragma unroll 8
     for (int i = grp; i < kPrepRows; i += 16) {
         const int64_t r = r0 + i;                                    // ((b * T) + t) * Hq + h
         float acc = 0.0f;
@@ -379,7 +347,6 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const int j = jw0 + l32;
     const bool jval = j < a.T;
     const int G = a.Hq / a.Hkv;
-    const size_t krs = (size_t)a.Hkv * kDqk, vrs = (size_t)a.Hkv * kDv;
     const size_t qrs = (size_t)a.Hq * kDqk, ors = (size_t)a.Hq * kDv;
 
     // per lane: K~ (B operand of S = Q~ K~^T), V (B operand of dP = dO V^T) of key j
