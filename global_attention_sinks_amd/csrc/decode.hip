@@ -42,6 +42,11 @@
 #ifndef MIMO_DECODE_SHARED
 #define MIMO_DECODE_SHARED 1
 #endif
+// Short caches (sliding rings, windowed paged caches) decoded one workgroup per
+// (sequence, KV head) without the split (0: always split).
+#ifndef MIMO_DECODE_DIRECT
+#define MIMO_DECODE_DIRECT 1
+#endif
 
 namespace mimo {
 
@@ -225,11 +230,24 @@ void decode_partial_kernel(DecodeArgs a) {
     constexpr int kStepB = kStep * (kKRowB + kVRowB);
     __shared__ __attribute__((aligned(16))) uint8_t sring[SW > 0 ? 2 * kStepB : 16];
     const int64_t wg = blockIdx.x;
-    const int64_t Ts = a.plan_start[a.S];
-    const int lo = a.plan_wg_seq[wg];   // meaningful only below the groups used
-    const int64_t ng = groups_used(Ts, a.n_groups);
-    if (wg >= ng) return;
-    const int64_t r_lo = wg * Ts / ng, r_hi = (wg + 1) * Ts / ng;
+    // step range of the workgroup: its share of the planned line, or (direct) the
+    // whole of sequence blockIdx.x
+    int lo, s_end;
+    int64_t r_lo, r_hi;
+    if (a.direct) {
+        lo = (int)wg;
+        s_end = lo + 1;
+        r_lo = 0;
+        r_hi = INT64_MAX;
+    } else {
+        const int64_t Ts = a.plan_start[a.S];
+        lo = a.plan_wg_seq[wg];   // meaningful only below the groups used
+        const int64_t ng = groups_used(Ts, a.n_groups);
+        if (wg >= ng) return;
+        r_lo = wg * Ts / ng;
+        r_hi = (wg + 1) * Ts / ng;
+        s_end = a.S;
+    }
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int gl = w / a.wph, sub = w - gl * a.wph;
@@ -260,13 +278,19 @@ void decode_partial_kernel(DecodeArgs a) {
     const uint8_t *k8 = static_cast<const uint8_t *>(a.k_cache) + (size_t)g * kDqk + 16 * lg;
     const uint8_t *v8 = static_cast<const uint8_t *>(a.v_cache) + (size_t)g * kDv + 8 * r16;
 
-    for (int s = lo; s < a.S; ++s) {
-        const int64_t st0 = a.plan_start[s];
-        if (st0 >= r_hi) break;
-        const int64_t st1 = a.plan_start[s + 1];
+    for (int s = lo; s < s_end; ++s) {
+        int64_t st0 = 0, st1;
+        if (a.direct) {
+            // a sequence without slots still gets its (zero) output written below
+            st1 = a.pos[s] >= 0 ? steps_of(a, a.pos[s]) : 0;
+        } else {
+            st0 = a.plan_start[s];
+            if (st0 >= r_hi) break;
+            st1 = a.plan_start[s + 1];
+        }
         const int64_t seg_lo = st0 > r_lo ? st0 : r_lo;
         const int64_t seg_hi = st1 < r_hi ? st1 : r_hi;
-        if (seg_lo >= seg_hi) continue;
+        if (seg_lo >= seg_hi && !a.direct) continue;
 
         const int64_t p = a.pos[s];   // newest query's position (>= 0: the sequence has steps)
         int jlo, n;
@@ -606,7 +630,7 @@ void decode_partial_kernel(DecodeArgs a) {
 
         // ---- this piece: lane (lg, r16) holds, for each i, dv [32*lg + 8*i, +8) of
         // its column in O[t][0..7][i]
-        const int cover = a.plan_cover[s];
+        const int cover = a.direct ? 1 : a.plan_cover[s];
 #pragma unroll
         for (int t = 0; t < NC; ++t) {
             float lt = sum_xor16(l_run[t]);
@@ -750,9 +774,43 @@ size_t decode_workspace_bytes(int32_t S, int32_t Hq, int32_t Hkv, int32_t n_q) {
     return parts + plan;
 }
 
+// Direct mode: a cache whose sequences read at most kDirectMaxSteps steps (a
+// sliding layer's ring, or a windowed paged cache) is walked one workgroup per
+// (sequence, KV head), each writing its output itself: no plan, no partials, no
+// combine.  Splitting such short sequences only added two launches and a merge.
+constexpr int kDirectMaxSteps = 8;
+
+static bool decode_direct(const DecodeArgs &a, const DecodeGeom &m) {
+    if (m.wph != 1 || MIMO_DECODE_DIRECT == 0) return false;
+    int64_t steps;
+    if (a.table) {
+        if (a.window <= 0) return false;
+        steps = (a.window + a.n_q - 2 + kStep - 1) / kStep + 1;   // 32-aligned start of the oldest window
+    } else {
+        steps = (a.cap + kStep - 1) / kStep;
+    }
+    return steps <= kDirectMaxSteps;
+}
+
 hipError_t launch_decode(DecodeArgs a, hipStream_t stream) {
     if (a.Hkv < 1 || a.Hkv > 8 || a.n_q < 1 || a.Hq / a.Hkv * a.n_q > 128) return hipErrorInvalidValue;
-    const DecodeGeom m = decode_geometry(a.Hq, a.Hkv, a.n_q);
+    DecodeGeom m = decode_geometry(a.Hq, a.Hkv, a.n_q);
+    if (decode_direct(a, m)) {
+        if (a.S == 0) return hipSuccess;
+        // one wave (one KV head) per workgroup: S * Hkv workgroups
+        a.direct = 1;
+        a.wph = 1;
+        a.kvpw = 1;
+        a.n_groups = a.S;
+        m.kvpw = 1;
+        m.n_hsub = a.Hkv;
+        m.threads = 64;
+        m.n_groups = a.S;
+        if (m.nc == 1) launch_partial<1, 256>(a, m, stream);
+        else launch_partial<2, 256>(a, m, stream);
+        return hipGetLastError();
+    }
+    a.direct = 0;
     a.n_groups = m.n_groups;
     a.wph = m.wph;
     a.kvpw = m.kvpw;

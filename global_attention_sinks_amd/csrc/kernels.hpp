@@ -101,6 +101,7 @@ struct DecodeArgs {
     int32_t max_blocks, block_shift, n_blocks;
     int32_t fp8;                   // pools hold fp8 e4m3 codes (scales folded into scale_log2, v_scale)
     int32_t n_groups, wph, kvpw;   // filled by the launcher
+    int32_t direct;                // 1: workgroup x = sequence x, all its steps, no plan / combine
     float scale_log2, v_scale;
     RopeTurns rt;
 };
