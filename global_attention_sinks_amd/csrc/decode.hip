@@ -88,18 +88,15 @@ __device__ __forceinline__ int64_t steps_of(const DecodeArgs &a, int64_t p) {
     return (hi - lo + kStep - 1) / kStep;
 }
 
-// 8 fp8 e4m3 codes (two dwords, code e in byte e) -> 8 bf16 (exact: every e4m3
-// value is a bf16 value)
+// 8 fp8 e4m3 codes (two dwords, code e in byte e) -> 8 bf16, two codes per
+// v_cvt_scalef32_pk_bf16_fp8 at scale 1 (exact: every e4m3 value is a bf16 value;
+// checked on all 256 codes against the format's definition)
 __device__ __forceinline__ u32x4 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
     u32x4 r;
-    const auto a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
-    const auto a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
-    const auto b0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
-    const auto b1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
-    r[0] = pack_bf16(a0[0], a0[1]);
-    r[1] = pack_bf16(a1[0], a1[1]);
-    r[2] = pack_bf16(b0[0], b0[1]);
-    r[3] = pack_bf16(b1[0], b1[1]);
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
     return r;
 }
 
