@@ -37,6 +37,11 @@
 #ifndef MIMO_DECODE_DEPTH
 #define MIMO_DECODE_DEPTH 2
 #endif
+// fp8 steps are half the bytes of bf16 ones: one-token fp8 decode keeps this
+// many steps' loads in flight per wave to cover the same HBM latency.
+#ifndef MIMO_DECODE_FP8_DEPTH
+#define MIMO_DECODE_FP8_DEPTH 3
+#endif
 // Multi-query decode with more than 2 column tiles per KV head: its 2 or 4
 // waves read each step from HBM once, through LDS (0: each wave reads it).
 #ifndef MIMO_DECODE_SHARED
@@ -589,38 +594,41 @@ void decode_partial_kernel(DecodeArgs a) {
             for (int ph = 0; ph < RS - 1; ++ph)
                 if (i0 + ph < nsteps) phase(i0 + ph, ph);
         } else {
+            // Loads are unconditional: a step past the last re-reads the last one (in
+            // bounds, never computed). A load under a data-dependent branch made the
+            // compiler wait for every load in flight, the next step's included.
+            const int klast = kend > kbeg ? kbeg + (kend - kbeg - 1) / kStep * kStep : kbeg;
+            auto lstep = [&](int j) { return j < klast ? j : klast; };
             Buf A, B;
             int j0 = kbeg;
-            if (j0 < kend) load(A, j0);   // first step's loads go out before q's
+            load(A, j0);   // first step's loads go out before q's
             init_q();
             if constexpr (DEPTH == 3) {
                 // three steps' loads in flight: the one computed and the next two
                 Buf C;
-                if (j0 + kStep < kend) load(B, j0 + kStep);
+                load(B, lstep(j0 + kStep));
                 while (j0 < kend) {
-                    if (j0 + 2 * kStep < kend) load(C, j0 + 2 * kStep);
+                    load(C, lstep(j0 + 2 * kStep));
                     compute(A, j0);
                     j0 += kStep;
                     if (j0 >= kend) break;
-                    if (j0 + 2 * kStep < kend) load(A, j0 + 2 * kStep);
+                    load(A, lstep(j0 + 2 * kStep));
                     compute(B, j0);
                     j0 += kStep;
                     if (j0 >= kend) break;
-                    if (j0 + 2 * kStep < kend) load(B, j0 + 2 * kStep);
+                    load(B, lstep(j0 + 2 * kStep));
                     compute(C, j0);
                     j0 += kStep;
                 }
             } else {
                 while (j0 < kend) {
-                    int j1 = j0 + kStep;
-                    if (j1 < kend) load(B, j1);
+                    load(B, lstep(j0 + kStep));
                     compute(A, j0);
-                    j0 = j1;
+                    j0 += kStep;
                     if (j0 >= kend) break;
-                    j1 = j0 + kStep;
-                    if (j1 < kend) load(A, j1);
+                    load(A, lstep(j0 + kStep));
                     compute(B, j0);
-                    j0 = j1;
+                    j0 += kStep;
                 }
             }
         }
@@ -757,7 +765,7 @@ void launch_partial(const DecodeArgs &a, const DecodeGeom &m, hipStream_t stream
     if (!a.table)
         hipLaunchKernelGGL((decode_partial_kernel<NC, MAXT, false, false, DEPTH>), grid, block, 0, stream, a);
     else if (a.fp8)
-        hipLaunchKernelGGL((decode_partial_kernel<NC, MAXT, true, true, DEPTH>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((decode_partial_kernel<NC, MAXT, true, true, (NC == 1 ? MIMO_DECODE_FP8_DEPTH : DEPTH)>), grid, block, 0, stream, a);
     else
         hipLaunchKernelGGL((decode_partial_kernel<NC, MAXT, false, true, DEPTH>), grid, block, 0, stream, a);
 }
