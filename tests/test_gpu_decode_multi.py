@@ -42,7 +42,7 @@ def test_multi_sliding_ring(nq):
     assert_parity(got, ref, "out")
 
 
-@pytest.mark.parametrize("nq", [2, 4, 8])
+@pytest.mark.parametrize("nq", [2, 4, 5, 8])
 @pytest.mark.parametrize("with_sinks", [False, True])
 def test_multi_global(nq, with_sinks):
     cap = 9000

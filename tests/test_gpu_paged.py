@@ -71,6 +71,21 @@ def test_paged_sliding(kv, nq, bs):
     assert_parity(run_paged(d, cfg), oracle_paged(d, cfg), "out")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("nq", [1, 4])
+def test_paged_wide_window(kv, nq):
+    """A 512-token window reads up to 18 steps: the balanced split, not one
+    workgroup per sequence."""
+    S, W = 20, 512
+    pos = np.random.Generator(np.random.PCG64(9040 + nq)).integers(0, 100000, size=S)
+    pos[:4] = [0, 300, 511, 512]
+    d = gen.paged_decode_inputs(S, nq, 128, 64, 8, seed=9040 + nq, window=W, pos=pos, with_sinks=True,
+                                kv_dtype=kv, k_scale=0.05, v_scale=0.04)
+    say(f"paged decode window {W} {kv} nq={nq}")
+    cfg = cfg_for(64, 8, W, 1e4)
+    assert_parity(run_paged(d, cfg), oracle_paged(d, cfg), "out")
+
+
 def test_paged_bf16_equals_per_sequence_cache_bitwise():
     """A global layer's paged bf16 cache and the same tokens in per-sequence
     caches run the same steps: identical bits."""

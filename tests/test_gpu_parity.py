@@ -225,6 +225,20 @@ def test_decode_negative_position_is_empty():
     assert_parity(got[[0, 2]], ref, "out")
 
 
+def test_decode_swa_large_ring_split():
+    """A sliding layer's ring larger than the window (12 steps): decoded with the
+    balanced split rather than one workgroup per sequence; wrap-around inside the
+    ring and positions before the window fills."""
+    S, cap = 40, 384
+    pos = np.random.Generator(np.random.PCG64(5005)).integers(0, 200000, size=S)
+    pos[:6] = [0, 100, 383, 384, 500, 767]
+    d = _decode_with_positions(S, cap, 64, 8, 5005, 128, pos, True)
+    say(f"decode sliding S={S} cap={cap}")
+    got = run_decode(d, 64, 8, 128, 1e4, cap)
+    ref = oracle.decode(d["q"], d["pos"], d["k_cache"], d["v_cache"], sinks=d["sinks"], window=128, base=1e4)
+    assert_parity(got, ref, "out")
+
+
 def test_decode_many_short_sequences():
     """More sequences than plan threads (several per thread), lengths from empty to
     a full ring, so the balanced split puts many sequences in one workgroup."""
