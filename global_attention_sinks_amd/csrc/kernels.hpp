@@ -48,6 +48,7 @@ struct PrefillArgs {
     int64_t lse_hstride;  // lse element stride between heads
     // filled by the launcher
     int32_t n_qblk, n_hgrp, xcd_remap;
+    int32_t band_runs;    // sliding band kernel: runs of query blocks per (sequence, KV head)
 };
 hipError_t launch_prefill(PrefillArgs a, hipStream_t stream);
 

@@ -450,6 +450,304 @@ void prefill_kernel(PrefillArgs a) {
     }
 }
 
+
+// ---- Sliding-window band kernel (window <= 128, 8 query heads per KV head).
+// One workgroup = the 8 query heads of one KV head (one wave each, two waves per
+// SIMD) of one sequence, walking a run of consecutive 32-query blocks.  The 32-key
+// K/V tiles of the band live in an LDS ring of kBandSlots slots: a block reads the
+// (at most 6) tiles of its window, and each new block stages just the one tile its
+// window gains, staged while the block before it computes.  K/V tiles are read
+// from HBM about once per run instead of five times per block and head group.
+constexpr int kBandSlots = 7;
+constexpr int kBandMaxWindow = 128;
+
+template <int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
+void prefill_band_kernel(PrefillArgs a) {
+    constexpr int NK = 32, QW = 32, NT = 64 * NW;
+    constexpr int VSTR = NK + 8;
+    constexpr int K_TILE = NK * KSTR, V_TILE = kDv * VSTR, SLOT = K_TILE + V_TILE;
+    static_assert(NT == 512, "staging split: 256 rotating + 512 pass-through + 256 V units");
+    __shared__ __attribute__((aligned(16))) uint16_t ring[kBandSlots * SLOT];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int h2 = lane >> 5, l32 = lane & 31;
+
+    // ---- (sequence b, KV head g, run r of query blocks)
+    const int runs = a.band_runs;
+    const int r = blockIdx.x % runs, bg = blockIdx.x / runs;
+    const int g = bg % a.Hkv, b = bg / a.Hkv;
+    const int head = g * NW + w;
+
+    int Tq, Tk;
+    size_t q_tok0, k_tok0, lse_off;
+    int64_t q_pos0, k_pos0;
+    if (a.cu_q) {
+        const int qs = a.cu_q[b], ks = a.cu_k[b];
+        Tq = a.cu_q[b + 1] - qs;
+        Tk = a.cu_k[b + 1] - ks;
+        q_tok0 = (size_t)qs;
+        k_tok0 = (size_t)ks;
+        k_pos0 = a.kpos ? a.kpos[b] : 0;
+        q_pos0 = k_pos0 + Tk - Tq;
+        lse_off = (size_t)qs;
+    } else {
+        Tq = a.Tq;
+        Tk = a.Tk;
+        q_tok0 = (size_t)b * a.Tq;
+        k_tok0 = (size_t)b * a.Tk;
+        q_pos0 = a.q_pos0;
+        k_pos0 = a.k_pos0;
+        lse_off = (size_t)b * a.Hq * a.Tq;
+    }
+    const int off = Tk - Tq;                       // query t is key index t + off
+    const int nqb = (Tq + QW - 1) / QW;
+    const int per = (a.n_qblk + runs - 1) / runs;
+    const int qb0 = r * per, qb1 = min(nqb, qb0 + per);
+    if (qb0 >= qb1) return;                        // whole workgroup
+    const int W = a.window;
+    // 32-key tiles of the keys block qb sees: index [32 qb + off - W + 1, last query + off]
+    auto tlo = [&](int qb) { const int j = qb * QW + off - W + 1; return j > 0 ? j / NK : 0; };
+    auto thi = [&](int qb) { return (min(qb * QW + QW - 1, Tq - 1) + off) / NK; };
+    const int t_last = thi(qb1 - 1);
+
+    const size_t krow_stride = (size_t)a.Hkv * kDqk;
+    const size_t vrow_stride = (size_t)a.Hkv * kDv;
+    const uint16_t *kbase = a.k + k_tok0 * krow_stride + (size_t)g * kDqk;
+    const uint16_t *vbase = a.v + k_tok0 * vrow_stride + (size_t)g * kDv;
+
+    // ---- staging of a tile: threads < 256 rotate K piece (row tid>>3, pairs
+    // 4*(tid&7)..+3); every thread moves pass-through chunk 8 + (tid&15) of row
+    // tid>>4; threads >= 256 transpose V (key pair u%16, 8-dv chunk u/16, u = tid-256)
+    const bool rot_thr = tid < 256;
+    const int rrow = (tid & 255) >> 3, rq = tid & 7;
+    const int prow_ = tid >> 4, pch = 8 + (tid & 15);
+    const int vu = tid & 255, vkp = vu % 16, vcc = vu / 16;
+    uint64_t my_turn[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) my_turn[e] = a.rt.turn[4 * rq + e];
+    struct TileRegs {
+        u32x2 rx, ry;
+        u32x4 pl;
+        u32x4 v[2];
+    };
+    // unconditional loads of tile jt (rows past Tk re-read the last key: masked, finite)
+    auto load_tile = [&](TileRegs &R, int jt) {
+        const int j0 = jt * NK, last = Tk - 1 - j0;
+        const uint16_t *kt = kbase + (size_t)j0 * krow_stride;
+        const uint16_t *vt = vbase + (size_t)j0 * vrow_stride;
+        if (rot_thr) {
+            const uint16_t *src = kt + (size_t)min(rrow, last) * krow_stride + 4 * rq;
+            R.rx = *reinterpret_cast<const u32x2 *>(src);
+            R.ry = *reinterpret_cast<const u32x2 *>(src + 32);
+        } else {
+            const uint16_t *src = vt + 8 * vcc;
+            R.v[0] = ldg128(src + (size_t)min(2 * vkp, last) * vrow_stride);
+            R.v[1] = ldg128(src + (size_t)min(2 * vkp + 1, last) * vrow_stride);
+        }
+        R.pl = ldg128(kt + (size_t)min(prow_, last) * krow_stride + 8 * pch);
+    };
+    auto store_tile = [&](const TileRegs &R, int jt) {
+        uint16_t *Ks = ring + (jt % kBandSlots) * SLOT;
+        uint16_t *Vs = Ks + K_TILE;
+        if (rot_thr) {
+            const uint64_t pos = (uint64_t)(k_pos0 + (int64_t)jt * NK + rrow);
+            u32x2 x = R.rx, y = R.ry;
+#pragma unroll
+            for (int wd = 0; wd < 2; ++wd) {
+                float s0, c0, s1, c1;
+                turn_sincos(pos * my_turn[2 * wd], s0, c0);
+                turn_sincos(pos * my_turn[2 * wd + 1], s1, c1);
+                const float x0 = bf_lo(x[wd]), x1 = bf_hi(x[wd]);
+                const float y0 = bf_lo(y[wd]), y1 = bf_hi(y[wd]);
+                x[wd] = pack_bf16(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
+                y[wd] = pack_bf16(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
+            }
+            *reinterpret_cast<u32x2 *>(Ks + rrow * KSTR + 4 * rq) = x;
+            *reinterpret_cast<u32x2 *>(Ks + rrow * KSTR + 4 * rq + 32) = y;
+        } else {
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
+                const uint32_t wv = __builtin_amdgcn_perm(R.v[1][d >> 1], R.v[0][d >> 1], sel);
+                *reinterpret_cast<uint32_t *>(Vs + (8 * vcc + d) * VSTR + 2 * vkp) = wv;
+            }
+        }
+        *reinterpret_cast<u32x4 *>(Ks + prow_ * KSTR + 8 * pch) = R.pl;
+    };
+
+    const float cl2 = a.scale_log2;
+    const int prow = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+
+    // ---- prologue: the tiles of the first block, then the next tile's loads in flight
+    TileRegs R;
+    {
+        const int tp = thi(qb0);
+        load_tile(R, tlo(qb0));
+        for (int jt = tlo(qb0); jt <= tp; ++jt) {
+            store_tile(R, jt);
+            load_tile(R, min(jt + 1, t_last));
+        }
+    }
+    __syncthreads();
+
+    // Q rows (raw) of block qb.  (Issuing the next block's right after a block's
+    // last QK product, to hide their latency, measured slower.)
+    u32x4 qr[12];
+    auto load_q = [&](int qb) {
+        const int tq = min(qb * QW + l32, Tq - 1);
+        const uint16_t *src = a.q + ((q_tok0 + tq) * a.Hq + head) * kDqk + 96 * h2;
+#pragma unroll
+        for (int ks = 0; ks < 12; ++ks) qr[ks] = ldg128(src + 8 * ks);
+    };
+    for (int qb = qb0; qb < qb1; ++qb) {
+        const int q0 = qb * QW;
+        const int t0 = tlo(qb), t1 = thi(qb);
+        // the tile the next block adds: its slot is outside this block's window
+        if (t1 + 1 <= t_last) {
+            store_tile(R, t1 + 1);
+            load_tile(R, min(t1 + 2, t_last));
+        }
+
+        // ---- this block's Q, rotated
+        load_q(qb);
+        const int t = q0 + l32;
+        const bool tval = t < Tq;
+        if (h2 == 0) {
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) rope_rotate8(qr[cc], qr[cc + 4], a.rt, 8 * cc, q_pos0 + t);
+        }
+
+        float m_run = a.sinks ? a.sinks[head] * kLog2e : kNegInf;
+        float l_run = (a.sinks && h2 == 0) ? 1.0f : 0.0f;
+        f32x16 O[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) O[mb][e] = 0.0f;
+        const int qhi = min(q0 + QW - 1, Tq - 1);
+
+        // S^T of tile jt
+        auto qk_tile = [&](int jt) {
+            const uint16_t *Ks = ring + (jt % kBandSlots) * SLOT;
+            f32x16 S;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) S[e] = 0.0f;
+            {
+                const uint16_t *kr0 = Ks + prow * KSTR + 96 * h2;
+                u32x4 kf[RING];
+#pragma unroll
+                for (int i = 0; i < RING; ++i) kf[i] = lds128(kr0 + 8 * i);
+#pragma unroll
+                for (int i = 0; i < 12; ++i) {
+                    S = mfma32(kf[i % RING], qr[i], S);
+                    if (i + RING < 12) kf[i % RING] = lds128(kr0 + 8 * (i + RING));
+                }
+            }
+            return S;
+        };
+        // mask, online softmax, O^T += V^T P^T of tile jt
+        auto rest_tile = [&](int jt, f32x16 S) {
+            const uint16_t *Ks = ring + (jt % kBandSlots) * SLOT;
+            const uint16_t *Vs = Ks + K_TILE;
+            const int j0 = jt * NK;
+
+            // ---- mask unless every key of the tile is visible to every query of the block
+            const bool full = (j0 + NK <= Tk) && (q0 + off - (j0 + NK - 1) >= 0) && (qhi + off - j0 < W);
+            if (!full) {
+                const int d = t + off - j0;        // query's key index - first key of the tile
+                const int kmax = Tk - j0;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int jrel = 16 * (e >> 3) + 8 * h2 + (e & 7);
+                    const bool vis = (jrel < kmax) && (jrel <= d) && (d - jrel < W);
+                    if (!vis) S[e] = kNegInf;
+                }
+            }
+
+            // ---- online softmax (exp2 domain), lazy rescale
+            float mx = kNegInf;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, S[e]);
+            mx = max_xor32(mx);
+            const float mc = mx * cl2;
+            const bool need = mc > m_run + 8.0f;
+            if (__any(need)) {
+                const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mc) : 1.0f;
+                if (need) m_run = mc;
+                l_run *= alpha;
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) O[mb][e] *= alpha;
+            }
+            const float mu = (m_run == kNegInf) ? 0.0f : m_run;
+            u32x4 P[2];
+            float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], cl2, -mu));
+                S[e] = p;
+                ls[e & 3] += p;
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int x = 0; x < 4; ++x) P[s][x] = pack_bf16(S[8 * s + 2 * x], S[8 * s + 2 * x + 1]);
+            l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+
+            // ---- O^T += V^T P^T
+            {
+                const uint16_t *vr0 = Vs + l32 * VSTR + 8 * h2;
+                auto vaddr = [&](int i) { return vr0 + (i >> 1) * 32 * VSTR + 16 * (i & 1); };
+                u32x4 vf[RING];
+#pragma unroll
+                for (int i = 0; i < RING; ++i) vf[i] = lds128(vaddr(i));
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    O[i >> 1] = mfma32(vf[i % RING], P[i & 1], O[i >> 1]);
+                    if (i + RING < 8) vf[i % RING] = lds128(vaddr(i + RING));
+                }
+            }
+        };
+        for (int jt = t0; jt <= t1; ++jt) rest_tile(jt, qk_tile(jt));
+
+        // ---- epilogue: o = v_scale * O / l, bf16
+        const float lt = sum_xor32(l_run);
+        if (tval) {
+            const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
+            uint16_t *dst = a.out + ((q_tok0 + t) * a.Hq + head) * kDv;
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    u32x2 o;
+                    o[0] = pack_bf16(O[mb][4 * a4] * inv, O[mb][4 * a4 + 1] * inv);
+                    o[1] = pack_bf16(O[mb][4 * a4 + 2] * inv, O[mb][4 * a4 + 3] * inv);
+                    *reinterpret_cast<u32x2 *>(dst + 32 * mb + 8 * a4 + 4 * h2) = o;
+                }
+            if (a.lse && h2 == 0)
+                a.lse[lse_off + (size_t)head * a.lse_hstride + t] = lt > 0.0f ? (m_run + log2f(lt)) * kLn2 : kNegInf;
+        }
+        __syncthreads();   // the tile stored above is visible; nobody still reads the slot reused next
+    }
+}
+
+static hipError_t launch_band(PrefillArgs a, hipStream_t stream) {
+    a.n_qblk = (a.Tq + 31) / 32;
+    // about one workgroup per CU: runs of blocks per (sequence, KV head)
+    const int pairs = a.B * a.Hkv;
+    int runs = (256 + pairs - 1) / pairs;
+    if (runs > a.n_qblk) runs = a.n_qblk;
+    if (runs < 1) runs = 1;
+    a.band_runs = runs;
+    const int64_t blocks = (int64_t)pairs * runs;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((prefill_band_kernel<8>), dim3((unsigned)blocks), dim3(512), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int NW, int NK>
 static hipError_t launch_variant(PrefillArgs a, hipStream_t stream) {
     const int QW = 32;
@@ -467,6 +765,11 @@ static hipError_t launch_variant(PrefillArgs a, hipStream_t stream) {
 #ifndef MIMO_PREFILL_SHAPE
 #define MIMO_PREFILL_SHAPE 0
 #endif
+// Sliding layers with 8 query heads per KV head and a window <= 128 run the
+// band kernel (0: the per-block kernel).
+#ifndef MIMO_PREFILL_BAND
+#define MIMO_PREFILL_BAND 1
+#endif
 
 hipError_t launch_prefill(PrefillArgs a, hipStream_t stream) {
     // GQA group sizes are multiples of 4 (checked by the caller).  Sliding
@@ -474,6 +777,8 @@ hipError_t launch_prefill(PrefillArgs a, hipStream_t stream) {
     // per CU.  Global prefixes are long: 8 heads share each 64-key tile.
     const bool wide = (a.Hq / a.Hkv) % 8 == 0;
     int shape = MIMO_PREFILL_SHAPE;
+    if (shape == 0 && MIMO_PREFILL_BAND && a.window > 0 && a.window <= kBandMaxWindow && a.Hq == 8 * a.Hkv)
+        return launch_band(a, stream);
     if (shape == 0) shape = (a.window > 0 || !wide) ? 2 : 1;
     if (shape == 1 && wide) return launch_variant<8, 64>(a, stream);
     if (shape == 4) return launch_variant<4, 64>(a, stream);
