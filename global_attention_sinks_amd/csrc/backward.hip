@@ -8,13 +8,13 @@
 // and dq, dk are dQ~, dK~ turned back by the transpose of the partial RoPE
 // rotation (the same angle, negated).
 //
-//   bwd_prep_kernel    D per (row, head) from O and dO; per workgroup and head,
-//                      the sum of its rows' sink terms
-//   bwd_sink_kernel    one workgroup per head sums those partials (fixed order)
 //   bwd_dq_kernel      query-major: a workgroup owns 32 queries x 4 heads of a
-//                      GQA group; per 32-key tile (K rotated, K^T and V staged
-//                      in LDS, shared by the 4 heads) it rebuilds S^T and dP^T
-//                      and accumulates dQ~^T = K~^T dS^T in registers
+//                      GQA group; it forms D per (row, head) from O and dO and
+//                      per head the sum of its rows' sink terms, then per 32-key
+//                      tile (K rotated, K^T and V staged in LDS, shared by the 4
+//                      heads) rebuilds S^T and dP^T and accumulates
+//                      dQ~^T = K~^T dS^T in registers
+//   bwd_sink_kernel    one workgroup per head sums the sink partials (fixed order)
 //   bwd_dkdv_kernel    key-major: a workgroup owns 128 keys of one KV head (one
 //                      wave per 32 keys, the keys' K~ and V held in registers);
 //                      it walks every query head of the group and every 32-query
@@ -38,7 +38,6 @@ constexpr float kPosInf = __builtin_inff();
 constexpr int RSTR = kDqk + 8;   // LDS row stride of a 192-dim tile (bf16)
 constexpr int VSTR = kDv + 8;    // LDS row stride of a 128-dim tile
 constexpr int TSTR = 32 + 8;     // LDS row stride of a transposed 32-column tile
-constexpr int kPrepRows = 1024;  // (row, head) pairs per workgroup of the D pass
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
@@ -124,53 +123,11 @@ __device__ __forceinline__ void rope_back(float &x, float &y, uint64_t turn, int
 
 }  // namespace
 
-// ---- D = rowsum(dO o O) per (row, head); 16 lanes per row (16 bytes each), a
-// workgroup takes kPrepRows consecutive rows and leaves, per head, the sum of
-// its rows' sink terms -exp(sink - L) D (summed in a fixed order)
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
-    __shared__ float term[kPrepRows];
-    const int tid = threadIdx.x, sub = tid & 15, grp = tid >> 4;   // 16 groups of 16 lanes
-    const int64_t n = (int64_t)a.B * a.T * a.Hq;
-    const int64_t r0 = (int64_t)blockIdx.x * kPrepRows;
-    for (int i = grp; i < kPrepRows; i += 16) {
-        const int64_t r = r0 + i;                                    // ((b * T) + t) * Hq + h
-        float acc = 0.0f;
-        if (r < n) {
-            const u32x4 x = ldg128(a.out + r * kDv + 8 * sub), y = ldg128(a.dout + r * kDv + 8 * sub);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) acc += bf_lo(x[w]) * bf_lo(y[w]) + bf_hi(x[w]) * bf_hi(y[w]);
-        }
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-        if (sub == 0) {
-            float t_ = 0.0f;
-            if (r < n) {
-                a.D[r] = acc;
-                if (a.sinks) {
-                    const int h = (int)(r % a.Hq);
-                    const int64_t bt = r / a.Hq;
-                    const int64_t b = bt / a.T, t = bt - b * a.T;
-                    t_ = -__expf(a.sinks[h] - a.lse[((size_t)b * a.Hq + h) * a.T + t]) * acc;
-                }
-            }
-            term[i] = t_;
-        }
-    }
-    if (!a.sinks) return;
-    __syncthreads();
-    // rows r0 + i with (r0 + i) % Hq == h, in increasing i
-    for (int h = tid; h < a.Hq; h += 256) {
-        float s_ = 0.0f;
-        for (int i = (int)((h - r0 % a.Hq + a.Hq) % a.Hq); i < kPrepRows; i += a.Hq) s_ += term[i];
-        a.csink[(size_t)blockIdx.x * a.Hq + h] = s_;
-    }
-}
-
 // ---- d sink_h: one workgroup per head, fixed-order tree sum over the workgroup partials
 __global__ __launch_bounds__(256) void bwd_sink_kernel(BwdArgs a) {
     __shared__ float red[256];
     const int h = blockIdx.x;
-    const int64_t nblk = ((int64_t)a.B * a.T * a.Hq + kPrepRows - 1) / kPrepRows;
+    const int64_t nblk = (int64_t)a.B * a.n_qblk;   // (batch, query block) partials
     float s_ = 0.0f;
     for (int64_t i = threadIdx.x; i < nblk; i += 256) s_ += a.csink[i * a.Hq + h];
     red[threadIdx.x] = s_;
@@ -226,15 +183,32 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 #pragma unroll
         for (int s = 0; s < 8; ++s) dof[s] = ldg128(gs + 8 * s);
         L2 = a.lse[((size_t)b * a.Hq + head) * a.T + t] * kLog2e;
-        Dq = a.D[qrow];
+        // D = <dO, O> of the row: this lane's 64 dims, then its h2 partner's
+        const uint16_t *os = a.out + qrow * kDv + 64 * h2;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const u32x4 o = ldg128(os + 8 * s);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) Dq += bf_lo(o[x]) * bf_lo(dof[s][x]) + bf_hi(o[x]) * bf_hi(dof[s][x]);
+        }
     } else {
 #pragma unroll
         for (int s = 0; s < 12; ++s) qf[s] = u32x4{0, 0, 0, 0};
 #pragma unroll
         for (int s = 0; s < 8; ++s) dof[s] = u32x4{0, 0, 0, 0};
     }
+    Dq = sum_xor32(Dq);
 #pragma unroll
     for (int s = 0; s < 8; ++s) *reinterpret_cast<u32x4 *>(dos + 8 * s) = dof[s];
+    if (tval && h2 == 0) a.D[qrow] = Dq;   // for the dk/dv pass
+    if (a.sinks) {
+        // this head's sink terms -exp(sink - L) D summed over the block's 32 rows
+        // (fixed order), one partial per (batch, query block, head)
+        float term = (tval && h2 == 0) ? -__builtin_amdgcn_exp2f(a.sinks[head] * kLog2e - L2) * Dq : 0.0f;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) term += __shfl_xor(term, o);
+        if (lane == 0) a.csink[((size_t)b * a.n_qblk + qb) * a.Hq + head] = term;
+    }
 
     f32x16 acc[6];
 #pragma unroll
@@ -561,7 +535,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
 
 size_t backward_workspace_bytes(int32_t B, int32_t T, int32_t Hq) {
     const size_t rows = (size_t)B * T * Hq;
-    return (rows + (rows + kPrepRows - 1) / kPrepRows * Hq) * sizeof(float);
+    return (rows + (size_t)B * ((T + 31) / 32) * Hq) * sizeof(float);
 }
 
 hipError_t launch_backward(BwdArgs a, hipStream_t stream) {
@@ -570,8 +544,9 @@ hipError_t launch_backward(BwdArgs a, hipStream_t stream) {
     a.n_qblk = (a.T + 31) / 32;
     a.n_hgrp = G / 4;
     a.n_kblk = (a.T + 127) / 128;
-    const int64_t rows = (int64_t)a.B * a.T * a.Hq;
-    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + kPrepRows - 1) / kPrepRows)), dim3(256), 0, stream, a);
+    // dq also forms D and the sink partials; d sink and dk/dv read them
+    const int64_t qblocks = (int64_t)a.B * a.Hkv * a.n_hgrp * a.n_qblk;
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)qblocks), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.sinks) {
@@ -579,10 +554,6 @@ hipError_t launch_backward(BwdArgs a, hipStream_t stream) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int64_t qblocks = (int64_t)a.B * a.Hkv * a.n_hgrp * a.n_qblk;
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)qblocks), dim3(256), 0, stream, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const int64_t kblocks = (int64_t)a.B * a.Hkv * a.n_kblk;
     hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kblocks), dim3(256), 0, stream, a);
     return hipGetLastError();

@@ -58,7 +58,7 @@ struct BwdArgs {
     const float *lse;                         // [B, Hq, T] natural-log LSE of the forward
     const float *sinks;                       // nullable
     float *D;                                 // workspace [B, T, Hq]: rowsum(dO o O)
-    float *csink;                             // workspace [row blocks, Hq]: sink-term partials
+    float *csink;                             // workspace [B * 32-query blocks, Hq]: sink-term partials
     uint16_t *dq, *dk, *dv;
     float *dsinks;                            // [Hq], written when sinks != NULL
     int32_t B, T, Hq, Hkv, window;

@@ -219,7 +219,7 @@ mimo_status mimo_attn_prefill_backward(const mimo_attn_cfg *cfg, const uint16_t 
                                        void *stream);
 
 /* Workspace bytes of mimo_attn_prefill_backward: one fp32 value per (token, query head) and
- * one per query head for every 1024 of those. */
+ * one per (batch row, block of 32 tokens, query head). */
 size_t mimo_attn_backward_workspace_size(const mimo_attn_cfg *cfg, int32_t B, int32_t T);
 
 /* Element type of a paged KV cache. */
