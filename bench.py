@@ -133,6 +133,8 @@ def setup_layer_step(torch, gen, Bd):
     ph["global_prefill"] = dict(
         cfg=Bd.global_cfg(), q=dev_bf16(d["q"]), k=dev_bf16(d["k"]), v=dev_bf16(d["v"]),
         out=torch.empty((1, 32768, 64, 128), dtype=torch.bfloat16, device="cuda"),
+        ws=torch.empty(Bd.mimo_attn_prefill_workspace_size(Bd.global_cfg(), 1, 32768), dtype=torch.uint8,
+                       device="cuda"),
         flops=FLOP_PER_PAIR_HEAD * 64 * causal_pairs(0, 32768),
         bytes=prefill_bytes(1, 32768, 32768, 64, 4, False), host=d)
     # 3. mixed decode
@@ -174,7 +176,8 @@ def run_layer_step(ph, Bd, ev=None):
     s = ph["swa_prefill"]
     rec("swa_prefill", lambda: Bd.mimo_attn_prefill_swa(s["cfg"], s["q"], s["k"], s["v"], s["sinks"], s["out"]))
     g = ph["global_prefill"]
-    rec("global_prefill", lambda: Bd.mimo_attn_prefill_global(g["cfg"], g["q"], g["k"], g["v"], g["out"]))
+    rec("global_prefill", lambda: Bd.mimo_attn_prefill_global(g["cfg"], g["q"], g["k"], g["v"], g["out"],
+                                                                ws=g["ws"]))
     for name in ("swa", "global"):
         d = ph["decode"][name]
         rec(f"append_{name}", lambda d=d: Bd.mimo_kv_ring_append(d["cfg"], d["k_new"], d["v_new"], d["pos"],
@@ -351,7 +354,8 @@ def main():
                                    "frac_hbm_peak": gbs(mixed_bytes, mixed_ms) / PEAK_HBM_GBS}
 
     achieved = tf(g["flops"], ms["global_prefill"])
-    roofline = {"bound": "mfma", "kernel": "prefill_kernel (global causal, T=32768)",
+    roofline = {"bound": "mfma", "kernel": "prefill_image_kernel (global causal, T=32768; its K/V image pass "
+                                           "is inside the timed call)",
                 "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": profiled_traffic("global prefill T32768"),
                 "algorithmic_flops": g["flops"], "algorithmic_bytes": g["bytes"]}
@@ -384,13 +388,14 @@ def main_long_prefill(args, torch, gen, Bd):
     out = torch.empty((1, T, 64, 128), dtype=torch.bfloat16, device="cuda")
     cfg = Bd.global_cfg()
     n_chunks = T // C
+    ws = torch.empty(Bd.mimo_attn_prefill_workspace_size(cfg, 1, T), dtype=torch.uint8, device="cuda")
 
     def step(ev=None):
         for c in range(n_chunks):
             if ev is not None:
                 ev[c][0].record()
             Bd.mimo_attn_prefill_global(cfg, q[:, c * C:(c + 1) * C], k[:, :(c + 1) * C], v[:, :(c + 1) * C],
-                                        out[:, c * C:(c + 1) * C], q_pos0=c * C)
+                                        out[:, c * C:(c + 1) * C], q_pos0=c * C, ws=ws)
             if ev is not None:
                 ev[c][1].record()
 
@@ -413,7 +418,7 @@ def main_long_prefill(args, torch, gen, Bd):
              "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
              "vs_baseline": None, "dtype": "bf16", "data": "synthetic: seeded N(0,1) bf16 q/k/v",
              "config": {"workload": "global_prefill_t524288 in 8 query chunks of 65536 against the full prefix"},
-             "roofline": {"bound": "mfma", "kernel": "prefill_kernel (global causal chunks)", "achieved": value,
+             "roofline": {"bound": "mfma", "kernel": "prefill_image_kernel (global causal chunks)", "achieved": value,
                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": value / PEAK_BF16_TFLOPS,
                           "traffic": None},
              "cpu_baseline": None,
@@ -448,6 +453,8 @@ def main_serving_chunks(args, torch, gen, Bd):
                   sinks=None if d["sinks"] is None else dev(d["sinks"]),
                   out=torch.empty((4 * C, 64, 128), dtype=torch.bfloat16, device="cuda"),
                   bytes=4 * C * 64 * (192 + 128) * 2 + int(d["cu_k"][-1]) * hkv * (192 + 128) * 2)
+        n = Bd.mimo_attn_prefill_workspace_size(pk["cfg"], 4, int(d["cu_k"][-1]))
+        pk["ws"] = torch.empty(n, dtype=torch.uint8, device="cuda") if n else False
         del pk["d"]
     names = list(packs)
 
@@ -457,7 +464,7 @@ def main_serving_chunks(args, torch, gen, Bd):
             if ev is not None:
                 ev[n][0].record()
             Bd.mimo_attn_prefill_varlen(pk["cfg"], pk["q"], pk["k"], pk["v"], pk["sinks"], pk["cu_q"], pk["cu_k"],
-                                        C, pk["out"], k_pos0=pk["kpos"])
+                                        C, pk["out"], k_pos0=pk["kpos"], ws=pk["ws"])
             if ev is not None:
                 ev[n][1].record()
 
@@ -487,7 +494,7 @@ def main_serving_chunks(args, torch, gen, Bd):
              "vs_baseline": None, "dtype": "bf16", "data": "synthetic: seeded N(0,1) bf16 q/k/v, N(0,1) fp32 sinks",
              "config": {"workload": "serving_chunks = packed sliding chunks 4x8192 (continuing at 8K..256K) + "
                                     "packed global chunks 4x8192 (prefixes 0..57344)"},
-             "roofline": {"bound": "mfma", "kernel": "prefill_kernel (packed global chunks)", "achieved": g["tflops"],
+             "roofline": {"bound": "mfma", "kernel": "prefill_image_kernel (packed global chunks)", "achieved": g["tflops"],
                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": g["frac_mfma_peak"],
                           "traffic": None},
              "cpu_baseline": None, "phases": phases}
@@ -688,7 +695,7 @@ def main_backward(args, torch, gen, Bd):
              "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
              "data": "synthetic: seeded N(0,1) bf16 q/k/v/dO, N(0,1) fp32 sinks",
              "config": {"workload": "swa_backward_b4_t8192 (dq, dk, dv, d sink from the forward's output and LSE)"},
-             "roofline": {"bound": "hbm", "kernel": "bwd_prep + bwd_sink + bwd_dq + bwd_dkdv (one call)",
+             "roofline": {"bound": "hbm", "kernel": "bwd_dq + bwd_sink + bwd_dkdv (one call)",
                           "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                           "traffic": None, "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
                           "tflops": tflops, "frac_mfma_peak": tflops / PEAK_BF16_TFLOPS},

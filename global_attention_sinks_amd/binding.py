@@ -61,8 +61,11 @@ def load_library(path: str = LIB_PATH):
     C = ctypes.POINTER(MimoAttnCfg)
     lib.mimo_rope_partial.argtypes = [C, P, P, I64, I32, P, P]
     lib.mimo_attn_prefill_swa.argtypes = [C, P, P, P, P, I32, I32, I64, P, P, P]
-    lib.mimo_attn_prefill_global.argtypes = [C, P, P, P, I32, I32, I32, I64, P, P, P]
-    lib.mimo_attn_prefill_varlen.argtypes = [C, P, P, P, P, I32, P, P, P, I32, I32, P, P, P]
+    lib.mimo_attn_prefill_global.argtypes = [C, P, P, P, I32, I32, I32, I64, P, P, P, ctypes.c_size_t, P]
+    lib.mimo_attn_prefill_varlen.argtypes = [C, P, P, P, P, I32, P, P, P, I32, I32, I64, P, P, P,
+                                             ctypes.c_size_t, P]
+    lib.mimo_attn_prefill_workspace_size.argtypes = [C, I32, I64]
+    lib.mimo_attn_prefill_workspace_size.restype = ctypes.c_size_t
     lib.mimo_attn_decode.argtypes = [C, I32, P, P, P, P, I32, P, P, P, ctypes.c_size_t, P]
     lib.mimo_attn_prefill_backward.argtypes = [C, P, P, P, P, I32, I32, I64, P, P, P, P, P, P, P, P,
                                                ctypes.c_size_t, P]
@@ -136,7 +139,24 @@ def mimo_attn_prefill_swa(cfg: MimoAttnCfg, q, k, v, sinks, out, pos0: int = 0, 
     return out
 
 
-def mimo_attn_prefill_global(cfg: MimoAttnCfg, q, k, v, out, q_pos0: int = 0, lse=None, stream=None):
+def mimo_attn_prefill_workspace_size(cfg: MimoAttnCfg, B: int, total_k: int) -> int:
+    return int(load_library().mimo_attn_prefill_workspace_size(ctypes.byref(cfg), B, total_k))
+
+
+def _prefill_ws(cfg, B, total_k, ws, device):
+    """ws: a uint8 device tensor, None (allocate one of the size the call needs) or
+    False (no tile images: the attention kernel stages every tile itself)."""
+    if ws is False:
+        return None, 0
+    if ws is None:
+        n = mimo_attn_prefill_workspace_size(cfg, B, total_k)
+        if n == 0:
+            return None, 0
+        ws = torch.empty(n, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def mimo_attn_prefill_global(cfg: MimoAttnCfg, q, k, v, out, q_pos0: int = 0, lse=None, ws=None, stream=None):
     """q [B,Tq,Hq,192] at positions q_pos0.., k/v [B,Tk,Hkv,*] at 0..Tk-1, Tk = q_pos0 + Tq."""
     lib = load_library()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
@@ -144,14 +164,15 @@ def mimo_attn_prefill_global(cfg: MimoAttnCfg, q, k, v, out, q_pos0: int = 0, ls
     _need(lse, torch.float32, "lse", 3)
     B, Tq = q.shape[:2]
     Tk = k.shape[1]
+    ws, ws_bytes = _prefill_ws(cfg, B, B * Tk, ws, q.device)
     _check("mimo_attn_prefill_global",
            lib.mimo_attn_prefill_global(ctypes.byref(cfg), _p(q), _p(k), _p(v), B, Tq, Tk, q_pos0,
-                                        _p(out), _p(lse), _stream(stream)))
+                                        _p(out), _p(lse), _p(ws), ws_bytes, _stream(stream)))
     return out
 
 
 def mimo_attn_prefill_varlen(cfg: MimoAttnCfg, q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
-                             out, k_pos0=None, lse=None, stream=None):
+                             out, k_pos0=None, lse=None, ws=None, stream=None):
     """Packed sequences: q [total_q,Hq,192], k/v [total_k,Hkv,*], out [total_q,Hq,128],
     cu_seqlens_q / cu_seqlens_k [B+1] int32, k_pos0 [B] int64 or None, lse [Hq,total_q]."""
     lib = load_library()
@@ -161,10 +182,11 @@ def mimo_attn_prefill_varlen(cfg: MimoAttnCfg, q, k, v, sinks, cu_seqlens_q, cu_
     _need(k_pos0, torch.int64, "k_pos0", 1); _need(sinks, torch.float32, "sinks", 1)
     _need(lse, torch.float32, "lse", 2)
     B = cu_seqlens_q.shape[0] - 1
+    ws, ws_bytes = _prefill_ws(cfg, B, k.shape[0], ws, q.device)
     _check("mimo_attn_prefill_varlen",
            lib.mimo_attn_prefill_varlen(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(sinks), B, _p(cu_seqlens_q),
-                                        _p(cu_seqlens_k), _p(k_pos0), max_seqlen_q, q.shape[0], _p(out),
-                                        _p(lse), _stream(stream)))
+                                        _p(cu_seqlens_k), _p(k_pos0), max_seqlen_q, q.shape[0], k.shape[0],
+                                        _p(out), _p(lse), _p(ws), ws_bytes, _stream(stream)))
     return out
 
 

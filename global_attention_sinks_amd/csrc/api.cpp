@@ -131,9 +131,33 @@ mimo_status mimo_attn_prefill_swa(const mimo_attn_cfg *cfg, const uint16_t *q, c
     return from_hip(launch_prefill(a, (hipStream_t)stream), "prefill_swa launch");
 }
 
+// Bytes of the K/V tile images a global-layer prefill uses (0 where the layer does
+// not use them: sliding windows, GQA groups that are not a multiple of 8).
+static size_t image_bytes(const mimo_attn_cfg *cfg, int32_t B, int64_t total_k) {
+    if (cfg->window != 0 || (cfg->num_q_heads / cfg->num_kv_heads) % 8 != 0 || B <= 0 || total_k <= 0) return 0;
+    return prefill_image_bytes(B, total_k, cfg->num_kv_heads);
+}
+
+size_t mimo_attn_prefill_workspace_size(const mimo_attn_cfg *cfg, int32_t B, int64_t total_k) {
+    if (check_cfg(cfg) != MIMO_OK) return 0;
+    return image_bytes(cfg, B, total_k);
+}
+
+// ws == NULL: no images (the attention kernel stages each tile itself).
+static mimo_status attach_images(PrefillArgs &a, const mimo_attn_cfg *cfg, int32_t B, int64_t total_k,
+                                 void *ws, size_t ws_bytes) {
+    const size_t need = image_bytes(cfg, B, total_k);
+    if (!ws || need == 0) return ok();
+    if (ws_bytes < need)
+        return fail(MIMO_ERR_WORKSPACE, "prefill workspace needs %zu bytes (got %zu)", need, ws_bytes);
+    a.kv_img = static_cast<uint16_t *>(ws);
+    return ok();
+}
+
 mimo_status mimo_attn_prefill_global(const mimo_attn_cfg *cfg, const uint16_t *q, const uint16_t *k,
                                      const uint16_t *v, int32_t B, int32_t Tq, int32_t Tk,
-                                     int64_t q_pos0, uint16_t *out, float *lse, void *stream) {
+                                     int64_t q_pos0, uint16_t *out, float *lse, void *ws,
+                                     size_t ws_bytes, void *stream) {
     mimo_status st = prefill_common(cfg, q, k, v, out, B, Tq, Tk);
     if (st != MIMO_OK) return st;
     if (cfg->window != 0) return fail(MIMO_ERR_INVALID_ARGUMENT, "global prefill needs window == 0");
@@ -148,6 +172,8 @@ mimo_status mimo_attn_prefill_global(const mimo_attn_cfg *cfg, const uint16_t *q
     a.q_pos0 = q_pos0; a.k_pos0 = 0; a.window = 0; a.lse_hstride = Tq;
     a.scale_log2 = scale_log2(cfg); a.v_scale = cfg->v_scale;
     a.rt = rope_turns(cfg->rope_base);
+    st = attach_images(a, cfg, B, (int64_t)B * Tk, ws, ws_bytes);
+    if (st != MIMO_OK) return st;
     return from_hip(launch_prefill(a, (hipStream_t)stream), "prefill_global launch");
 }
 
@@ -155,11 +181,12 @@ mimo_status mimo_attn_prefill_varlen(const mimo_attn_cfg *cfg, const uint16_t *q
                                      const uint16_t *v, const float *sinks, int32_t B,
                                      const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
                                      const int64_t *k_pos0, int32_t max_seqlen_q, int32_t total_q,
-                                     uint16_t *out, float *lse, void *stream) {
+                                     int64_t total_k, uint16_t *out, float *lse, void *ws,
+                                     size_t ws_bytes, void *stream) {
     mimo_status st = check_cfg(cfg);
     if (st != MIMO_OK) return st;
-    if (B < 0 || max_seqlen_q < 0 || total_q < 0)
-        return fail(MIMO_ERR_INVALID_ARGUMENT, "B, max_seqlen_q and total_q must be >= 0");
+    if (B < 0 || max_seqlen_q < 0 || total_q < 0 || total_k < 0)
+        return fail(MIMO_ERR_INVALID_ARGUMENT, "B, max_seqlen_q, total_q and total_k must be >= 0");
     if ((cfg->num_q_heads / cfg->num_kv_heads) % 4 != 0)
         return fail(MIMO_ERR_UNSUPPORTED, "prefill needs a GQA group size that is a multiple of 4 (got %d)",
                     cfg->num_q_heads / cfg->num_kv_heads);
@@ -175,6 +202,8 @@ mimo_status mimo_attn_prefill_varlen(const mimo_attn_cfg *cfg, const uint16_t *q
     a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k; a.kpos = k_pos0;
     a.scale_log2 = scale_log2(cfg); a.v_scale = cfg->v_scale;
     a.rt = rope_turns(cfg->rope_base);
+    st = attach_images(a, cfg, B, total_k, ws, ws_bytes);
+    if (st != MIMO_OK) return st;
     return from_hip(launch_prefill(a, (hipStream_t)stream), "prefill_varlen launch");
 }
 

@@ -49,7 +49,12 @@ struct PrefillArgs {
     // filled by the launcher
     int32_t n_qblk, n_hgrp, xcd_remap;
     int32_t band_runs;    // sliding band kernel: runs of query blocks per (sequence, KV head)
+    // global layers (window 0, GQA group a multiple of 8): device buffer of at least
+    // prefill_image_bytes() for the rotated-K / transposed-V tile images, or NULL to
+    // stage each tile inside the attention kernel
+    uint16_t *kv_img;
 };
+size_t prefill_image_bytes(int32_t B, int64_t total_k, int32_t Hkv);
 hipError_t launch_prefill(PrefillArgs a, hipStream_t stream);
 
 // ---- prefill backward (backward.hip)

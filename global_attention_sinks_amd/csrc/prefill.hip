@@ -51,6 +51,37 @@ __device__ __forceinline__ u32x4 lds128(const uint16_t *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// ---- which (query block, batch, KV head, head group) workgroup blockIdx.x owns.
+// With the (KV head, head group) pairs split evenly over the 8 XCDs, an XCD walks
+// its pairs sequence by sequence, query blocks longest-first: its resident
+// workgroups then sweep the same K/V rows together (L2 reuse), and every XCD gets
+// the same share of every sequence.
+__device__ __forceinline__ void map_block(const PrefillArgs &a, int &qb, int &b, int &pair) {
+    const int P = a.Hkv * a.n_hgrp;
+    const int i = blockIdx.x;
+    if (a.xcd_remap == 2) {
+        const int x = i & 7, j = i >> 3, ppx = P >> 3;
+        const int per_b = ppx * a.n_qblk;
+        b = j / per_b;
+        const int r = j - b * per_b;
+        pair = x * ppx + r % ppx;
+        qb = a.n_qblk - 1 - r / ppx;
+    } else if (a.xcd_remap == 1) {
+        const int combos = a.B * P;
+        const int x = i & 7, j = i >> 3, cpx = combos >> 3;
+        const int c = x * cpx + j % cpx;
+        qb = a.n_qblk - 1 - j / cpx;
+        b = c % a.B;
+        pair = c / a.B;
+    } else {
+        const int combos = a.B * P;
+        const int c = i % combos;
+        qb = a.n_qblk - 1 - i / combos;
+        b = c % a.B;
+        pair = c / a.B;
+    }
+}
+
 }  // namespace
 
 template <int NW, int NK>
@@ -78,37 +109,8 @@ void prefill_kernel(PrefillArgs a) {
     const int lane = tid & 63, w = tid >> 6;
     const int h2 = lane >> 5, l32 = lane & 31;
 
-    // ---- which (query block, batch, KV head, head group) this workgroup owns.
-    // With the (KV head, head group) pairs split evenly over the 8 XCDs, an XCD
-    // walks its pairs sequence by sequence, query blocks longest-first: its
-    // resident workgroups then sweep the same K/V rows together (L2 reuse),
-    // and every XCD gets the same share of every sequence.
-    const int P = a.Hkv * a.n_hgrp;
     int qb, b, pair;
-    {
-        const int i = blockIdx.x;
-        if (a.xcd_remap == 2) {
-            const int x = i & 7, j = i >> 3, ppx = P >> 3;
-            const int per_b = ppx * a.n_qblk;
-            b = j / per_b;
-            const int r = j - b * per_b;
-            pair = x * ppx + r % ppx;
-            qb = a.n_qblk - 1 - r / ppx;
-        } else if (a.xcd_remap == 1) {
-            const int combos = a.B * P;
-            const int x = i & 7, j = i >> 3, cpx = combos >> 3;
-            const int c = x * cpx + j % cpx;
-            qb = a.n_qblk - 1 - j / cpx;
-            b = c % a.B;
-            pair = c / a.B;
-        } else {
-            const int combos = a.B * P;
-            const int c = i % combos;
-            qb = a.n_qblk - 1 - i / combos;
-            b = c % a.B;
-            pair = c / a.B;
-        }
-    }
+    map_block(a, qb, b, pair);
     const int hg = pair % a.n_hgrp;
     const int g = pair / a.n_hgrp;
     const int G = a.Hq / a.Hkv;
@@ -451,6 +453,321 @@ void prefill_kernel(PrefillArgs a) {
 }
 
 
+// ---- K/V tile images for the global kernel below.  Every workgroup whose queries
+// follow a key stages that key again (thousands of times over a long chunk), so
+// rotating K and transposing V once per call, instead of once per workgroup and
+// tile, takes that work out of the attention loop.  One workgroup
+// per 64-key tile of one (sequence, KV head) writes the tile's exact LDS image:
+// K rotated (rows padded to KSTR), then V^T (rows padded to kImgVS); rows past the
+// sequence's end are zero.  Tiles of sequence b start at tile index
+// floor(cu_k[b] / 64) + b (packed) or b * ceil(Tk / 64) (dense), and tile t of KV
+// head g is image (start + t) * Hkv + g.
+constexpr int kImgNK = 64;
+constexpr int kPrepVS = kDv + 8;                             // V row stride while transposing
+constexpr int kImgVS = kImgNK + 8;                           // V^T row stride in the image
+constexpr int kImgK = kImgNK * KSTR;                         // bf16 elements
+constexpr int kImgTile = kImgK + kDv * kImgVS;               // 22016 bf16 = 43 KiB
+
+__global__ __launch_bounds__(256) void kv_image_kernel(PrefillArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t vs[kImgNK * kPrepVS];
+    const int b = blockIdx.y, g = blockIdx.z, tid = threadIdx.x;
+    int Tk, tile_base;
+    size_t k_tok0;
+    int64_t k_pos0;
+    if (a.cu_k) {
+        const int ks = a.cu_k[b];
+        Tk = a.cu_k[b + 1] - ks;
+        k_tok0 = (size_t)ks;
+        k_pos0 = a.kpos ? a.kpos[b] : 0;
+        tile_base = ks / kImgNK + b;
+    } else {
+        Tk = a.Tk;
+        k_tok0 = (size_t)b * a.Tk;
+        k_pos0 = a.k_pos0;
+        tile_base = b * ((a.Tk + kImgNK - 1) / kImgNK);
+    }
+    const int ntile = (Tk + kImgNK - 1) / kImgNK;
+    const size_t krow = (size_t)a.Hkv * kDqk, vrow = (size_t)a.Hkv * kDv;
+    for (int t = blockIdx.x; t < ntile; t += gridDim.x) {
+        const size_t tile_id = (size_t)(tile_base + t) * a.Hkv + g;
+        uint16_t *wk = a.kv_img + tile_id * kImgTile;
+        uint16_t *wv = wk + kImgK;
+        const int j0 = t * kImgNK;
+        {   // rotating chunks: row tid/4, pairs 8*(tid%4)..+7
+            const int row = tid >> 2, cc = tid & 3, j = j0 + row;
+            u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
+            if (j < Tk) {
+                const uint16_t *src = a.k + (k_tok0 + j) * krow + (size_t)g * kDqk;
+                x = ldg128(src + 8 * cc);
+                y = ldg128(src + 32 + 8 * cc);
+                rope_rotate8(x, y, a.rt, 8 * cc, k_pos0 + j);
+            }
+            *reinterpret_cast<u32x4 *>(wk + row * KSTR + 8 * cc) = x;
+            *reinterpret_cast<u32x4 *>(wk + row * KSTR + 32 + 8 * cc) = y;
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {   // pass-through chunks 8..23
+            const int u = tid + 256 * m, row = u >> 4, c = 8 + (u & 15), j = j0 + row;
+            u32x4 x = {0, 0, 0, 0};
+            if (j < Tk) x = ldg128(a.k + (k_tok0 + j) * krow + (size_t)g * kDqk + 8 * c);
+            *reinterpret_cast<u32x4 *>(wk + row * KSTR + 8 * c) = x;
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {   // V rows into LDS
+            const int u = tid + 256 * m, row = u >> 4, c = u & 15, j = j0 + row;
+            u32x4 x = {0, 0, 0, 0};
+            if (j < Tk) x = ldg128(a.v + (k_tok0 + j) * vrow + (size_t)g * kDv + 8 * c);
+            *reinterpret_cast<u32x4 *>(vs + row * kPrepVS + 8 * c) = x;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {   // V^T rows: dv, keys 8c..8c+7
+            const int u = tid + 256 * m, dv = u >> 3, c = u & 7;
+            u32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                o[i] = (uint32_t)vs[(8 * c + 2 * i) * kPrepVS + dv] |
+                       ((uint32_t)vs[(8 * c + 2 * i + 1) * kPrepVS + dv] << 16);
+            *reinterpret_cast<u32x4 *>(wv + dv * kImgVS + 8 * c) = o;
+        }
+        __syncthreads();
+    }
+}
+
+// ---- Global prefill over the tile images: the math of prefill_kernel<8, 64>
+// (same workgroup shape, block mapping, MFMA layout and online softmax), with each
+// tile moved HBM -> LDS by the global_load_lds path: 43 copies of 1 KiB, 16 bytes
+// per lane, straight into LDS.  No staging registers, no RoPE or transpose VALU
+// work and no LDS stores remain in the loop.
+template <int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
+void prefill_image_kernel(PrefillArgs a) {
+    constexpr int NK = 64;
+    constexpr int QW = 32;
+    constexpr int KB = NK / 32;
+    constexpr int VSTR = NK + 8;
+    constexpr int K_TILE = NK * KSTR;               // 25600 bytes
+    constexpr int V_TILE = kDv * VSTR;              // 18432 bytes
+    constexpr int STAGE = K_TILE + V_TILE;
+    constexpr int K_OPS = K_TILE * 2 / 1024, V_OPS = V_TILE * 2 / 1024;   // 25 + 18 copies of 1 KiB
+    constexpr int OPS = K_OPS + V_OPS;
+    constexpr int OPW = (OPS + NW - 1) / NW;        // per wave
+    static_assert(K_TILE * 2 % 1024 == 0 && V_TILE * 2 % 1024 == 0, "whole 1 KiB copies");
+    static_assert(STAGE == kImgTile && VSTR == kImgVS, "prepared image = LDS stage");
+
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h2 = lane >> 5, l32 = lane & 31;
+
+    int qb, b, pair;
+    map_block(a, qb, b, pair);
+    const int hg = pair % a.n_hgrp;
+    const int g = pair / a.n_hgrp;
+    const int G = a.Hq / a.Hkv;
+    const int head = g * G + hg * NW + w;
+    const int q0 = qb * QW;
+
+    int Tq, Tk, tile_base;
+    size_t q_tok0, lse_off;
+    int64_t q_pos0, k_pos0;
+    if (a.cu_q) {
+        const int qs = a.cu_q[b], ks = a.cu_k[b];
+        Tq = a.cu_q[b + 1] - qs;
+        Tk = a.cu_k[b + 1] - ks;
+        q_tok0 = (size_t)qs;
+        k_pos0 = a.kpos ? a.kpos[b] : 0;
+        q_pos0 = k_pos0 + Tk - Tq;
+        lse_off = (size_t)qs;
+        tile_base = ks / NK + b;
+    } else {
+        Tq = a.Tq;
+        Tk = a.Tk;
+        q_tok0 = (size_t)b * a.Tq;
+        q_pos0 = a.q_pos0;
+        k_pos0 = a.k_pos0;
+        lse_off = (size_t)b * a.Hq * a.Tq;
+        tile_base = b * ((a.Tk + NK - 1) / NK);
+    }
+    if (q0 >= Tq) return;
+
+    const int t_last = min(q0 + QW, Tq) - 1;
+    const int64_t qp_lo = q_pos0 + q0;
+    const int64_t qp_hi = q_pos0 + t_last;
+    int64_t jlo = 0;
+    if (a.window > 0) jlo = qp_lo - a.window + 1 - k_pos0;
+    if (jlo < 0) jlo = 0;
+    int64_t jhi = qp_hi - k_pos0;
+    if (jhi > Tk - 1) jhi = Tk - 1;
+    const int tile_lo = (int)(jlo / NK);
+    const int tile_hi = jhi >= jlo ? (int)(jhi / NK) : tile_lo - 1;
+
+    u32x4 qr[12];
+    {
+        const int t = q0 + l32;
+        if (t < Tq) {
+            const uint16_t *src = a.q + ((q_tok0 + t) * a.Hq + head) * kDqk + 96 * h2;
+#pragma unroll
+            for (int ks = 0; ks < 12; ++ks) qr[ks] = ldg128(src + 8 * ks);
+            if (h2 == 0) {
+                const int64_t qp = q_pos0 + t;
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) rope_rotate8(qr[cc], qr[cc + 4], a.rt, 8 * cc, qp);
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 12; ++ks) qr[ks] = u32x4{0, 0, 0, 0};
+        }
+    }
+
+    float m_run = a.sinks ? a.sinks[head] * kLog2e : kNegInf;
+    float l_run = (a.sinks && h2 == 0) ? 1.0f : 0.0f;
+    f32x16 O[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) O[mb][e] = 0.0f;
+
+    // ---- a tile's image is STAGE contiguous elements: OPS copies of 1 KiB, op i
+    // landing at LDS byte 1024 * i of the stage; wave w issues ops w, w + NW, ...
+    auto copy_tile = [&](int jt, int buf) {
+        const size_t tile_id = (size_t)(tile_base + jt) * a.Hkv + g;
+        const char *src = reinterpret_cast<const char *>(a.kv_img + tile_id * STAGE) + lane * 16;
+        uint16_t *dst = smem + buf * STAGE;
+#pragma unroll
+        for (int m = 0; m < OPW; ++m) {
+            const int op = w + NW * m;
+            if (op < OPS)
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src + op * 1024),
+                                                 (__attribute__((address_space(3))) void *)(dst + op * 512),
+                                                 16, 0, 0);
+        }
+    };
+
+    const float cl2 = a.scale_log2;
+    const int prow = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+    const int64_t qp = q_pos0 + q0 + l32;
+
+    auto qk = [&](int buf, f32x16 (&S)[KB]) {
+        const uint16_t *Ks = smem + buf * STAGE;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) S[kb][e] = 0.0f;
+        const uint16_t *kr0 = Ks + prow * KSTR + 96 * h2;
+        auto kaddr = [&](int i) { return kr0 + (i % KB) * 32 * KSTR + 8 * (i / KB); };
+        u32x4 kf[RING];
+#pragma unroll
+        for (int i = 0; i < RING; ++i) kf[i] = lds128(kaddr(i));
+#pragma unroll
+        for (int i = 0; i < 12 * KB; ++i) {
+            S[i % KB] = mfma32(kf[i % RING], qr[i / KB], S[i % KB]);
+            if (i + RING < 12 * KB) kf[i % RING] = lds128(kaddr(i + RING));
+        }
+    };
+
+    auto softmax_pv = [&](f32x16 (&S)[KB], int jt, int buf) {
+        const uint16_t *Vs = smem + buf * STAGE + K_TILE;
+        const int j0 = jt * NK;
+        const int64_t kp0 = k_pos0 + j0;
+        const bool full = (j0 + NK <= Tk) && (kp0 + NK - 1 <= qp_lo) &&
+                          (a.window == 0 || qp_hi - kp0 < a.window);
+        if (!full) {
+            int64_t d64 = qp - kp0;
+            d64 = d64 < -(1 << 30) ? -(1 << 30) : (d64 > (1 << 30) ? (1 << 30) : d64);
+            const int d = (int)d64;
+            const int kmax = Tk - j0;
+            const int win = a.window > 0 ? a.window : 0x7fffffff;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int jrel = 32 * kb + 16 * (e >> 3) + 8 * h2 + (e & 7);
+                    const bool vis = (jrel < kmax) && (jrel <= d) && (d - jrel < win);
+                    if (!vis) S[kb][e] = kNegInf;
+                }
+        }
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, S[kb][e]);
+        mx = max_xor32(mx);
+        const float mc = mx * cl2;
+        const bool need = mc > m_run + 8.0f;
+        if (__any(need)) {
+            const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mc) : 1.0f;
+            if (need) m_run = mc;
+            l_run *= alpha;
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) O[mb][e] *= alpha;
+        }
+        const float mu = (m_run == kNegInf) ? 0.0f : m_run;
+        u32x4 Pm[KB][2];
+        float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e], cl2, -mu));
+                S[kb][e] = p;
+                ls[e & 3] += p;
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    Pm[kb][s][x] = pack_bf16(S[kb][8 * s + 2 * x], S[kb][8 * s + 2 * x + 1]);
+        }
+        l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        const uint16_t *vr0 = Vs + l32 * VSTR + 8 * h2;
+        auto vaddr = [&](int i) {
+            const int mb = i / (2 * KB), kb = (i / 2) % KB, s = i & 1;
+            return vr0 + mb * 32 * VSTR + 32 * kb + 16 * s;
+        };
+        u32x4 vf[RING];
+#pragma unroll
+        for (int i = 0; i < RING; ++i) vf[i] = lds128(vaddr(i));
+#pragma unroll
+        for (int i = 0; i < 8 * KB; ++i) {
+            O[i / (2 * KB)] = mfma32(vf[i % RING], Pm[(i / 2) % KB][i & 1], O[i / (2 * KB)]);
+            if (i + RING < 8 * KB) vf[i % RING] = lds128(vaddr(i + RING));
+        }
+    };
+
+    f32x16 S[KB];
+    if (tile_hi >= tile_lo) copy_tile(tile_lo, 0);
+    __syncthreads();
+    for (int jt = tile_lo; jt <= tile_hi; ++jt) {
+        const int buf = (jt - tile_lo) & 1;
+        if (jt < tile_hi) copy_tile(jt + 1, buf ^ 1);   // buffer buf ^ 1 was last read before the barrier
+        qk(buf, S);
+        softmax_pv(S, jt, buf);
+        __syncthreads();   // also waits for this wave's copies of tile jt + 1
+    }
+
+    const float lt = sum_xor32(l_run);
+    const int t = q0 + l32;
+    if (t < Tq) {
+        const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
+        uint16_t *dst = a.out + ((q_tok0 + t) * a.Hq + head) * kDv;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                u32x2 o;
+                o[0] = pack_bf16(O[mb][4 * a4] * inv, O[mb][4 * a4 + 1] * inv);
+                o[1] = pack_bf16(O[mb][4 * a4 + 2] * inv, O[mb][4 * a4 + 3] * inv);
+                *reinterpret_cast<u32x2 *>(dst + 32 * mb + 8 * a4 + 4 * h2) = o;
+            }
+        if (a.lse && h2 == 0)
+            a.lse[lse_off + (size_t)head * a.lse_hstride + t] = lt > 0.0f ? (m_run + log2f(lt)) * kLn2 : kNegInf;
+    }
+}
+
 // ---- Sliding-window band kernel (window <= 128, 8 query heads per KV head).
 // One workgroup = the 8 query heads of one KV head (one wave each, two waves per
 // SIMD) of one sequence, walking a run of consecutive 32-query blocks.  The 32-key
@@ -771,7 +1088,32 @@ static hipError_t launch_variant(PrefillArgs a, hipStream_t stream) {
 #define MIMO_PREFILL_BAND 1
 #endif
 
+size_t prefill_image_bytes(int32_t B, int64_t total_k, int32_t Hkv) {
+    return (size_t)((total_k + kImgNK - 1) / kImgNK + B) * Hkv * kImgTile * sizeof(uint16_t);
+}
+
+static hipError_t launch_image(PrefillArgs a, hipStream_t stream) {
+    const int QW = 32, NW = 8;
+    const int G = a.Hq / a.Hkv;
+    a.n_qblk = (a.Tq + QW - 1) / QW;
+    a.n_hgrp = G / NW;
+    // dense: one workgroup per tile; packed: a fixed grid striding over each
+    // sequence's tiles (their count is only known on the device)
+    int tiles = a.cu_k ? 64 : (a.Tk + kImgNK - 1) / kImgNK;
+    if (tiles > 65535) tiles = 65535;
+    if (tiles < 1) tiles = 1;
+    hipLaunchKernelGGL(kv_image_kernel, dim3(tiles, a.B, a.Hkv), dim3(256), 0, stream, a);
+    const int64_t combos = (int64_t)a.B * a.Hkv * a.n_hgrp;
+    const int64_t blocks = combos * a.n_qblk;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    a.xcd_remap = ((a.Hkv * a.n_hgrp) % 8 == 0) ? 2 : (combos % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL((prefill_image_kernel<8>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill(PrefillArgs a, hipStream_t stream) {
+    // Global layers given a tile-image workspace: image pass + DMA-staged kernel.
+    if (a.kv_img && a.window == 0 && (a.Hq / a.Hkv) % 8 == 0) return launch_image(a, stream);
     // GQA group sizes are multiples of 4 (checked by the caller).  Sliding
     // windows see a short band of keys: 4 heads x 32-key tiles, two workgroups
     // per CU.  Global prefixes are long: 8 heads share each 64-key tile.

@@ -54,7 +54,7 @@ typedef enum mimo_status {
     MIMO_OK = 0,
     MIMO_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, inconsistent sizes */
     MIMO_ERR_UNSUPPORTED = 2,      /* head geometry the kernels are not built for */
-    MIMO_ERR_WORKSPACE = 3,        /* decode workspace missing or too small */
+    MIMO_ERR_WORKSPACE = 3,        /* workspace missing or too small */
     MIMO_ERR_HIP = 4               /* the HIP runtime refused a launch */
 } mimo_status;
 
@@ -102,6 +102,18 @@ mimo_status mimo_attn_prefill_swa(const mimo_attn_cfg *cfg, const uint16_t *q, c
                                   int64_t pos0, uint16_t *out, float *lse, void *stream);
 
 /*
+ * Workspace of the global-layer prefill calls (mimo_attn_prefill_global, and
+ * mimo_attn_prefill_varlen with cfg->window == 0): room for one image per 64-key
+ * tile and KV head, holding the tile's rotated K and transposed V exactly as the
+ * attention kernel keeps them in LDS, so that each tile is rotated and transposed
+ * once per call rather than once per workgroup that reads it.  total_k is the
+ * number of key tokens over the batch (B * Tk for a dense call, the row count of k
+ * for a packed one).  Returns 0 where the images are not used (sliding windows,
+ * GQA groups that are not a multiple of 8) or the arguments are invalid.
+ */
+size_t mimo_attn_prefill_workspace_size(const mimo_attn_cfg *cfg, int32_t B, int64_t total_k);
+
+/*
  * Global causal prefill of one query chunk against its whole prefix (the tiled
  * global-attention prefill of the Gaudi recipe page, Launch section: query tiles
  * instead of a dense bias).
@@ -109,11 +121,17 @@ mimo_status mimo_attn_prefill_swa(const mimo_attn_cfg *cfg, const uint16_t *q, c
  *   k, v  : [B, Tk, num_kv_heads, 192|128], key j has position j
  *   Tk must equal q_pos0 + Tq (each chunk sees its full prefix).
  *   out   : [B, Tq, num_q_heads, 128] bf16;  lse : [B, num_q_heads, Tq] fp32 or NULL.
+ *   ws    : device workspace of at least mimo_attn_prefill_workspace_size(cfg, B,
+ *           B * Tk) bytes, not overlapping any other argument, owned by the caller and
+ *           overwritten by the call; or NULL, which stages every tile inside the
+ *           attention kernel instead (same results up to the rounding of the
+ *           rotated keys, slower).  A smaller non-NULL ws is MIMO_ERR_WORKSPACE.
  * Needs cfg->window == 0.
  */
 mimo_status mimo_attn_prefill_global(const mimo_attn_cfg *cfg, const uint16_t *q, const uint16_t *k,
                                      const uint16_t *v, int32_t B, int32_t Tq, int32_t Tk,
-                                     int64_t q_pos0, uint16_t *out, float *lse, void *stream);
+                                     int64_t q_pos0, uint16_t *out, float *lse, void *ws,
+                                     size_t ws_bytes, void *stream);
 
 /*
  * Prefill of packed variable-length sequences (THD layout), which also covers
@@ -133,9 +151,14 @@ mimo_status mimo_attn_prefill_global(const mimo_attn_cfg *cfg, const uint16_t *q
  *   sink included).
  *   cu_seqlens_q / cu_seqlens_k : [B+1] int32 device arrays, non-decreasing,
  *   starting at 0;  k_pos0 : [B] int64 device array or NULL.
+ *   total_k : rows of k and v.
+ *   ws      : with cfg->window == 0, as for mimo_attn_prefill_global with
+ *             mimo_attn_prefill_workspace_size(cfg, B, total_k) bytes (or NULL);
+ *             ignored on sliding layers.
  * The caller guarantees, for every b: 0 <= Tq_b <= Tk_b, Tq_b <= max_seqlen_q,
- * cu_seqlens_q[B] <= total_q, and positions >= 0.  These device values are not
- * read on the host; rows of a sequence past max_seqlen_q are left unwritten.
+ * cu_seqlens_q[B] <= total_q, cu_seqlens_k[B] <= total_k, and positions >= 0.
+ * These device values are not read on the host; rows of a sequence past
+ * max_seqlen_q are left unwritten.
  * The attention runs over the keys given: a sliding chunk must carry the
  * min(window - 1, P) keys before its first query, a global chunk its whole
  * prefix (P_b = 0).
@@ -144,7 +167,8 @@ mimo_status mimo_attn_prefill_varlen(const mimo_attn_cfg *cfg, const uint16_t *q
                                      const uint16_t *v, const float *sinks, int32_t B,
                                      const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
                                      const int64_t *k_pos0, int32_t max_seqlen_q, int32_t total_q,
-                                     uint16_t *out, float *lse, void *stream);
+                                     int64_t total_k, uint16_t *out, float *lse, void *ws,
+                                     size_t ws_bytes, void *stream);
 
 /*
  * One decode query per sequence over a KV cache (window-sized ring on sliding

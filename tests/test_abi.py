@@ -65,8 +65,9 @@ def swa(lib, cfg, q=FAKE, k=FAKE, v=FAKE, sinks=FAKE, Bn=1, T=16, pos0=0, out=FA
     return lib.mimo_attn_prefill_swa(ctypes.byref(cfg), q, k, v, sinks, Bn, T, pos0, out, None, None)
 
 
-def glob(lib, cfg, Bn=1, Tq=16, Tk=16, q_pos0=0, q=FAKE, out=FAKE):
-    return lib.mimo_attn_prefill_global(ctypes.byref(cfg), q, FAKE, FAKE, Bn, Tq, Tk, q_pos0, out, None, None)
+def glob(lib, cfg, Bn=1, Tq=16, Tk=16, q_pos0=0, q=FAKE, out=FAKE, ws=None, ws_bytes=0):
+    return lib.mimo_attn_prefill_global(ctypes.byref(cfg), q, FAKE, FAKE, Bn, Tq, Tk, q_pos0, out, None, ws,
+                                        ws_bytes, None)
 
 
 def test_null_cfg(lib):
@@ -111,9 +112,9 @@ def test_global_prefill_contract(lib):
     assert glob(lib, cfg_glob(), Tq=0, Tk=0, q=None, out=None) == OK
 
 
-def varlen(lib, cfg, Bn=2, max_q=64, total_q=128, q=FAKE, cu_q=FAKE, cu_k=FAKE):
+def varlen(lib, cfg, Bn=2, max_q=64, total_q=128, q=FAKE, cu_q=FAKE, cu_k=FAKE, total_k=256, ws=None, ws_bytes=0):
     return lib.mimo_attn_prefill_varlen(ctypes.byref(cfg), q, FAKE, FAKE, None, Bn, cu_q, cu_k, None, max_q,
-                                        total_q, FAKE, None, None)
+                                        total_q, total_k, FAKE, None, ws, ws_bytes, None)
 
 
 def test_varlen_prefill_contract(lib):
@@ -127,6 +128,33 @@ def test_varlen_prefill_contract(lib):
     # nothing to do is valid with NULL data
     assert varlen(lib, cfg_swa(), Bn=0, q=None, cu_q=None, cu_k=None) == OK
     assert varlen(lib, cfg_glob(), max_q=0, total_q=0, q=None) == OK
+
+
+# One image per 64-key tile and KV head: K rows of 192 + 8 pad elements, then V^T rows
+# of 64 + 8, all bf16; a packed call may start each sequence on a fresh tile.
+IMAGE_BYTES = (64 * 200 + 128 * 72) * 2
+
+
+def test_prefill_workspace_size(lib):
+    size = lambda cfg, b, tk: lib.mimo_attn_prefill_workspace_size(ctypes.byref(cfg), b, tk)
+    assert IMAGE_BYTES == 44032
+    assert size(cfg_glob(), 1, 32768) == (512 + 1) * 4 * IMAGE_BYTES
+    assert size(cfg_glob(), 4, 4 * 1000) == (63 + 4) * 4 * IMAGE_BYTES
+    # a dense batch of B sequences of Tk keys fits in the size for B * Tk keys
+    for b, tk in ((1, 1), (3, 63), (3, 65), (2, 8192), (5, 777)):
+        assert size(cfg_glob(), b, b * tk) >= b * -(-tk // 64) * 4 * IMAGE_BYTES
+    assert size(cfg_swa(), 1, 32768) == 0                                  # sliding layers stage in-kernel
+    assert size(cfg_glob(num_q_heads=16), 1, 4096) == 0                     # GQA group 4
+    assert size(cfg_glob(num_kv_heads=7), 1, 4096) == 0                     # invalid cfg
+    assert size(cfg_glob(), 0, 4096) == 0 and size(cfg_glob(), 1, 0) == 0
+
+
+def test_prefill_workspace_too_small(lib):
+    need = lib.mimo_attn_prefill_workspace_size(ctypes.byref(cfg_glob()), 1, 16)
+    assert glob(lib, cfg_glob(), ws=FAKE, ws_bytes=need - 1) == WS
+    assert "workspace" in err(lib)
+    assert varlen(lib, cfg_glob(), total_k=256, ws=FAKE, ws_bytes=4096) == WS
+    assert varlen(lib, cfg_glob(), total_k=-1) == INVAL
 
 
 def dec(lib, cfg, S=4, cap=128, ws=FAKE, ws_bytes=1 << 30, q=FAKE):

@@ -49,11 +49,13 @@ def test_swa_prefill_b4_t8192():
     assert_parity(got, ref, f"{len(rows)} rows x 4 seqs")
 
 
-def test_global_prefill_t32768():
-    say("full-size global prefill T=32768")
+@pytest.mark.parametrize("images", [True, False], ids=["images", "staged"])
+def test_global_prefill_t32768(images):
+    say(f"full-size global prefill T=32768 images={images}")
     d = gen.prefill_inputs(1, 32768, 64, 4, seed=1002, with_sinks=False)
     out = torch.empty((1, 32768, 64, 128), dtype=torch.bfloat16, device="cuda")
-    Bd.mimo_attn_prefill_global(Bd.global_cfg(), dev_bf16(d["q"]), dev_bf16(d["k"]), dev_bf16(d["v"]), out)
+    Bd.mimo_attn_prefill_global(Bd.global_cfg(), dev_bf16(d["q"]), dev_bf16(d["k"]), dev_bf16(d["v"]), out,
+                                ws=None if images else False)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(out).all())
     rows = sample_rows(32768, 12, 2, must=(16383, 16384))

@@ -129,12 +129,18 @@ def test_prefill_swa_sink_dominates():
     assert_parity(got, ref, "out")
 
 
-def run_global(q, k, v, hq, hkv, q_pos0=0, want_lse=False):
+def run_global(q, k, v, hq, hkv, q_pos0=0, want_lse=False, images=True):
+    """images: give the call a tile-image workspace, filled with 0xFF bytes (NaN
+    bf16) so that any image byte the kernels read without writing shows up."""
     B, Tq = q.shape[:2]
     out = torch.empty((B, Tq, hq, 128), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, hq, Tq), dtype=torch.float32, device="cuda") if want_lse else None
-    Bd.mimo_attn_prefill_global(cfg_for(hq, hkv, 0, 1e7), dev_bf16(q), dev_bf16(k), dev_bf16(v), out,
-                                q_pos0=q_pos0, lse=lse)
+    cfg = cfg_for(hq, hkv, 0, 1e7)
+    ws = False
+    if images:
+        n = Bd.mimo_attn_prefill_workspace_size(cfg, B, B * k.shape[1])
+        ws = torch.full((max(n, 1),), 255, dtype=torch.uint8, device="cuda") if n else False
+    Bd.mimo_attn_prefill_global(cfg, dev_bf16(q), dev_bf16(k), dev_bf16(v), out, q_pos0=q_pos0, lse=lse, ws=ws)
     torch.cuda.synchronize()
     return (host_f64(out), lse.cpu().numpy().astype(np.float64)) if want_lse else host_f64(out)
 
@@ -149,13 +155,14 @@ GLOBAL_CASES = [
 ]
 
 
+@pytest.mark.parametrize("images", [True, False], ids=["images", "staged"])
 @pytest.mark.parametrize("B,T,q_pos0,heads", GLOBAL_CASES)
-def test_prefill_global(B, T, q_pos0, heads):
+def test_prefill_global(B, T, q_pos0, heads, images):
     hq, hkv = heads
-    say(f"prefill_global B={B} Tk={T} q_pos0={q_pos0} heads={heads}")
+    say(f"prefill_global B={B} Tk={T} q_pos0={q_pos0} heads={heads} images={images}")
     d = gen.prefill_inputs(B, T, hq, hkv, seed=4000 + T, with_sinks=False)
     q = d["q"][:, q_pos0:]
-    got, lse = run_global(q, d["k"], d["v"], hq, hkv, q_pos0=q_pos0, want_lse=True)
+    got, lse = run_global(q, d["k"], d["v"], hq, hkv, q_pos0=q_pos0, want_lse=True, images=images)
     ref, rlse = oracle.prefill_global(q, d["k"], d["v"], q_pos0=q_pos0, base=1e7, want_lse=True)
     assert_parity(got, ref, "out")
     assert np.max(np.abs(lse - rlse.transpose(0, 2, 1))) < 1e-2

@@ -19,8 +19,14 @@ def cfg_for(hq, hkv, window, base):
     return Bd.MimoAttnCfg(hq, hkv, 192, 128, 64, base, 1.0 / math.sqrt(192.0), 0.707, window)
 
 
-def run_varlen(d, cfg, max_q=None, want_lse=True, out_fill=None):
+def run_varlen(d, cfg, max_q=None, want_lse=True, out_fill=None, images=True):
+    """images: global layers get a tile-image workspace filled with 0xFF bytes (NaN
+    bf16), so any image byte read without being written shows up."""
     total_q, hq = d["q"].shape[:2]
+    ws = False
+    if images:
+        n = Bd.mimo_attn_prefill_workspace_size(cfg, len(d["cu_q"]) - 1, d["k"].shape[0])
+        ws = torch.full((n,), 255, dtype=torch.uint8, device="cuda") if n else False
     lens_q = np.diff(d["cu_q"])
     max_q = int(lens_q.max()) if max_q is None else max_q
     out = torch.empty((total_q, hq, 128), dtype=torch.bfloat16, device="cuda")
@@ -30,7 +36,7 @@ def run_varlen(d, cfg, max_q=None, want_lse=True, out_fill=None):
     Bd.mimo_attn_prefill_varlen(cfg, dev_bf16(d["q"]), dev_bf16(d["k"]), dev_bf16(d["v"]),
                                 None if d["sinks"] is None else dev(d["sinks"]), dev(d["cu_q"]),
                                 dev(d["cu_k"]), max_q, out,
-                                k_pos0=None if d["k_pos0"] is None else dev(d["k_pos0"]), lse=lse)
+                                k_pos0=None if d["k_pos0"] is None else dev(d["k_pos0"]), lse=lse, ws=ws)
     torch.cuda.synchronize()
     return out, lse
 
@@ -46,7 +52,7 @@ def check_against_oracle(d, cfg, out, lse, what):
         assert err.max() < 1e-2
 
 
-@pytest.mark.parametrize("layer", ["sliding", "global"])
+@pytest.mark.parametrize("layer", ["sliding", "global", "global-staged"])
 def test_thd_ragged_sequences(layer):
     """Several packed sequences of ragged lengths (one token, tile edges, an empty
     one, several tiles), each starting at its own position."""
@@ -59,7 +65,7 @@ def test_thd_ragged_sequences(layer):
         pos0 = [0] * len(lens)   # a global chunk holding its whole prefix starts at 0
     d = gen.varlen_inputs(lens, lens, 64, hkv, seed=7001, with_sinks=sinks, k_pos0=pos0)
     say(f"varlen {layer}: lens {lens}")
-    out, lse = run_varlen(d, cfg)
+    out, lse = run_varlen(d, cfg, images=layer != "global-staged")
     check_against_oracle(d, cfg, out, lse, f"{layer} THD")
 
 
@@ -87,11 +93,14 @@ def test_global_chunk_continuation():
     check_against_oracle(d, cfg_for(64, 4, 0, 1e7), out, lse, "global chunks")
 
 
-@pytest.mark.parametrize("layer", ["sliding", "global"])
+@pytest.mark.parametrize("layer", ["sliding", "global", "global-staged"])
 def test_packed_equals_dense_bitwise(layer):
-    """Dense batches and the same batches packed run the same kernel: identical bits."""
+    """Dense batches and the same batches packed run the same kernel: identical bits
+    (global layers with tile images, whose tiles then sit at other places of the
+    workspace, and without)."""
     B, T = 2, 384
     sliding = layer == "sliding"
+    ws = False if layer == "global-staged" else None
     hkv = 8 if sliding else 4
     cfg = cfg_for(64, hkv, 128 if sliding else 0, 1e4 if sliding else 1e7)
     d = gen.prefill_inputs(B, T, 64, hkv, seed=7004, with_sinks=sliding)
@@ -101,12 +110,12 @@ def test_packed_equals_dense_bitwise(layer):
     if sliding:
         Bd.mimo_attn_prefill_swa(cfg, q, k, v, dev(d["sinks"]), dense, lse=dlse)
     else:
-        Bd.mimo_attn_prefill_global(cfg, q, k, v, dense, lse=dlse)
+        Bd.mimo_attn_prefill_global(cfg, q, k, v, dense, lse=dlse, ws=ws)
     cu = dev(np.array([0, T, 2 * T], np.int32))
     packed = torch.empty((B * T, 64, 128), dtype=torch.bfloat16, device="cuda")
     plse = torch.empty((64, B * T), dtype=torch.float32, device="cuda")
     Bd.mimo_attn_prefill_varlen(cfg, q.view(B * T, 64, 192), k.view(B * T, hkv, 192), v.view(B * T, hkv, 128),
-                                dev(d["sinks"]) if sliding else None, cu, cu, T, packed, lse=plse)
+                                dev(d["sinks"]) if sliding else None, cu, cu, T, packed, lse=plse, ws=ws)
     torch.cuda.synchronize()
     assert np.array_equal(host_bits(dense).reshape(B * T, 64, 128), host_bits(packed))
     assert torch.equal(dlse.permute(1, 0, 2).reshape(64, B * T), plse)
