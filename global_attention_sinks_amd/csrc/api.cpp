@@ -197,7 +197,8 @@ mimo_status mimo_attn_prefill_varlen(const mimo_attn_cfg *cfg, const uint16_t *q
         return fail(MIMO_ERR_INVALID_ARGUMENT, "q, k, v, out, cu_seqlens_q and cu_seqlens_k must be non-NULL");
     PrefillArgs a{};
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.sinks = sinks;
-    a.B = B; a.Tq = max_seqlen_q; a.Tk = 0; a.Hq = cfg->num_q_heads; a.Hkv = cfg->num_kv_heads;
+    a.B = B; a.Tq = max_seqlen_q; a.Hq = cfg->num_q_heads; a.Hkv = cfg->num_kv_heads;
+    a.Tk = total_k > INT32_MAX ? INT32_MAX : (int32_t)total_k;   // packed: bounds every sequence's keys
     a.window = cfg->window; a.lse_hstride = total_q;
     a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k; a.kpos = k_pos0;
     a.scale_log2 = scale_log2(cfg); a.v_scale = cfg->v_scale;

@@ -42,7 +42,7 @@ struct PrefillArgs {
     // packed sequences (all NULL for dense batches): sequence b owns query tokens
     // cu_q[b]..cu_q[b+1]-1 and key tokens cu_k[b]..cu_k[b+1]-1, its first key sits
     // at position kpos[b] (0 if kpos is NULL) and its queries are its last keys;
-    // Tq is then the longest query count
+    // Tq is then the longest query count and Tk the total key count
     const int32_t *cu_q, *cu_k;
     const int64_t *kpos;
     int64_t lse_hstride;  // lse element stride between heads

@@ -1097,12 +1097,14 @@ static hipError_t launch_image(PrefillArgs a, hipStream_t stream) {
     const int G = a.Hq / a.Hkv;
     a.n_qblk = (a.Tq + QW - 1) / QW;
     a.n_hgrp = G / NW;
-    // dense: one workgroup per tile; packed: a fixed grid striding over each
-    // sequence's tiles (their count is only known on the device)
-    int tiles = a.cu_k ? 64 : (a.Tk + kImgNK - 1) / kImgNK;
+    // one workgroup per tile of the longest sequence (packed: Tk is the total key
+    // count, which bounds it; the count of each sequence is only known on the
+    // device), capped; workgroups stride over the tiles of their own sequence
+    int64_t tiles = ((int64_t)a.Tk + kImgNK - 1) / kImgNK;
+    if (a.cu_k && tiles > 4096) tiles = 4096;
     if (tiles > 65535) tiles = 65535;
     if (tiles < 1) tiles = 1;
-    hipLaunchKernelGGL(kv_image_kernel, dim3(tiles, a.B, a.Hkv), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(kv_image_kernel, dim3((unsigned)tiles, a.B, a.Hkv), dim3(256), 0, stream, a);
     const int64_t combos = (int64_t)a.B * a.Hkv * a.n_hgrp;
     const int64_t blocks = combos * a.n_qblk;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
