@@ -133,3 +133,40 @@ def test_rows_past_max_seqlen_are_left_alone():
                                 base=1e4)
     rows = np.r_[0:64, 100:140]
     assert_parity(got[rows], ref[rows], "rows below max_seqlen_q")
+
+
+def test_one_workspace_across_global_calls():
+    """A tile-image workspace sized for the largest call serves calls of other shapes
+    in turn (dense, packed, dense again): each call rewrites the images it reads."""
+    cfg = cfg_for(64, 4, 0, 1e7)
+    d1 = gen.prefill_inputs(1, 700, 64, 4, seed=7010, with_sinks=False)
+    d2 = gen.varlen_inputs([40, 300, 1], [40 + 250, 300, 1], 64, 4, seed=7011, with_sinks=False)
+    d3 = gen.prefill_inputs(2, 130, 64, 4, seed=7012, with_sinks=False)
+    n = max(Bd.mimo_attn_prefill_workspace_size(cfg, 1, 700),
+            Bd.mimo_attn_prefill_workspace_size(cfg, 3, d2["k"].shape[0]),
+            Bd.mimo_attn_prefill_workspace_size(cfg, 2, 260))
+    ws = torch.full((n,), 255, dtype=torch.uint8, device="cuda")
+
+    def dense(d, q_pos0):
+        B, Tk = d["k"].shape[:2]
+        out = torch.empty((B, Tk - q_pos0, 64, 128), dtype=torch.bfloat16, device="cuda")
+        Bd.mimo_attn_prefill_global(cfg, dev_bf16(d["q"][:, q_pos0:]), dev_bf16(d["k"]), dev_bf16(d["v"]), out,
+                                    q_pos0=q_pos0, ws=ws)
+        torch.cuda.synchronize()
+        ref = oracle.prefill_global(d["q"][:, q_pos0:], d["k"], d["v"], q_pos0=q_pos0, base=1e7)
+        return host_f64(out), ref
+
+    say("one workspace: dense B=1 Tk=700 (chunk at 300)")
+    got, ref = dense(d1, 300)
+    assert_parity(got, ref, "dense 700")
+    say("one workspace: packed 3 sequences")
+    total_q = d2["q"].shape[0]
+    out = torch.empty((total_q, 64, 128), dtype=torch.bfloat16, device="cuda")
+    Bd.mimo_attn_prefill_varlen(cfg, dev_bf16(d2["q"]), dev_bf16(d2["k"]), dev_bf16(d2["v"]), None, dev(d2["cu_q"]),
+                                dev(d2["cu_k"]), 300, out, ws=ws)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_varlen(d2["q"], d2["k"], d2["v"], d2["cu_q"], d2["cu_k"], window=0, base=1e7)
+    assert_parity(host_f64(out), ref, "packed")
+    say("one workspace: dense B=2 Tk=130")
+    got, ref = dense(d3, 0)
+    assert_parity(got, ref, "dense 2 x 130")
