@@ -151,6 +151,8 @@ static mimo_status attach_images(PrefillArgs &a, const mimo_attn_cfg *cfg, int32
     if (ws_bytes < need)
         return fail(MIMO_ERR_WORKSPACE, "prefill workspace needs %zu bytes (got %zu)", need, ws_bytes);
     a.kv_img = static_cast<uint16_t *>(ws);
+    a.kv_norm = reinterpret_cast<float *>(static_cast<char *>(ws) +
+                                          prefill_image_norm_offset(B, total_k, cfg->num_kv_heads));
     return ok();
 }
 

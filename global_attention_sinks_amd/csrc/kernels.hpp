@@ -53,7 +53,12 @@ struct PrefillArgs {
     // prefill_image_bytes() for the rotated-K / transposed-V tile images, or NULL to
     // stage each tile inside the attention kernel
     uint16_t *kv_img;
+    float *kv_norm;       // largest key norm of each tile image (same index), with kv_img
 };
+// Tile images a global prefill over B sequences of total_k keys may use, and the
+// workspace they take: the images, then one fp32 norm per image.
+size_t prefill_image_count(int32_t B, int64_t total_k, int32_t Hkv);
+size_t prefill_image_norm_offset(int32_t B, int64_t total_k, int32_t Hkv);   // bytes before the norms
 size_t prefill_image_bytes(int32_t B, int64_t total_k, int32_t Hkv);
 hipError_t launch_prefill(PrefillArgs a, hipStream_t stream);
 

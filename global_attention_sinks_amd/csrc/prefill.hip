@@ -467,9 +467,23 @@ constexpr int kPrepVS = kDv + 8;                             // V row stride whi
 constexpr int kImgVS = kImgNK + 8;                           // V^T row stride in the image
 constexpr int kImgK = kImgNK * KSTR;                         // bf16 elements
 constexpr int kImgTile = kImgK + kDv * kImgVS;               // 22016 bf16 = 43 KiB
+constexpr float kSkipMax = 32.0f;   // exp2-domain headroom before the row max is needed
+
+// Sum of squares of 8 bf16 values.
+__device__ __forceinline__ float sumsq8(u32x4 x) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = bf_lo(x[i]), hi = bf_hi(x[i]);
+        s = __builtin_fmaf(lo, lo, s);
+        s = __builtin_fmaf(hi, hi, s);
+    }
+    return s;
+}
 
 __global__ __launch_bounds__(256) void kv_image_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t vs[kImgNK * kPrepVS];
+    __shared__ float rn[kImgNK];   // squared norm of each rotated key row of the tile
     const int b = blockIdx.y, g = blockIdx.z, tid = threadIdx.x;
     int Tk, tile_base;
     size_t k_tok0;
@@ -488,6 +502,8 @@ __global__ __launch_bounds__(256) void kv_image_kernel(PrefillArgs a) {
     }
     const int ntile = (Tk + kImgNK - 1) / kImgNK;
     const size_t krow = (size_t)a.Hkv * kDqk, vrow = (size_t)a.Hkv * kDv;
+    if (tid < kImgNK) rn[tid] = 0.0f;
+    __syncthreads();
     for (int t = blockIdx.x; t < ntile; t += gridDim.x) {
         const size_t tile_id = (size_t)(tile_base + t) * a.Hkv + g;
         uint16_t *wk = a.kv_img + tile_id * kImgTile;
@@ -504,6 +520,7 @@ __global__ __launch_bounds__(256) void kv_image_kernel(PrefillArgs a) {
             }
             *reinterpret_cast<u32x4 *>(wk + row * KSTR + 8 * cc) = x;
             *reinterpret_cast<u32x4 *>(wk + row * KSTR + 32 + 8 * cc) = y;
+            atomicAdd(&rn[row], sumsq8(x) + sumsq8(y));
         }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {   // pass-through chunks 8..23
@@ -511,6 +528,7 @@ __global__ __launch_bounds__(256) void kv_image_kernel(PrefillArgs a) {
             u32x4 x = {0, 0, 0, 0};
             if (j < Tk) x = ldg128(a.k + (k_tok0 + j) * krow + (size_t)g * kDqk + 8 * c);
             *reinterpret_cast<u32x4 *>(wk + row * KSTR + 8 * c) = x;
+            atomicAdd(&rn[row], sumsq8(x));
         }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {   // V rows into LDS
@@ -520,6 +538,13 @@ __global__ __launch_bounds__(256) void kv_image_kernel(PrefillArgs a) {
             *reinterpret_cast<u32x4 *>(vs + row * kPrepVS + 8 * c) = x;
         }
         __syncthreads();
+        if (tid < kImgNK) {   // wave 0: the tile's largest key norm; clear for the next tile
+            float n = sqrtf(rn[tid]);
+            rn[tid] = 0.0f;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) n = fmaxf(n, __shfl_xor(n, off));
+            if (tid == 0) a.kv_norm[tile_id] = n;
+        }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {   // V^T rows: dv, keys 8c..8c+7
             const int u = tid + 256 * m, dv = u >> 3, c = u & 7;
@@ -621,6 +646,15 @@ void prefill_image_kernel(PrefillArgs a) {
         }
     }
 
+    // |q| * scale * log2(e): with a tile's largest |k| it bounds every score of the
+    // tile in the exp2 domain (Cauchy-Schwarz)
+    float qbound;
+    {
+        float qss = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < 12; ++ks) qss += sumsq8(qr[ks]);
+        qbound = sqrtf(sum_xor32(qss)) * a.scale_log2;
+    }
     float m_run = a.sinks ? a.sinks[head] * kLog2e : kNegInf;
     float l_run = (a.sinks && h2 == 0) ? 1.0f : 0.0f;
     f32x16 O[4];
@@ -667,7 +701,7 @@ void prefill_image_kernel(PrefillArgs a) {
         }
     };
 
-    auto softmax_pv = [&](f32x16 (&S)[KB], int jt, int buf) {
+    auto softmax_pv = [&](f32x16 (&S)[KB], int jt, int buf, float kn) {
         const uint16_t *Vs = smem + buf * STAGE + K_TILE;
         const int j0 = jt * NK;
         const int64_t kp0 = k_pos0 + j0;
@@ -688,22 +722,27 @@ void prefill_image_kernel(PrefillArgs a) {
                     if (!vis) S[kb][e] = kNegInf;
                 }
         }
-        float mx = kNegInf;
+        // The row max is only needed when a score could exceed the running max by
+        // more than 2^kSkipMax in the exp2 domain (fp32 holds such terms easily):
+        // interior tiles whose norm bound rules that out skip it.
+        if (!full || __any(qbound * kn > m_run + kSkipMax)) {
+            float mx = kNegInf;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, S[kb][e]);
-        mx = max_xor32(mx);
-        const float mc = mx * cl2;
-        const bool need = mc > m_run + 8.0f;
-        if (__any(need)) {
-            const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mc) : 1.0f;
-            if (need) m_run = mc;
-            l_run *= alpha;
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, S[kb][e]);
+            mx = max_xor32(mx);
+            const float mc = mx * cl2;
+            const bool need = mc > m_run + 8.0f;
+            if (__any(need)) {
+                const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mc) : 1.0f;
+                if (need) m_run = mc;
+                l_run *= alpha;
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
+                for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) O[mb][e] *= alpha;
+                    for (int e = 0; e < 16; ++e) O[mb][e] *= alpha;
+            }
         }
         const float mu = (m_run == kNegInf) ? 0.0f : m_run;
         u32x4 Pm[KB][2];
@@ -738,15 +777,26 @@ void prefill_image_kernel(PrefillArgs a) {
         }
     };
 
+    // a tile's key norm (uniform: a scalar load) is fetched one tile ahead, with the
+    // tile's copies, so no wait in the loop has to cover copies still in flight
+    auto tile_norm = [&](int jt) {
+        return a.kv_norm[__builtin_amdgcn_readfirstlane((tile_base + jt) * a.Hkv + g)];
+    };
     f32x16 S[KB];
-    if (tile_hi >= tile_lo) copy_tile(tile_lo, 0);
+    float kn = 0.0f;
+    if (tile_hi >= tile_lo) {
+        copy_tile(tile_lo, 0);
+        kn = tile_norm(tile_lo);
+    }
     __syncthreads();
     for (int jt = tile_lo; jt <= tile_hi; ++jt) {
         const int buf = (jt - tile_lo) & 1;
         if (jt < tile_hi) copy_tile(jt + 1, buf ^ 1);   // buffer buf ^ 1 was last read before the barrier
+        const float kn_next = tile_norm(min(jt + 1, tile_hi));
         qk(buf, S);
-        softmax_pv(S, jt, buf);
+        softmax_pv(S, jt, buf, kn);
         __syncthreads();   // also waits for this wave's copies of tile jt + 1
+        kn = kn_next;
     }
 
     const float lt = sum_xor32(l_run);
@@ -1088,8 +1138,16 @@ static hipError_t launch_variant(PrefillArgs a, hipStream_t stream) {
 #define MIMO_PREFILL_BAND 1
 #endif
 
+size_t prefill_image_count(int32_t B, int64_t total_k, int32_t Hkv) {
+    return (size_t)((total_k + kImgNK - 1) / kImgNK + B) * Hkv;
+}
+
+size_t prefill_image_norm_offset(int32_t B, int64_t total_k, int32_t Hkv) {
+    return prefill_image_count(B, total_k, Hkv) * kImgTile * sizeof(uint16_t);
+}
+
 size_t prefill_image_bytes(int32_t B, int64_t total_k, int32_t Hkv) {
-    return (size_t)((total_k + kImgNK - 1) / kImgNK + B) * Hkv * kImgTile * sizeof(uint16_t);
+    return prefill_image_norm_offset(B, total_k, Hkv) + prefill_image_count(B, total_k, Hkv) * sizeof(float);
 }
 
 static hipError_t launch_image(PrefillArgs a, hipStream_t stream) {

@@ -105,8 +105,9 @@ mimo_status mimo_attn_prefill_swa(const mimo_attn_cfg *cfg, const uint16_t *q, c
  * Workspace of the global-layer prefill calls (mimo_attn_prefill_global, and
  * mimo_attn_prefill_varlen with cfg->window == 0): room for one image per 64-key
  * tile and KV head, holding the tile's rotated K and transposed V exactly as the
- * attention kernel keeps them in LDS, so that each tile is rotated and transposed
- * once per call rather than once per workgroup that reads it.  total_k is the
+ * attention kernel keeps them in LDS (so that each tile is rotated and transposed
+ * once per call rather than once per workgroup that reads it), and the tile's
+ * largest key norm.  total_k is the
  * number of key tokens over the batch (B * Tk for a dense call, the row count of k
  * for a packed one).  Returns 0 where the images are not used (sliding windows,
  * GQA groups that are not a multiple of 8) or the arguments are invalid.

@@ -131,13 +131,14 @@ def test_varlen_prefill_contract(lib):
 
 
 # One image per 64-key tile and KV head: K rows of 192 + 8 pad elements, then V^T rows
-# of 64 + 8, all bf16; a packed call may start each sequence on a fresh tile.
-IMAGE_BYTES = (64 * 200 + 128 * 72) * 2
+# of 64 + 8, all bf16, plus one fp32 key norm; a packed call may start each sequence
+# on a fresh tile.
+IMAGE_BYTES = (64 * 200 + 128 * 72) * 2 + 4
 
 
 def test_prefill_workspace_size(lib):
     size = lambda cfg, b, tk: lib.mimo_attn_prefill_workspace_size(ctypes.byref(cfg), b, tk)
-    assert IMAGE_BYTES == 44032
+    assert IMAGE_BYTES == 44036
     assert size(cfg_glob(), 1, 32768) == (512 + 1) * 4 * IMAGE_BYTES
     assert size(cfg_glob(), 4, 4 * 1000) == (63 + 4) * 4 * IMAGE_BYTES
     # a dense batch of B sequences of Tk keys fits in the size for B * Tk keys
