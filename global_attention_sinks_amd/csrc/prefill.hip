@@ -818,6 +818,63 @@ void prefill_image_kernel(PrefillArgs a) {
     }
 }
 
+// ---- RoPE of a block's 32 query rows with both wave halves at work.  Lane (l, 0)
+// holds dims 0..95 of row l and lane (l, 1) dims 96..191, so all 32 rotating pairs
+// (dims i and i + 32, i < 32) sit in the lower half.  Pairs 16..31 move to the upper
+// half (lane swaps, undone at the end) and every lane rotates 16 pairs.  The angle
+// of pair i for row l is the block's base angle (position pos0, exact fixed-point
+// turns, the same for every lane) plus l * theta_i (under 32 positions: fp32 keeps
+// it to ~3e-7 turns), which saves the per-row 64-bit turn products.
+__device__ __forceinline__ void swap_halves(u32x4 &lo_keep, u32x4 &hi_keep) {
+    // upper lanes' lo_keep <-> lower lanes' hi_keep
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const auto r = __builtin_amdgcn_permlane32_swap(lo_keep[i], hi_keep[i], false, false);
+        lo_keep[i] = r[0];
+        hi_keep[i] = r[1];
+    }
+}
+
+__device__ __forceinline__ void rope_rotate_block(u32x4 (&qr)[12], int64_t pos0, int l32, int h2,
+                                                  const RopeTurns &rt) {
+    swap_halves(qr[0], qr[2]);
+    swap_halves(qr[1], qr[3]);
+    swap_halves(qr[4], qr[6]);
+    swap_halves(qr[5], qr[7]);
+    const float lf = (float)l32;
+    const bool up = h2 != 0;
+    constexpr float k2m32 = 2.3283064365386963e-10f;   // 2^-32
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            float cs[2], sn[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int i = 8 * c + 2 * w + k;   // pair in the lower half; i + 16 in the upper
+                // the block's base angles (uniform, scalar unit) and theta's high words,
+                // picked per half; recomputed per block rather than held in registers
+                uint32_t th_lo = (uint32_t)(rt.turn[i] >> 32), th_hi = (uint32_t)(rt.turn[i + 16] >> 32);
+                uint32_t b_lo = (uint32_t)(((uint64_t)pos0 * rt.turn[i]) >> 32);
+                uint32_t b_hi = (uint32_t)(((uint64_t)pos0 * rt.turn[i + 16]) >> 32);
+                asm volatile("" : "+s"(th_lo), "+s"(th_hi), "+s"(b_lo), "+s"(b_hi));
+                const float th = (float)(up ? th_hi : th_lo) * k2m32;
+                const float b = (float)(int32_t)(up ? b_hi : b_lo) * k2m32;
+                const float r = __builtin_fmaf(lf, th, b);
+                sn[k] = __builtin_amdgcn_sinf(r);
+                cs[k] = __builtin_amdgcn_cosf(r);
+            }
+            const float x0 = bf_lo(qr[c][w]), x1 = bf_hi(qr[c][w]);
+            const float y0 = bf_lo(qr[c + 4][w]), y1 = bf_hi(qr[c + 4][w]);
+            qr[c][w] = pack_bf16(x0 * cs[0] - y0 * sn[0], x1 * cs[1] - y1 * sn[1]);
+            qr[c + 4][w] = pack_bf16(y0 * cs[0] + x0 * sn[0], y1 * cs[1] + x1 * sn[1]);
+        }
+    swap_halves(qr[0], qr[2]);
+    swap_halves(qr[1], qr[3]);
+    swap_halves(qr[4], qr[6]);
+    swap_halves(qr[5], qr[7]);
+}
+
 // ---- Sliding-window band kernel (window <= 128, 8 query heads per KV head).
 // One workgroup = the 8 query heads of one KV head (one wave each, two waves per
 // SIMD) of one sequence, walking a run of consecutive 32-query blocks.  The 32-key
@@ -971,20 +1028,17 @@ void prefill_band_kernel(PrefillArgs a) {
     for (int qb = qb0; qb < qb1; ++qb) {
         const int q0 = qb * QW;
         const int t0 = tlo(qb), t1 = thi(qb);
+        // ---- this block's Q (issued first: vmcnt counts in issue order, so waiting
+        // for Q then does not also wait for the next tile's loads issued below)
+        load_q(qb);
         // the tile the next block adds: its slot is outside this block's window
         if (t1 + 1 <= t_last) {
             store_tile(R, t1 + 1);
             load_tile(R, min(t1 + 2, t_last));
         }
-
-        // ---- this block's Q, rotated
-        load_q(qb);
         const int t = q0 + l32;
         const bool tval = t < Tq;
-        if (h2 == 0) {
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) rope_rotate8(qr[cc], qr[cc + 4], a.rt, 8 * cc, q_pos0 + t);
-        }
+        rope_rotate_block(qr, q_pos0 + q0, l32, h2, a.rt);
 
         float m_run = a.sinks ? a.sinks[head] * kLog2e : kNegInf;
         float l_run = (a.sinks && h2 == 0) ? 1.0f : 0.0f;
