@@ -1183,9 +1183,6 @@ static hipError_t launch_variant(PrefillArgs a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-#ifndef MIMO_PREFILL_SHAPE
-#define MIMO_PREFILL_SHAPE 0
-#endif
 // Sliding layers with 8 query heads per KV head and a window <= 128 run the
 // band kernel (0: the per-block kernel).
 #ifndef MIMO_PREFILL_BAND
@@ -1229,15 +1226,13 @@ hipError_t launch_prefill(PrefillArgs a, hipStream_t stream) {
     // Global layers given a tile-image workspace: image pass + DMA-staged kernel.
     if (a.kv_img && a.window == 0 && (a.Hq / a.Hkv) % 8 == 0) return launch_image(a, stream);
     // GQA group sizes are multiples of 4 (checked by the caller).  Sliding
-    // windows see a short band of keys: 4 heads x 32-key tiles, two workgroups
-    // per CU.  Global prefixes are long: 8 heads share each 64-key tile.
+    // windows see a short band of keys: the band kernel (8 query heads per KV
+    // head, window <= 128), else 4 heads x 32-key tiles, two workgroups per CU.
+    // Global prefixes are long: 8 heads share each 64-key tile.
     const bool wide = (a.Hq / a.Hkv) % 8 == 0;
-    int shape = MIMO_PREFILL_SHAPE;
-    if (shape == 0 && MIMO_PREFILL_BAND && a.window > 0 && a.window <= kBandMaxWindow && a.Hq == 8 * a.Hkv)
+    if (MIMO_PREFILL_BAND && a.window > 0 && a.window <= kBandMaxWindow && a.Hq == 8 * a.Hkv)
         return launch_band(a, stream);
-    if (shape == 0) shape = (a.window > 0 || !wide) ? 2 : 1;
-    if (shape == 1 && wide) return launch_variant<8, 64>(a, stream);
-    if (shape == 4) return launch_variant<4, 64>(a, stream);
+    if (a.window == 0 && wide) return launch_variant<8, 64>(a, stream);
     return launch_variant<4, 32>(a, stream);
 }
 
