@@ -51,6 +51,32 @@ __device__ __forceinline__ u32x4 lds128(const uint16_t *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// ---- one query row's output, o = inv * O, as bf16 with 16-byte stores.  In the
+// O^T accumulators lane half h2 holds dims 32 mb + 8 a4 + 4 h2 + (0..3); one lane
+// swap per pair of 4-dim pieces gives the lower half all 8 dims of the even pieces
+// and the upper half those of the odd ones.
+__device__ __forceinline__ void store_out_row(const f32x16 (&O)[4], float inv, uint16_t *dst, int h2) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int a2 = 0; a2 < 2; ++a2) {
+            u32x2 pe, po;   // pieces a4 = 2 a2 and 2 a2 + 1
+            pe[0] = pack_bf16(O[mb][8 * a2] * inv, O[mb][8 * a2 + 1] * inv);
+            pe[1] = pack_bf16(O[mb][8 * a2 + 2] * inv, O[mb][8 * a2 + 3] * inv);
+            po[0] = pack_bf16(O[mb][8 * a2 + 4] * inv, O[mb][8 * a2 + 5] * inv);
+            po[1] = pack_bf16(O[mb][8 * a2 + 6] * inv, O[mb][8 * a2 + 7] * inv);
+            // upper lanes' pe <-> lower lanes' po
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const auto r = __builtin_amdgcn_permlane32_swap(pe[x], po[x], false, false);
+                pe[x] = r[0];
+                po[x] = r[1];
+            }
+            const u32x4 o = {pe[0], pe[1], po[0], po[1]};
+            *reinterpret_cast<u32x4 *>(dst + 32 * mb + 8 * (2 * a2 + h2)) = o;
+        }
+}
+
 // ---- which (query block, batch, KV head, head group) workgroup blockIdx.x owns.
 // With the (KV head, head group) pairs split evenly over the 8 XCDs, an XCD walks
 // its pairs sequence by sequence, query blocks longest-first: its resident
@@ -438,15 +464,7 @@ void prefill_kernel(PrefillArgs a) {
     if (t < Tq) {
         const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
         uint16_t *dst = a.out + ((q_tok0 + t) * a.Hq + head) * kDv;
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                u32x2 o;
-                o[0] = pack_bf16(O[mb][4 * a4] * inv, O[mb][4 * a4 + 1] * inv);
-                o[1] = pack_bf16(O[mb][4 * a4 + 2] * inv, O[mb][4 * a4 + 3] * inv);
-                *reinterpret_cast<u32x2 *>(dst + 32 * mb + 8 * a4 + 4 * h2) = o;
-            }
+        store_out_row(O, inv, dst, h2);
         if (a.lse && h2 == 0)
             a.lse[lse_off + (size_t)head * a.lse_hstride + t] = lt > 0.0f ? (m_run + log2f(lt)) * kLn2 : kNegInf;
     }
@@ -804,15 +822,7 @@ void prefill_image_kernel(PrefillArgs a) {
     if (t < Tq) {
         const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
         uint16_t *dst = a.out + ((q_tok0 + t) * a.Hq + head) * kDv;
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                u32x2 o;
-                o[0] = pack_bf16(O[mb][4 * a4] * inv, O[mb][4 * a4 + 1] * inv);
-                o[1] = pack_bf16(O[mb][4 * a4 + 2] * inv, O[mb][4 * a4 + 3] * inv);
-                *reinterpret_cast<u32x2 *>(dst + 32 * mb + 8 * a4 + 4 * h2) = o;
-            }
+        store_out_row(O, inv, dst, h2);
         if (a.lse && h2 == 0)
             a.lse[lse_off + (size_t)head * a.lse_hstride + t] = lt > 0.0f ? (m_run + log2f(lt)) * kLn2 : kNegInf;
     }
@@ -1065,6 +1075,15 @@ void prefill_band_kernel(PrefillArgs a) {
                     S = mfma32(kf[i % RING], qr[i], S);
                     if (i + RING < 12) kf[i % RING] = lds128(kr0 + 8 * (i + RING));
                 }
+                // keep RING reads in flight: left alone, the scheduler waits for each
+                // fragment right before its MFMA here
+                __builtin_amdgcn_sched_group_barrier(0x100, RING, 0);   // LDS reads
+#pragma unroll
+                for (int i = 0; i < 12 - RING; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, RING, 0);
             }
             return S;
         };
@@ -1077,13 +1096,21 @@ void prefill_band_kernel(PrefillArgs a) {
             // ---- mask unless every key of the tile is visible to every query of the block
             const bool full = (j0 + NK <= Tk) && (q0 + off - (j0 + NK - 1) >= 0) && (qhi + off - j0 < W);
             if (!full) {
-                const int d = t + off - j0;        // query's key index - first key of the tile
-                const int kmax = Tk - j0;
+                // Score e holds tile key 16 (e >> 3) + 8 h2 + (e & 7).  Less 8 h2, the
+                // keys this lane's query sees form the range [lo, hi]; a key c is in
+                // it when c - lo <= hi - lo as unsigned (constants c: no per-key registers).
+                const int dd = t + off - j0 - 8 * h2;
+                const int hi = min(dd, Tk - j0 - 8 * h2 - 1);
+                int lo = max(dd - W + 1, 0);
+                uint32_t span = (uint32_t)(hi - lo);
+                if (hi < lo) {   // nothing visible
+                    lo = 0x40000000;
+                    span = 0;
+                }
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const int jrel = 16 * (e >> 3) + 8 * h2 + (e & 7);
-                    const bool vis = (jrel < kmax) && (jrel <= d) && (d - jrel < W);
-                    if (!vis) S[e] = kNegInf;
+                    const int c = 16 * (e >> 3) + (e & 7);
+                    if ((uint32_t)(c - lo) > span) S[e] = kNegInf;
                 }
             }
 
@@ -1139,15 +1166,7 @@ void prefill_band_kernel(PrefillArgs a) {
         if (tval) {
             const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
             uint16_t *dst = a.out + ((q_tok0 + t) * a.Hq + head) * kDv;
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                for (int a4 = 0; a4 < 4; ++a4) {
-                    u32x2 o;
-                    o[0] = pack_bf16(O[mb][4 * a4] * inv, O[mb][4 * a4 + 1] * inv);
-                    o[1] = pack_bf16(O[mb][4 * a4 + 2] * inv, O[mb][4 * a4 + 3] * inv);
-                    *reinterpret_cast<u32x2 *>(dst + 32 * mb + 8 * a4 + 4 * h2) = o;
-                }
+            store_out_row(O, inv, dst, h2);
             if (a.lse && h2 == 0)
                 a.lse[lse_off + (size_t)head * a.lse_hstride + t] = lt > 0.0f ? (m_run + log2f(lt)) * kLn2 : kNegInf;
         }
