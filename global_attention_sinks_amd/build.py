@@ -21,6 +21,11 @@ ARCH = "gfx950"
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs.  In kernels past 256 registers (dK/dV, multi-query
+    # decode) the default form left the allocator copying accumulators between
+    # AGPRs and VGPRs around every MFMA (383 copies per dK/dV step); with this
+    # form AGPRs only hold values that wait.  Kernels under 256 are unchanged.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", os.path.join(ROOT, "include"),
 ]
 
