@@ -1014,163 +1014,176 @@ void prefill_band_kernel(PrefillArgs a) {
     const float cl2 = a.scale_log2;
     const int prow = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
 
-    // ---- prologue: the tiles of the first block, then the next tile's loads in flight
+    // ---- Two phases per CU.  Waves w and w + 4 share a SIMD; the odd waves ("late")
+    // take block n - 1 whole in iteration n, the even waves ("early") finish block
+    // n - 1 and then start block n (its Q, RoPE and first tile) before the
+    // iteration's barrier, so half the SIMDs run about half a block ahead of the
+    // other half (3.5-4.5 % faster than every wave in step).  Iteration n stages
+    // tile thi(n), read from iteration n + 1 on; its reads lie in tlo(n - 1) ..
+    // thi(n) - 1, so with tile thi(n) at most 7 distinct tiles: the ring's slots.
+    const bool early = (w & 1) == 0;
+    // first tile of a block's second half (the first half never takes thi)
+    auto mid = [&](int qb) { return min(tlo(qb) + 1, thi(qb)); };
+
     TileRegs R;
+    int staged;
     {
-        const int tp = thi(qb0);
-        load_tile(R, tlo(qb0));
-        for (int jt = tlo(qb0); jt <= tp; ++jt) {
+        const int t0 = tlo(qb0), tp = thi(qb0) - 1;
+        load_tile(R, t0);
+        for (int jt = t0; jt <= tp; ++jt) {
             store_tile(R, jt);
             load_tile(R, min(jt + 1, t_last));
         }
+        staged = max(tp, t0 - 1);   // R holds tile staged + 1 = thi(qb0)
     }
     __syncthreads();
 
-    // Q rows (raw) of block qb.  (Issuing the next block's right after a block's
-    // last QK product, to hide their latency, measured slower.)
     u32x4 qr[12];
-    auto load_q = [&](int qb) {
-        const int tq = min(qb * QW + l32, Tq - 1);
+    float m_run = 0.0f, l_run = 0.0f;
+    f32x16 O[4];
+    auto begin_block = [&](int qb) {
+        const int q0 = qb * QW;
+        const int tq = min(q0 + l32, Tq - 1);
         const uint16_t *src = a.q + ((q_tok0 + tq) * a.Hq + head) * kDqk + 96 * h2;
 #pragma unroll
         for (int ks = 0; ks < 12; ++ks) qr[ks] = ldg128(src + 8 * ks);
-    };
-    for (int qb = qb0; qb < qb1; ++qb) {
-        const int q0 = qb * QW;
-        const int t0 = tlo(qb), t1 = thi(qb);
-        // ---- this block's Q (issued first: vmcnt counts in issue order, so waiting
-        // for Q then does not also wait for the next tile's loads issued below)
-        load_q(qb);
-        // the tile the next block adds: its slot is outside this block's window
-        if (t1 + 1 <= t_last) {
-            store_tile(R, t1 + 1);
-            load_tile(R, min(t1 + 2, t_last));
-        }
-        const int t = q0 + l32;
-        const bool tval = t < Tq;
         rope_rotate_block(qr, q_pos0 + q0, l32, h2, a.rt);
-
-        float m_run = a.sinks ? a.sinks[head] * kLog2e : kNegInf;
-        float l_run = (a.sinks && h2 == 0) ? 1.0f : 0.0f;
-        f32x16 O[4];
+        m_run = a.sinks ? a.sinks[head] * kLog2e : kNegInf;
+        l_run = (a.sinks && h2 == 0) ? 1.0f : 0.0f;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) O[mb][e] = 0.0f;
+    };
+
+    // S^T of tile jt
+    auto qk_tile = [&](int jt) {
+        const uint16_t *Ks = ring + (jt % kBandSlots) * SLOT;
+        f32x16 S;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) S[e] = 0.0f;
+        {
+            const uint16_t *kr0 = Ks + prow * KSTR + 96 * h2;
+            u32x4 kf[RING];
+#pragma unroll
+            for (int i = 0; i < RING; ++i) kf[i] = lds128(kr0 + 8 * i);
+#pragma unroll
+            for (int i = 0; i < 12; ++i) {
+                S = mfma32(kf[i % RING], qr[i], S);
+                if (i + RING < 12) kf[i % RING] = lds128(kr0 + 8 * (i + RING));
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, RING, 0);   // LDS reads
+#pragma unroll
+            for (int i = 0; i < 12 - RING; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, RING, 0);
+        }
+        return S;
+    };
+    // mask, online softmax, O^T += V^T P^T of tile jt for block qb
+    auto rest_tile = [&](int qb, int jt, f32x16 S) {
+        const uint16_t *Ks = ring + (jt % kBandSlots) * SLOT;
+        const uint16_t *Vs = Ks + K_TILE;
+        const int j0 = jt * NK;
+        const int q0 = qb * QW, t = q0 + l32;
         const int qhi = min(q0 + QW - 1, Tq - 1);
-
-        // S^T of tile jt
-        auto qk_tile = [&](int jt) {
-            const uint16_t *Ks = ring + (jt % kBandSlots) * SLOT;
-            f32x16 S;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) S[e] = 0.0f;
-            {
-                const uint16_t *kr0 = Ks + prow * KSTR + 96 * h2;
-                u32x4 kf[RING];
-#pragma unroll
-                for (int i = 0; i < RING; ++i) kf[i] = lds128(kr0 + 8 * i);
-#pragma unroll
-                for (int i = 0; i < 12; ++i) {
-                    S = mfma32(kf[i % RING], qr[i], S);
-                    if (i + RING < 12) kf[i % RING] = lds128(kr0 + 8 * (i + RING));
-                }
-                // keep RING reads in flight: left alone, the scheduler waits for each
-                // fragment right before its MFMA here
-                __builtin_amdgcn_sched_group_barrier(0x100, RING, 0);   // LDS reads
-#pragma unroll
-                for (int i = 0; i < 12 - RING; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, RING, 0);
+        const bool full = (j0 + NK <= Tk) && (q0 + off - (j0 + NK - 1) >= 0) && (qhi + off - j0 < W);
+        if (!full) {
+            const int dd = t + off - j0 - 8 * h2;
+            const int hi = min(dd, Tk - j0 - 8 * h2 - 1);
+            int lo = max(dd - W + 1, 0);
+            uint32_t span = (uint32_t)(hi - lo);
+            if (hi < lo) {
+                lo = 0x40000000;
+                span = 0;
             }
-            return S;
-        };
-        // mask, online softmax, O^T += V^T P^T of tile jt
-        auto rest_tile = [&](int jt, f32x16 S) {
-            const uint16_t *Ks = ring + (jt % kBandSlots) * SLOT;
-            const uint16_t *Vs = Ks + K_TILE;
-            const int j0 = jt * NK;
-
-            // ---- mask unless every key of the tile is visible to every query of the block
-            const bool full = (j0 + NK <= Tk) && (q0 + off - (j0 + NK - 1) >= 0) && (qhi + off - j0 < W);
-            if (!full) {
-                // Score e holds tile key 16 (e >> 3) + 8 h2 + (e & 7).  Less 8 h2, the
-                // keys this lane's query sees form the range [lo, hi]; a key c is in
-                // it when c - lo <= hi - lo as unsigned (constants c: no per-key registers).
-                const int dd = t + off - j0 - 8 * h2;
-                const int hi = min(dd, Tk - j0 - 8 * h2 - 1);
-                int lo = max(dd - W + 1, 0);
-                uint32_t span = (uint32_t)(hi - lo);
-                if (hi < lo) {   // nothing visible
-                    lo = 0x40000000;
-                    span = 0;
-                }
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int c = 16 * (e >> 3) + (e & 7);
-                    if ((uint32_t)(c - lo) > span) S[e] = kNegInf;
-                }
-            }
-
-            // ---- online softmax (exp2 domain), lazy rescale
-            float mx = kNegInf;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, S[e]);
-            mx = max_xor32(mx);
-            const float mc = mx * cl2;
-            const bool need = mc > m_run + 8.0f;
-            if (__any(need)) {
-                const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mc) : 1.0f;
-                if (need) m_run = mc;
-                l_run *= alpha;
-#pragma unroll
-                for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) O[mb][e] *= alpha;
-            }
-            const float mu = (m_run == kNegInf) ? 0.0f : m_run;
-            u32x4 P[2];
-            float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], cl2, -mu));
-                S[e] = p;
-                ls[e & 3] += p;
+                const int c = 16 * (e >> 3) + (e & 7);
+                if ((uint32_t)(c - lo) > span) S[e] = kNegInf;
             }
+        }
+        float mx = kNegInf;
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, S[e]);
+        mx = max_xor32(mx);
+        const float mc = mx * cl2;
+        const bool need = mc > m_run + 8.0f;
+        if (__any(need)) {
+            const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mc) : 1.0f;
+            if (need) m_run = mc;
+            l_run *= alpha;
 #pragma unroll
-                for (int x = 0; x < 4; ++x) P[s][x] = pack_bf16(S[8 * s + 2 * x], S[8 * s + 2 * x + 1]);
-            l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-
-            // ---- O^T += V^T P^T
-            {
-                const uint16_t *vr0 = Vs + l32 * VSTR + 8 * h2;
-                auto vaddr = [&](int i) { return vr0 + (i >> 1) * 32 * VSTR + 16 * (i & 1); };
-                u32x4 vf[RING];
+            for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-                for (int i = 0; i < RING; ++i) vf[i] = lds128(vaddr(i));
+                for (int e = 0; e < 16; ++e) O[mb][e] *= alpha;
+        }
+        const float mu = (m_run == kNegInf) ? 0.0f : m_run;
+        u32x4 P[2];
+        float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    O[i >> 1] = mfma32(vf[i % RING], P[i & 1], O[i >> 1]);
-                    if (i + RING < 8) vf[i % RING] = lds128(vaddr(i + RING));
-                }
+        for (int e = 0; e < 16; ++e) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], cl2, -mu));
+            S[e] = p;
+            ls[e & 3] += p;
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) P[s][x] = pack_bf16(S[8 * s + 2 * x], S[8 * s + 2 * x + 1]);
+        l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        {
+            const uint16_t *vr0 = Vs + l32 * VSTR + 8 * h2;
+            auto vaddr = [&](int i) { return vr0 + (i >> 1) * 32 * VSTR + 16 * (i & 1); };
+            u32x4 vf[RING];
+#pragma unroll
+            for (int i = 0; i < RING; ++i) vf[i] = lds128(vaddr(i));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                O[i >> 1] = mfma32(vf[i % RING], P[i & 1], O[i >> 1]);
+                if (i + RING < 8) vf[i % RING] = lds128(vaddr(i + RING));
             }
-        };
-        for (int jt = t0; jt <= t1; ++jt) rest_tile(jt, qk_tile(jt));
-
-        // ---- epilogue: o = v_scale * O / l, bf16
+        }
+    };
+    auto run_tiles = [&](int qb, int ta, int tb) {
+        for (int jt = ta; jt <= tb; ++jt) rest_tile(qb, jt, qk_tile(jt));
+    };
+    // o = v_scale * O / l, bf16
+    auto end_block = [&](int qb) {
+        const int t = qb * QW + l32;
         const float lt = sum_xor32(l_run);
-        if (tval) {
+        if (t < Tq) {
             const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
             uint16_t *dst = a.out + ((q_tok0 + t) * a.Hq + head) * kDv;
             store_out_row(O, inv, dst, h2);
             if (a.lse && h2 == 0)
                 a.lse[lse_off + (size_t)head * a.lse_hstride + t] = lt > 0.0f ? (m_run + log2f(lt)) * kLn2 : kNegInf;
         }
-        __syncthreads();   // the tile stored above is visible; nobody still reads the slot reused next
+    };
+
+    for (int n = qb0; n <= qb1; ++n) {
+        if (n < qb1 && thi(n) > staged) {   // uniform over the workgroup
+            store_tile(R, thi(n));
+            staged = thi(n);
+            load_tile(R, min(staged + 1, t_last));
+        }
+        if (early) {
+            if (n > qb0) {
+                run_tiles(n - 1, mid(n - 1), thi(n - 1));
+                end_block(n - 1);
+            }
+            if (n < qb1) {
+                begin_block(n);
+                run_tiles(n, tlo(n), mid(n) - 1);
+            }
+        } else if (n > qb0) {
+            begin_block(n - 1);
+            run_tiles(n - 1, tlo(n - 1), thi(n - 1));
+            end_block(n - 1);
+        }
+        __syncthreads();   // tile thi(n) is visible; no wave still reads the slot written next
     }
 }
 
