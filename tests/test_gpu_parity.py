@@ -105,6 +105,9 @@ SWA_CASES = [
     (1, 77, 3, 128, False, (64, 8)),     # no sink
     (3, 65, 0, 128, True, (16, 4)),      # GQA group of 4
     (1, 1, 0, 128, True, (64, 8)),       # one token
+    (40, 96, 0, 128, True, (64, 8)),     # 320 (sequence, KV head) pairs: one run each, 3 blocks
+    (1, 2000, 0, 128, True, (64, 8)),    # runs of 2 blocks, the last run 1 block
+    (1, 500, 7, 64, True, (64, 8)),      # window 64, positions offset by 7
 ]
 
 
