@@ -831,8 +831,12 @@ hipError_t launch_decode(DecodeArgs a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.n_q == 1) {
+#if MIMO_DECODE_SPLIT_HEADS
+        launch_partial<1, 256, MIMO_DECODE_DEPTH>(a, m, stream);   // at most 4 KV heads: 256 threads
+#else
         if (m.threads <= 256) launch_partial<1, 256, MIMO_DECODE_DEPTH>(a, m, stream);
         else launch_partial<1, 512>(a, m, stream);
+#endif
     }
     else if (m.wph == 2 && m.kvpw == 1) launch_shared<2>(a, m, stream);
     else if (m.wph == 4 && m.kvpw == 1) launch_shared<4>(a, m, stream);
