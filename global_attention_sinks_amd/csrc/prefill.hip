@@ -595,6 +595,7 @@ void prefill_image_kernel(PrefillArgs a) {
     constexpr int K_OPS = K_TILE * 2 / 1024, V_OPS = V_TILE * 2 / 1024;   // 25 + 18 copies of 1 KiB
     constexpr int OPS = K_OPS + V_OPS;
     constexpr int OPW = (OPS + NW - 1) / NW;        // per wave
+    constexpr int RQ = 4, RV = 6;                   // K / V^T fragment reads in flight
     static_assert(K_TILE * 2 % 1024 == 0 && V_TILE * 2 % 1024 == 0, "whole 1 KiB copies");
     static_assert(STAGE == kImgTile && VSTR == kImgVS, "prepared image = LDS stage");
 
@@ -709,14 +710,23 @@ void prefill_image_kernel(PrefillArgs a) {
             for (int e = 0; e < 16; ++e) S[kb][e] = 0.0f;
         const uint16_t *kr0 = Ks + prow * KSTR + 96 * h2;
         auto kaddr = [&](int i) { return kr0 + (i % KB) * 32 * KSTR + 8 * (i / KB); };
-        u32x4 kf[RING];
+        u32x4 kf[RQ];
 #pragma unroll
-        for (int i = 0; i < RING; ++i) kf[i] = lds128(kaddr(i));
+        for (int i = 0; i < RQ; ++i) kf[i] = lds128(kaddr(i));
 #pragma unroll
         for (int i = 0; i < 12 * KB; ++i) {
-            S[i % KB] = mfma32(kf[i % RING], qr[i / KB], S[i % KB]);
-            if (i + RING < 12 * KB) kf[i % RING] = lds128(kaddr(i + RING));
+            S[i % KB] = mfma32(kf[i % RQ], qr[i / KB], S[i % KB]);
+            if (i + RQ < 12 * KB) kf[i % RQ] = lds128(kaddr(i + RQ));
         }
+        // keep RQ reads in flight (left alone, the scheduler let them drain to one
+        // or two and waited before most MFMAs)
+        __builtin_amdgcn_sched_group_barrier(0x100, RQ, 0);   // LDS reads
+#pragma unroll
+        for (int i = 0; i < 12 * KB - RQ; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, RQ, 0);
     };
 
     auto softmax_pv = [&](f32x16 (&S)[KB], int jt, int buf, float kn) {
@@ -785,14 +795,21 @@ void prefill_image_kernel(PrefillArgs a) {
             const int mb = i / (2 * KB), kb = (i / 2) % KB, s = i & 1;
             return vr0 + mb * 32 * VSTR + 32 * kb + 16 * s;
         };
-        u32x4 vf[RING];
+        u32x4 vf[RV];
 #pragma unroll
-        for (int i = 0; i < RING; ++i) vf[i] = lds128(vaddr(i));
+        for (int i = 0; i < RV; ++i) vf[i] = lds128(vaddr(i));
 #pragma unroll
         for (int i = 0; i < 8 * KB; ++i) {
-            O[i / (2 * KB)] = mfma32(vf[i % RING], Pm[(i / 2) % KB][i & 1], O[i / (2 * KB)]);
-            if (i + RING < 8 * KB) vf[i % RING] = lds128(vaddr(i + RING));
+            O[i / (2 * KB)] = mfma32(vf[i % RV], Pm[(i / 2) % KB][i & 1], O[i / (2 * KB)]);
+            if (i + RV < 8 * KB) vf[i % RV] = lds128(vaddr(i + RV));
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, RV, 1);
+#pragma unroll
+        for (int i = 0; i < 8 * KB - RV; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, RV, 1);
     };
 
     // a tile's key norm (uniform: a scalar load) is fetched one tile ahead, with the
