@@ -1089,6 +1089,8 @@ void prefill_band_kernel(PrefillArgs a) {
                 S = mfma32(kf[i % RING], qr[i], S);
                 if (i + RING < 12) kf[i % RING] = lds128(kr0 + 8 * (i + RING));
             }
+            // keep RING reads in flight: left alone, the scheduler waits for each
+            // fragment right before its MFMA here
             __builtin_amdgcn_sched_group_barrier(0x100, RING, 0);   // LDS reads
 #pragma unroll
             for (int i = 0; i < 12 - RING; ++i) {
@@ -1106,13 +1108,17 @@ void prefill_band_kernel(PrefillArgs a) {
         const int j0 = jt * NK;
         const int q0 = qb * QW, t = q0 + l32;
         const int qhi = min(q0 + QW - 1, Tq - 1);
+        // ---- mask unless every key of the tile is visible to every query of the block
         const bool full = (j0 + NK <= Tk) && (q0 + off - (j0 + NK - 1) >= 0) && (qhi + off - j0 < W);
         if (!full) {
+            // Score e holds tile key 16 (e >> 3) + 8 h2 + (e & 7).  Less 8 h2, the
+            // keys this lane's query sees form the range [lo, hi]; a key c is in
+            // it when c - lo <= hi - lo as unsigned (constants c: no per-key registers).
             const int dd = t + off - j0 - 8 * h2;
             const int hi = min(dd, Tk - j0 - 8 * h2 - 1);
             int lo = max(dd - W + 1, 0);
             uint32_t span = (uint32_t)(hi - lo);
-            if (hi < lo) {
+            if (hi < lo) {   // nothing visible
                 lo = 0x40000000;
                 span = 0;
             }
@@ -1122,6 +1128,7 @@ void prefill_band_kernel(PrefillArgs a) {
                 if ((uint32_t)(c - lo) > span) S[e] = kNegInf;
             }
         }
+        // ---- online softmax (exp2 domain), lazy rescale
         float mx = kNegInf;
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, S[e]);
