@@ -263,7 +263,7 @@ def main():
     ap.add_argument("--workload", choices=["layer_step", "long_prefill", "serving_chunks", "spec_decode", "paged_decode",
                                             "backward"], default="layer_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--cpu-budget", type=float, default=40.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run three 1 GiB device-to-device copies (a known-size reference "
                          "for the FETCH_SIZE / WRITE_SIZE counters)")
