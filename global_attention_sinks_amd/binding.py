@@ -67,6 +67,7 @@ def load_library(path: str = LIB_PATH):
     lib.mimo_attn_prefill_workspace_size.argtypes = [C, I32, I64]
     lib.mimo_attn_prefill_workspace_size.restype = ctypes.c_size_t
     lib.mimo_attn_decode.argtypes = [C, I32, P, P, P, P, I32, P, P, P, ctypes.c_size_t, P]
+    lib.mimo_attn_decode_noalloc.argtypes = [C, I32, P, P, P, P, I32, P, P, P]
     lib.mimo_attn_prefill_backward.argtypes = [C, P, P, P, P, I32, I32, I64, P, P, P, P, P, P, P, P,
                                                ctypes.c_size_t, P]
     lib.mimo_attn_backward_workspace_size.argtypes = [C, I32, I32]
@@ -83,7 +84,7 @@ def load_library(path: str = LIB_PATH):
     lib.mimo_kv_ring_append.argtypes = [C, I32, P, P, P, P, P, I32, P]
     lib.mimo_last_error.restype = ctypes.c_char_p
     for fn in ("mimo_rope_partial", "mimo_attn_prefill_swa", "mimo_attn_prefill_global",
-               "mimo_attn_prefill_varlen", "mimo_attn_decode", "mimo_attn_decode_multi",
+               "mimo_attn_prefill_varlen", "mimo_attn_decode", "mimo_attn_decode_noalloc", "mimo_attn_decode_multi",
                "mimo_attn_decode_paged", "mimo_kv_paged_append", "mimo_kv_ring_append",
                "mimo_attn_prefill_backward"):
         getattr(lib, fn).restype = ctypes.c_int
@@ -233,6 +234,21 @@ def mimo_attn_decode(cfg: MimoAttnCfg, q, q_pos, k_cache, v_cache, sinks, out, w
     _check("mimo_attn_decode",
            lib.mimo_attn_decode(ctypes.byref(cfg), S, _p(q), _p(q_pos), _p(k_cache), _p(v_cache), cap,
                                 _p(sinks), _p(out), _p(ws), ws_bytes, _stream(stream)))
+    return out
+
+
+def mimo_attn_decode_noalloc(cfg: MimoAttnCfg, q, q_pos, k_cache, v_cache, sinks, out, stream=None):
+    """mimo_attn_decode without a workspace: the library's per-GPU scratch holds the
+    partials (calls that overlap in time on one GPU race)."""
+    lib = load_library()
+    _need(q, torch.bfloat16, "q", 3); _need(out, torch.bfloat16, "out", 3)
+    _need(k_cache, torch.bfloat16, "k_cache", 4); _need(v_cache, torch.bfloat16, "v_cache", 4)
+    _need(q_pos, torch.int64, "q_pos", 1); _need(sinks, torch.float32, "sinks", 1)
+    S = q.shape[0]
+    cap = k_cache.shape[1]
+    _check("mimo_attn_decode_noalloc",
+           lib.mimo_attn_decode_noalloc(ctypes.byref(cfg), S, _p(q), _p(q_pos), _p(k_cache), _p(v_cache), cap,
+                                        _p(sinks), _p(out), _stream(stream)))
     return out
 
 

@@ -250,10 +250,12 @@ mimo_status mimo_attn_prefill_backward(const mimo_attn_cfg *cfg, const uint16_t 
     return from_hip(launch_backward(a, (hipStream_t)stream), "prefill_backward launch");
 }
 
-static mimo_status decode_common(const mimo_attn_cfg *cfg, int32_t S, int32_t n_q, const uint16_t *q,
-                                 const int64_t *q_pos, const void *k_cache, const void *v_cache,
-                                 int32_t cap, const float *sinks, uint16_t *out, void *ws, size_t ws_bytes,
-                                 void *stream, const PagedLayout &pl = PagedLayout()) {
+// Validation shared by the decode calls; fills everything of `a` but the
+// workspace.  All checks run before any HIP call.
+static mimo_status decode_prepare(const mimo_attn_cfg *cfg, int32_t S, int32_t n_q, const uint16_t *q,
+                                  const int64_t *q_pos, const void *k_cache, const void *v_cache,
+                                  int32_t cap, const float *sinks, uint16_t *out, const PagedLayout &pl,
+                                  DecodeArgs &a) {
     mimo_status st = check_cfg(cfg);
     if (st != MIMO_OK) return st;
     if (S < 0 || cap < 1) return fail(MIMO_ERR_INVALID_ARGUMENT, "S must be >= 0 and cap >= 1");
@@ -272,13 +274,8 @@ static mimo_status decode_common(const mimo_attn_cfg *cfg, int32_t S, int32_t n_
     if (S == 0) return ok();
     if (!q || !q_pos || !k_cache || !v_cache || !out)
         return fail(MIMO_ERR_INVALID_ARGUMENT, "q, q_pos, the caches and out must be non-NULL");
-    const size_t need = decode_workspace_bytes(S, cfg->num_q_heads, cfg->num_kv_heads, n_q);
-    if (!ws || ws_bytes < need)
-        return fail(MIMO_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu)", need,
-                    ws ? ws_bytes : (size_t)0);
-    DecodeArgs a{};
+    a = DecodeArgs{};
     a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.pos = q_pos; a.sinks = sinks; a.out = out;
-    a.ws_o = (float *)ws;
     a.S = S; a.Hq = cfg->num_q_heads; a.Hkv = cfg->num_kv_heads; a.cap = cap; a.window = cfg->window;
     a.n_q = n_q;
     a.scale_log2 = scale_log2(cfg); a.v_scale = cfg->v_scale;
@@ -289,6 +286,21 @@ static mimo_status decode_common(const mimo_attn_cfg *cfg, int32_t S, int32_t n_
         a.v_scale *= pl.v_scale;
     }
     a.rt = rope_turns(cfg->rope_base);
+    return ok();
+}
+
+static mimo_status decode_common(const mimo_attn_cfg *cfg, int32_t S, int32_t n_q, const uint16_t *q,
+                                 const int64_t *q_pos, const void *k_cache, const void *v_cache,
+                                 int32_t cap, const float *sinks, uint16_t *out, void *ws, size_t ws_bytes,
+                                 void *stream, const PagedLayout &pl = PagedLayout()) {
+    DecodeArgs a;
+    mimo_status st = decode_prepare(cfg, S, n_q, q, q_pos, k_cache, v_cache, cap, sinks, out, pl, a);
+    if (st != MIMO_OK || S == 0) return st;
+    const size_t need = decode_workspace_bytes(S, cfg->num_q_heads, cfg->num_kv_heads, n_q);
+    if (!ws || ws_bytes < need)
+        return fail(MIMO_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu)", need,
+                    ws ? ws_bytes : (size_t)0);
+    a.ws_o = (float *)ws;
     return from_hip(launch_decode(a, (hipStream_t)stream), "decode launch");
 }
 
@@ -311,6 +323,28 @@ mimo_status mimo_attn_decode(const mimo_attn_cfg *cfg, int32_t S, const uint16_t
                              int32_t cap, const float *sinks, uint16_t *out, void *ws,
                              size_t ws_bytes, void *stream) {
     return decode_common(cfg, S, 1, q, q_pos, k_cache, v_cache, cap, sinks, out, ws, ws_bytes, stream);
+}
+
+mimo_status mimo_attn_decode_noalloc(const mimo_attn_cfg *cfg, int32_t S, const uint16_t *q,
+                                     const int64_t *q_pos, const uint16_t *k_cache, const uint16_t *v_cache,
+                                     int32_t cap, const float *sinks, uint16_t *out, void *stream) {
+    static_assert(kDecodeScratchBytes == MIMO_DECODE_NOALLOC_MAX_BYTES, "scratch size in the header");
+    DecodeArgs a;
+    mimo_status st = decode_prepare(cfg, S, 1, q, q_pos, k_cache, v_cache, cap, sinks, out, PagedLayout(), a);
+    if (st != MIMO_OK || S == 0) return st;
+    const size_t need = decode_workspace_bytes(S, cfg->num_q_heads, cfg->num_kv_heads, 1);
+    if (need > kDecodeScratchBytes)
+        return fail(MIMO_ERR_WORKSPACE,
+                    "allocation-free decode: %d sequences need %zu bytes of scratch, more than the %zu the "
+                    "library holds per GPU; use mimo_attn_decode with a workspace", S, need,
+                    kDecodeScratchBytes);
+    void *ptr = nullptr;
+    const hipError_t e = decode_scratch((hipStream_t)stream, &ptr);
+    if (e == hipErrorInvalidDevice)
+        return fail(MIMO_ERR_INVALID_ARGUMENT, "allocation-free decode: the stream must belong to the current device");
+    if (e != hipSuccess) return from_hip(e, "decode scratch lookup");
+    a.ws_o = (float *)ptr;
+    return from_hip(launch_decode(a, (hipStream_t)stream), "decode launch");
 }
 
 size_t mimo_attn_decode_multi_workspace_size(const mimo_attn_cfg *cfg, int32_t S, int32_t n_q, int32_t cap) {

@@ -25,6 +25,9 @@
 // The sink logit (techniques map page, Learnable attention sink) is folded into
 // the piece holding a sequence's first step as the initial (max, sum) =
 // (sink * log2 e, 1).
+#include <atomic>
+#include <mutex>
+
 #include "kernels.hpp"
 
 // One-token decode: at most 4 KV heads (waves) per workgroup, so that every
@@ -846,6 +849,42 @@ hipError_t launch_decode(DecodeArgs a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(a.S * rows)), dim3(kDv), 0, stream, a);
     return hipGetLastError();
+}
+
+// ---- scratch of the allocation-free decode call
+// One file-scope device array; every GPU the library runs on holds its own copy
+// at its own address until the process ends (zero-initialised storage: it takes
+// no space in the library file).  In host code the array's name is not a device
+// address, so it is only ever used to look that address up.
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(hipStream_t stream, void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<void *> addr[kMaxDevices];
+    static std::mutex mu;
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (stream) {
+        hipDevice_t sdev = cur;
+        e = hipStreamGetDevice(stream, &sdev);
+        if (e != hipSuccess) return e;
+        if (sdev != cur) return hipErrorInvalidDevice;
+    }
+    if (cur < 0 || cur >= kMaxDevices) return hipErrorInvalidDevice;
+    void *p = addr[cur].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(mu);
+        p = addr[cur].load(std::memory_order_relaxed);
+        if (!p) {   // first call on this device, which is current
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            addr[cur].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 }  // namespace mimo

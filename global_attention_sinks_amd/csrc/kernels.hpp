@@ -128,5 +128,11 @@ struct DecodeGeom {
 DecodeGeom decode_geometry(int32_t Hq, int32_t Hkv, int32_t n_q);
 size_t decode_workspace_bytes(int32_t S, int32_t Hq, int32_t Hkv, int32_t n_q);
 hipError_t launch_decode(DecodeArgs a, hipStream_t stream);
+// Scratch of the allocation-free decode call: a device array of this many bytes
+// that the library holds on every GPU it runs on.  decode_scratch() returns its
+// address on the current device (looked up once per device); hipErrorInvalidDevice
+// if `stream` belongs to another device.
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+hipError_t decode_scratch(hipStream_t stream, void **ptr);
 
 }  // namespace mimo

@@ -199,6 +199,28 @@ mimo_status mimo_attn_decode(const mimo_attn_cfg *cfg, int32_t S, const uint16_t
 size_t mimo_attn_decode_workspace_size(const mimo_attn_cfg *cfg, int32_t S, int32_t cap);
 
 /*
+ * Allocation-free variant of mimo_attn_decode, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  The same kernels and results as mimo_attn_decode;
+ * the split-K partials and the plan go to a scratch array that the library
+ * holds on every GPU it runs on (MIMO_DECODE_NOALLOC_MAX_BYTES, kept until the
+ * process ends) instead of a caller workspace.  Arguments as in
+ * mimo_attn_decode without ws / ws_bytes.
+ *   - A call whose workspace (mimo_attn_decode_workspace_size) exceeds the
+ *     scratch returns MIMO_ERR_WORKSPACE; at 64 query heads that is more than
+ *     751 sequences with 4 KV heads or 879 with 8.
+ *   - `stream` must belong to the current device (else MIMO_ERR_INVALID_ARGUMENT).
+ *   - Every call on one GPU uses that GPU's one scratch array: calls that may
+ *     overlap in time on the same GPU (other streams, other threads) race and
+ *     give wrong results.  Calls in order on one stream are safe.  Nothing in
+ *     the scratch has to start at zero: each call writes all it reads.
+ */
+#define MIMO_DECODE_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+mimo_status mimo_attn_decode_noalloc(const mimo_attn_cfg *cfg, int32_t S, const uint16_t *q,
+                                     const int64_t *q_pos, const uint16_t *k_cache, const uint16_t *v_cache,
+                                     int32_t cap, const float *sinks, uint16_t *out, void *stream);
+
+/*
  * Multi-query decode for speculative verification: n_q query tokens per
  * sequence, the newest at q_pos[s] and token i at q_pos[s] - (n_q - 1 - i),
  * each attending causally to the cache (a draft token sees the tokens before

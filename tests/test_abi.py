@@ -191,6 +191,23 @@ def test_decode_workspace(lib):
     assert dec(lib, cfg_swa(), S=4, cap=128, ws=None, ws_bytes=0) == WS
 
 
+def test_decode_noalloc_contract(lib):
+    """The allocation-free decode validates like mimo_attn_decode and refuses a
+    call whose workspace exceeds its 32 MiB scratch, all before any HIP call."""
+    def call(cfg, S, cap=131072, q=FAKE):
+        return lib.mimo_attn_decode_noalloc(ctypes.byref(cfg), S, q, FAKE, FAKE, FAKE, cap, None, FAKE, None)
+    g = cfg_glob()
+    assert lib.mimo_attn_decode_workspace_size(ctypes.byref(g), 752, 131072) > 32 << 20
+    assert call(g, 752) == WS
+    assert "scratch" in err(lib) and str(32 << 20) in err(lib)
+    assert call(cfg_swa(), 880, cap=384) == WS
+    assert call(g, -1) == INVAL
+    assert call(cfg_swa(), 4, cap=64) == INVAL     # ring shorter than the window
+    assert call(cfg_swa(num_kv_heads=2), 4, cap=128) == UNSUP
+    assert call(g, 4, q=None) == INVAL
+    assert call(g, 0, q=None) == OK
+
+
 def decm(lib, cfg, S=4, nq=4, cap=256, ws=FAKE, ws_bytes=1 << 30, q=FAKE):
     return lib.mimo_attn_decode_multi(ctypes.byref(cfg), S, nq, q, FAKE, FAKE, FAKE, cap, None, FAKE, ws,
                                       ws_bytes, None)
