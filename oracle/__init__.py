@@ -71,6 +71,11 @@ def _load():
             ctypes.c_double, P, ctypes.c_int64, ctypes.c_double, ctypes.c_double,
             P, P, P, P, P, ctypes.c_int]
         lib.oracle_attention_backward.restype = None
+        lib.oracle_operand_rounding.argtypes = [
+            P, P, ctypes.c_int64, P, P, ctypes.c_int64, P,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_double, P, ctypes.c_int64, ctypes.c_double, ctypes.c_double, P, P, ctypes.c_int]
+        lib.oracle_operand_rounding.restype = None
         _lib = lib
     return _lib
 
@@ -147,6 +152,32 @@ def attention_backward(q, q_pos, k, k_pos, v, dout, *, sinks=None, window: int =
                                       float(v_scale), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ds),
                                       int(n_threads))
     return dq, dk, dv, ds
+
+
+def operand_rounding(q, q_pos, k, k_pos, v, *, sinks=None, window: int = 0, base: float,
+                     softmax_scale: float = SOFTMAX_SCALE, v_scale: float = V_SCALE,
+                     rope_dim: int = ROPE_DIM, n_threads: int = 0):
+    """What holding rope(q) and rope(k) as bf16 operands does to attention() (k
+    unrotated): returns (out_rounded, bound), both [nq,Hq,Dv] fp64 --
+    out_rounded: the rows with the rotated dims of rope(q) and rope(k_j) rounded
+    to the nearest bf16 before the scores; bound: the largest change of the exact
+    rows that any rounding within bf16's unit roundoff 2^-8 can cause (derived in
+    mimo_oracle.c, no first-order approximation)."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    q_pos = np.ascontiguousarray(q_pos, dtype=np.int64)
+    k_pos = np.ascontiguousarray(k_pos, dtype=np.int64)
+    nq, hq, dqk = q.shape
+    nk, hkv, _ = k.shape
+    dv = v.shape[2]
+    s = None if sinks is None else np.ascontiguousarray(sinks, dtype=np.float64)
+    out_r = np.empty((nq, hq, dv))
+    bound = np.empty((nq, hq, dv))
+    _load().oracle_operand_rounding(_ptr(q), _ptr(q_pos), nq, _ptr(k), _ptr(k_pos), nk, _ptr(v), hq, hkv, dqk,
+                                    dv, rope_dim, float(base), _ptr(s), int(window), float(softmax_scale),
+                                    float(v_scale), _ptr(out_r), _ptr(bound), int(n_threads))
+    return out_r, bound
 
 
 def prefill_backward(q, k, v, dout, *, sinks=None, pos0: int = 0, window: int, base: float, n_threads: int = 0):

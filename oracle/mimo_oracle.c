@@ -314,3 +314,149 @@ void oracle_attention_backward(const uint16_t *q, const int64_t *q_pos, int64_t 
     free(kr);
     free(dkr);
 }
+
+/* Nearest bf16 value of x (8 significant bits, ties to even), from the fp64
+ * value directly so there is no double rounding through fp32.  Values beyond
+ * bf16's normal range do not occur in the rows this is used on. */
+static double bf16_round(double x) {
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    double m = frexp(x, &e);                  /* x = m * 2^e, 0.5 <= |m| < 1 */
+    return ldexp(nearbyint(ldexp(m, 8)), e - 8);   /* default mode: ties to even */
+}
+
+/*
+ * What holding rope(q) and rope(k) as bf16 matrix-multiply operands does to the
+ * attention rows.  Only the R rotated dims change: the others are bf16 inputs
+ * already.  Same arguments as oracle_attention (k unrotated).  Outputs (fp64):
+ *
+ *   out_rounded [nq, Hq, Dv]: the rows with every rotated element of rope(q)
+ *     and rope(k_j) rounded to its nearest bf16 value before the scores.
+ *
+ *   bound [nq, Hq, Dv]: how far any such rounding can move the exact output.
+ *     A rounded element x' of x obeys |x' - x| <= u |x| with u = 2^-8 (half an
+ *     ulp is at most 2^-8 |x|; a kernel that lands a hair past a midpoint and
+ *     rounds to the other neighbour stays within it too), so each score moves by
+ *     at most delta_j = scale (2u + u^2) sum_{i<R} |rope(q)_i rope(k_j)_i|.
+ *     With p_j = exp(s_j)/Z, w_j = v_scale v_j and the row's largest delta_bar:
+ *     p'_j = p_j e^{D_j} / E with |D_j| <= delta_j and E = sum_k p_k e^{D_k} +
+ *     p_sink in [e^-delta_bar, e^delta_bar], hence |p'_j - p_j| <= p_j
+ *     (e^{delta_j + delta_bar} - 1) and |p'_sink - p_sink| <= p_sink (e^delta_bar
+ *     - 1); and o' - o = sum_j (p'_j - p_j)(w_j - o) + (p_sink - p'_sink) o, so
+ *     |o'_d - o_d| <= sum_j p_j (e^{delta_j + delta_bar} - 1) |w_jd - o_d|
+ *                     + p_sink (e^delta_bar - 1) |o_d|.
+ *     No first-order step: the bound holds for any rounding within u.
+ */
+void oracle_operand_rounding(const uint16_t *q, const int64_t *q_pos, int64_t nq,
+                             const uint16_t *k, const int64_t *k_pos, int64_t nk,
+                             const uint16_t *v, int Hq, int Hkv, int Dqk, int Dv, int R,
+                             double base, const double *sinks, int64_t window,
+                             double softmax_scale, double v_scale,
+                             double *out_rounded, double *bound, int n_threads) {
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+    const double u = ldexp(1.0, -8);
+    int group = Hq / Hkv;
+    double *kr = (double *)malloc((size_t)nk * Hkv * Dqk * sizeof(double));
+    #pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < nk; ++j) {
+        double buf[1024];
+        for (int g = 0; g < Hkv; ++g) {
+            const uint16_t *src = k + ((size_t)j * Hkv + g) * Dqk;
+            for (int d = 0; d < Dqk; ++d) buf[d] = bf16_value(src[d]);
+            rope_one(buf, kr + ((size_t)j * Hkv + g) * Dqk, Dqk, R, base, k_pos[j]);
+        }
+    }
+    #pragma omp parallel
+    {
+        size_t cap = (size_t)(nk > 0 ? nk : 1);
+        double *s = (double *)malloc(cap * sizeof(double));    /* exact scores */
+        double *sr = (double *)malloc(cap * sizeof(double));   /* scores of the rounded operands */
+        double *dl = (double *)malloc(cap * sizeof(double));   /* delta_j */
+        int64_t *keys = (int64_t *)malloc(cap * sizeof(int64_t));
+        double qraw[1024], qrot[1024], o[1024], acc[1024];
+        #pragma omp for schedule(dynamic, 1)
+        for (int64_t idx = 0; idx < nq * Hq; ++idx) {
+            int64_t r = idx / Hq;
+            int h = (int)(idx % Hq);
+            int g = h / group;
+            const uint16_t *qs = q + ((size_t)r * Hq + h) * Dqk;
+            for (int d = 0; d < Dqk; ++d) qraw[d] = bf16_value(qs[d]);
+            rope_one(qraw, qrot, Dqk, R, base, q_pos[r]);
+            int64_t n = 0;
+            double dbar = 0.0;
+            for (int64_t j = 0; j < nk; ++j) {
+                if (!visible(q_pos[r], k_pos[j], window)) continue;
+                const double *kj = kr + ((size_t)j * Hkv + g) * Dqk;
+                double dot = 0.0, dotr = 0.0, mag = 0.0;
+                for (int d = 0; d < Dqk; ++d) {
+                    dot += qrot[d] * kj[d];
+                    if (d < R) {
+                        dotr += bf16_round(qrot[d]) * bf16_round(kj[d]);
+                        mag += fabs(qrot[d] * kj[d]);
+                    } else {
+                        dotr += qrot[d] * kj[d];
+                    }
+                }
+                s[n] = softmax_scale * dot;
+                sr[n] = softmax_scale * dotr;
+                dl[n] = softmax_scale * (2.0 * u + u * u) * mag;
+                if (dl[n] > dbar) dbar = dl[n];
+                keys[n] = j;
+                ++n;
+            }
+            double *orr = out_rounded + ((size_t)r * Hq + h) * Dv;
+            double *bd = bound + ((size_t)r * Hq + h) * Dv;
+            const double *sk = sinks ? &sinks[h] : NULL;
+            /* both rows by the same two-pass softmax: pass 0 the exact scores
+             * (kept in o for the bound), pass 1 the rounded ones */
+            for (int pass = 0; pass < 2; ++pass) {
+                const double *sc = pass == 0 ? s : sr;
+                double *dst = pass == 0 ? o : orr;
+                double m = -INFINITY;
+                for (int64_t t = 0; t < n; ++t) if (sc[t] > m) m = sc[t];
+                if (sk && *sk > m) m = *sk;
+                if (m == -INFINITY) {
+                    for (int d = 0; d < Dv; ++d) dst[d] = 0.0;
+                    continue;
+                }
+                double z = 0.0;
+                for (int d = 0; d < Dv; ++d) acc[d] = 0.0;
+                for (int64_t t = 0; t < n; ++t) {
+                    double p = exp(sc[t] - m);
+                    z += p;
+                    const uint16_t *vj = v + ((size_t)keys[t] * Hkv + g) * Dv;
+                    for (int d = 0; d < Dv; ++d) acc[d] += p * bf16_value(vj[d]);
+                }
+                z += sk ? exp(*sk - m) : 0.0;
+                for (int d = 0; d < Dv; ++d) dst[d] = v_scale * acc[d] / z;
+            }
+            /* the bound, from the exact p_j, p_sink and o */
+            double m = -INFINITY;
+            for (int64_t t = 0; t < n; ++t) if (s[t] > m) m = s[t];
+            if (sk && *sk > m) m = *sk;
+            for (int d = 0; d < Dv; ++d) bd[d] = 0.0;
+            if (m == -INFINITY) continue;
+            double z = sk ? exp(*sk - m) : 0.0;
+            for (int64_t t = 0; t < n; ++t) z += exp(s[t] - m);
+            for (int64_t t = 0; t < n; ++t) {
+                double p = exp(s[t] - m) / z;
+                double f = p * expm1(dl[t] + dbar);
+                const uint16_t *vj = v + ((size_t)keys[t] * Hkv + g) * Dv;
+                for (int d = 0; d < Dv; ++d) bd[d] += f * fabs(v_scale * bf16_value(vj[d]) - o[d]);
+            }
+            if (sk) {
+                double ps = exp(*sk - m) / z;
+                for (int d = 0; d < Dv; ++d) bd[d] += ps * expm1(dbar) * fabs(o[d]);
+            }
+        }
+        free(s);
+        free(sr);
+        free(dl);
+        free(keys);
+    }
+    free(kr);
+}

@@ -577,3 +577,84 @@ def test_input_rounding_is_round_to_nearest_even():
     # 1 + 2^-8 is a tie between 1 and 1+2^-7 -> even (1.0); 1+3*2^-8 -> 1+2^-6
     assert list(gen.bf16_bits_to_f32(b)[:3]) == [1.0, 1.0, 1.015625]
     assert np.allclose(gen.bf16_bits_to_f32(b), x, rtol=2 ** -8)
+
+
+# ------------------------------------- bf16 operands: rounded rows and their bound
+
+def _scaled_case(seed, nq, nk, hq, hkv, qmul, kmul):
+    qb, kb, vb = rand_case(seed, nq, nk, hq, hkv, 192, 128)
+    return bf16(f64(qb) * qmul), bf16(f64(kb) * kmul), vb
+
+
+def _round_rotated(x):
+    """The first 64 (rotated) dims through torch's bfloat16 cast; the rest unchanged."""
+    y = x.copy()
+    y[..., :64] = torch.from_numpy(np.ascontiguousarray(x[..., :64])).to(torch.bfloat16).to(torch.float64).numpy()
+    return y
+
+
+@pytest.mark.parametrize("window,with_sink", [(0, False), (16, True)])
+def test_operand_rounding_rows_match_sdpa_on_rounded_operands(window, with_sink):
+    """out_rounded equals torch SDPA over rope(q), rope(k) whose rotated dims went
+    through torch's own bf16 cast; at position 0 (no rotation) nothing is rounded
+    and out_rounded is the exact row."""
+    nq = nk = 40
+    qb, kb, vb = _scaled_case(71 + window, nq, nk, 4, 2, 2.0, 4.0)
+    sinks = np.array([0.5, -1.0, 2.0, 0.0]) if with_sink else None
+    pos = np.arange(90000, 90000 + nk, dtype=np.int64)
+    got, bound = oracle.operand_rounding(qb, pos, kb, pos, vb, sinks=sinks, window=window, base=1e7)
+    qr = _round_rotated(oracle.rope_partial(qb, pos, 1e7))
+    kr = _round_rotated(oracle.rope_partial(kb, pos, 1e7))
+    want = _sdpa_reference(qr, kr, f64(vb), pos, pos, sinks, window, oracle.SOFTMAX_SCALE, 0.707)
+    assert np.max(np.abs(got - want)) < 1e-12
+    exact = oracle.attention(qb, pos, kb, pos, vb, sinks=sinks, window=window, base=1e7)
+    assert np.max(np.abs(got - exact)) > 1e-4          # the rounding does move these rows
+    assert np.all(np.abs(got - exact) <= bound)
+    z = np.zeros(nk, np.int64)                           # one position: no rotation
+    got0, _ = oracle.operand_rounding(qb, z, kb, z, vb, sinks=sinks, window=0, base=1e7)
+    assert np.max(np.abs(got0 - oracle.attention(qb, z, kb, z, vb, sinks=sinks, window=0, base=1e7))) < 1e-13
+
+
+@pytest.mark.parametrize("window,with_sink", [(0, False), (16, True)])
+def test_operand_rounding_bound_holds_for_adversarial_perturbations(window, with_sink):
+    """Brute force over perturbations of the rotated operands within bf16's unit
+    roundoff 2^-8 (torch SDPA on the perturbed operands): random ones stay within
+    the bound everywhere, and one aimed at a chosen output element (every key's
+    score pushed by half the per-score budget, each in the direction that moves
+    that element up) reaches a good part of its bound, so the bound is not vacuous."""
+    nq, nk, hq, hkv = 8, 48, 4, 2
+    qb, kb, vb = _scaled_case(91 + window, nq, nk, hq, hkv, 2.0, 4.0)
+    sinks = np.array([1.0, -0.5, 0.0, 2.5]) if with_sink else None
+    pos = np.arange(200000, 200000 + nk, dtype=np.int64)
+    qpos = pos[nk - nq:]
+    q_rows = qb[:nq]
+    u = 2.0 ** -8
+    base, scale = 1e7, oracle.SOFTMAX_SCALE
+    exact = oracle.attention(q_rows, qpos, kb, pos, vb, sinks=sinks, window=window, base=base)
+    _, bound = oracle.operand_rounding(q_rows, qpos, kb, pos, vb, sinks=sinks, window=window, base=base)
+    qr = oracle.rope_partial(q_rows, qpos, base)
+    kr = oracle.rope_partial(kb, pos, base)
+    v = f64(vb)
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        eq = rng.uniform(-u, u, qr.shape)
+        ek = rng.uniform(-u, u, kr.shape)
+        eq[..., 64:] = 0
+        ek[..., 64:] = 0
+        o = _sdpa_reference(qr * (1 + eq), kr * (1 + ek), v, qpos, pos, sinks, window, scale, 0.707)
+        assert np.all(np.abs(o - exact) <= bound)
+    # aimed: row r, head h, dim d; keys of KV head g get k_i (1 + u sign(q_i k_i) sigma_j)
+    r, h, d = nq - 1, 3, 17
+    g = h // (hq // hkv)
+    s = scale * np.einsum("d,jd->j", qr[r, h], kr[:, g])
+    vis = (pos <= qpos[r]) & ((qpos[r] - pos < window) if window else True)
+    s = np.where(vis, s, -np.inf)
+    m = max(s.max(), sinks[h] if with_sink else -np.inf)
+    p = np.exp(s - m) / (np.exp(s - m).sum() + (np.exp(sinks[h] - m) if with_sink else 0.0))
+    sigma = np.sign(p * (0.707 * v[:, g, d] - exact[r, h, d]))
+    ek = np.zeros_like(kr)
+    ek[:, g, :64] = u * np.sign(qr[r, h, None, :64] * kr[:, g, :64]) * sigma[:, None]
+    o = _sdpa_reference(qr, kr * (1 + ek), v, qpos, pos, sinks, window, scale, 0.707)
+    moved = o[r, h, d] - exact[r, h, d]
+    assert 0 < moved <= bound[r, h, d]
+    assert moved >= 0.1 * bound[r, h, d]
