@@ -112,6 +112,24 @@ def test_global_prefill_contract(lib):
     assert glob(lib, cfg_glob(), Tq=0, Tk=0, q=None, out=None) == OK
 
 
+def test_global_prefill_null_workspace_is_the_plain_call(lib):
+    """The boundary's global prefill is q, k, v in and out out (one query chunk
+    against its prefix).  The tile-image workspace is an optional extra: ws = NULL
+    is accepted at every size (the attention kernel then stages each tile itself;
+    tests/test_gpu_parity.py and tests/test_gpu_fullsize.py run it against the
+    oracle as the "staged" cases), ws_bytes is not looked at without a ws, and the
+    only workspace error is a non-NULL ws smaller than the size query."""
+    for ws_bytes in (0, 5):
+        assert glob(lib, cfg_glob(), Tq=16, Tk=17, ws=None, ws_bytes=ws_bytes) == INVAL
+        assert "q_pos0 + Tq" in err(lib)          # the error is the real one, never the workspace
+        assert glob(lib, cfg_glob(), Tq=0, Tk=0, q=None, out=None, ws=None, ws_bytes=ws_bytes) == OK
+    need = lib.mimo_attn_prefill_workspace_size(ctypes.byref(cfg_glob()), 1, 16)
+    assert glob(lib, cfg_glob(), ws=FAKE, ws_bytes=need - 1) == WS
+    # the sliding prefill's sinks may be NULL (no sink column), never required
+    assert swa(lib, cfg_swa(), sinks=None, T=0) == OK
+    assert swa(lib, cfg_swa(), sinks=None, T=-1) == INVAL and "sink" not in err(lib)
+
+
 def varlen(lib, cfg, Bn=2, max_q=64, total_q=128, q=FAKE, cu_q=FAKE, cu_k=FAKE, total_k=256, ws=None, ws_bytes=0):
     return lib.mimo_attn_prefill_varlen(ctypes.byref(cfg), q, FAKE, FAKE, None, Bn, cu_q, cu_k, None, max_q,
                                         total_q, total_k, FAKE, None, ws, ws_bytes, None)
