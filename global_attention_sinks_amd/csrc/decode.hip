@@ -30,32 +30,6 @@
 
 #include "kernels.hpp"
 
-// One-token decode: at most 4 KV heads (waves) per workgroup, so that every
-// workgroup runs one wave per SIMD and the step ranges cover all CUs (on
-// sliding layers, 8 KV heads in one workgroup left half the CUs idle).
-#ifndef MIMO_DECODE_SPLIT_HEADS
-#define MIMO_DECODE_SPLIT_HEADS 1
-#endif
-// Steps whose loads are in flight per wave (2: the computed one and the next).
-#ifndef MIMO_DECODE_DEPTH
-#define MIMO_DECODE_DEPTH 2
-#endif
-// fp8 steps are half the bytes of bf16 ones: one-token fp8 decode keeps this
-// many steps' loads in flight per wave to cover the same HBM latency.
-#ifndef MIMO_DECODE_FP8_DEPTH
-#define MIMO_DECODE_FP8_DEPTH 3
-#endif
-// Multi-query decode with more than 2 column tiles per KV head: its 2 or 4
-// waves read each step from HBM once, through LDS (0: each wave reads it).
-#ifndef MIMO_DECODE_SHARED
-#define MIMO_DECODE_SHARED 1
-#endif
-// Short caches (sliding rings, windowed paged caches) decoded one workgroup per
-// (sequence, KV head) without the split (0: always split).
-#ifndef MIMO_DECODE_DIRECT
-#define MIMO_DECODE_DIRECT 1
-#endif
-
 namespace mimo {
 
 namespace {
@@ -65,6 +39,11 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr int kStep = 32;              // cache slots per step
 constexpr int kPlanThreads = 1024;
 constexpr int kMaxGroups = kDecodeWaves;   // workgroups of one wave when Hkv = 1
+// Steps whose loads are in flight per wave: the computed one and the next; fp8
+// steps are half the bytes, so one-token fp8 decode keeps three in flight to
+// cover the same HBM latency.
+constexpr int kDepth = 2;
+constexpr int kFp8Depth = 3;
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
@@ -726,9 +705,12 @@ DecodeGeom decode_geometry(int32_t Hq, int32_t Hkv, int32_t n_q) {
     const int G = Hq / Hkv;
     const int tiles = (G * n_q + 15) / 16;
     if (n_q == 1) {   // one tile per wave, one wave per KV head
-        m.nc = 1; m.wph = 1; m.kvpw = MIMO_DECODE_SPLIT_HEADS ? (Hkv < 4 ? Hkv : 4) : Hkv;
+        // at most 4 KV heads (waves) per workgroup, so every workgroup runs one wave
+        // per SIMD and the step ranges cover all CUs (8 KV heads in one workgroup
+        // left half the CUs idle on sliding layers)
+        m.nc = 1; m.wph = 1; m.kvpw = Hkv < 4 ? Hkv : 4;
         while (Hkv % m.kvpw) --m.kvpw;
-    } else if (tiles <= 2 || !MIMO_DECODE_SHARED) {   // up to 2 tiles per wave, at most four waves per workgroup
+    } else if (tiles <= 2) {   // up to 2 tiles per wave, at most four waves per workgroup
         m.wph = (tiles + 1) / 2;
         m.nc = (tiles + m.wph - 1) / m.wph;
         m.kvpw = m.wph >= 4 ? 1 : 4 / m.wph;
@@ -762,13 +744,13 @@ void launch_shared(const DecodeArgs &a, const DecodeGeom &m, hipStream_t stream)
         hipLaunchKernelGGL((decode_partial_kernel<2, 256, false, true, 2, SW>), grid, block, 0, stream, a);
 }
 
-template <int NC, int MAXT, int DEPTH = 2>
+template <int NC, int MAXT, int DEPTH = kDepth>
 void launch_partial(const DecodeArgs &a, const DecodeGeom &m, hipStream_t stream) {
     const dim3 grid(m.n_groups, m.n_hsub), block(m.threads);
     if (!a.table)
         hipLaunchKernelGGL((decode_partial_kernel<NC, MAXT, false, false, DEPTH>), grid, block, 0, stream, a);
     else if (a.fp8)
-        hipLaunchKernelGGL((decode_partial_kernel<NC, MAXT, true, true, (NC == 1 ? MIMO_DECODE_FP8_DEPTH : DEPTH)>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((decode_partial_kernel<NC, MAXT, true, true, (NC == 1 ? kFp8Depth : DEPTH)>), grid, block, 0, stream, a);
     else
         hipLaunchKernelGGL((decode_partial_kernel<NC, MAXT, false, true, DEPTH>), grid, block, 0, stream, a);
 }
@@ -789,7 +771,7 @@ size_t decode_workspace_bytes(int32_t S, int32_t Hq, int32_t Hkv, int32_t n_q) {
 constexpr int kDirectMaxSteps = 8;
 
 static bool decode_direct(const DecodeArgs &a, const DecodeGeom &m) {
-    if (m.wph != 1 || MIMO_DECODE_DIRECT == 0) return false;
+    if (m.wph != 1) return false;
     int64_t steps;
     if (a.table) {
         if (a.window <= 0) return false;
@@ -834,12 +816,7 @@ hipError_t launch_decode(DecodeArgs a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.n_q == 1) {
-#if MIMO_DECODE_SPLIT_HEADS
-        launch_partial<1, 256, MIMO_DECODE_DEPTH>(a, m, stream);   // at most 4 KV heads: 256 threads
-#else
-        if (m.threads <= 256) launch_partial<1, 256, MIMO_DECODE_DEPTH>(a, m, stream);
-        else launch_partial<1, 512>(a, m, stream);
-#endif
+        launch_partial<1, 256>(a, m, stream);   // at most 4 KV heads: 256 threads
     }
     else if (m.wph == 2 && m.kvpw == 1) launch_shared<2>(a, m, stream);
     else if (m.wph == 4 && m.kvpw == 1) launch_shared<4>(a, m, stream);

@@ -81,16 +81,11 @@ size_t backward_workspace_bytes(int32_t B, int32_t T, int32_t Hq);
 hipError_t launch_backward(BwdArgs a, hipStream_t stream);
 
 // ---- decode (decode.hip)
-#ifndef MIMO_DECODE_WAVES
-#define MIMO_DECODE_WAVES 1024
-#endif
-#ifndef MIMO_DECODE_MIN_STEPS
-#define MIMO_DECODE_MIN_STEPS 1
-#endif
 // The batch's 32-slot steps are split evenly over step ranges, each taking at
-// least kDecodeMinSteps steps; the partial pass runs kDecodeWaves waves in all.
-constexpr int kDecodeWaves = MIMO_DECODE_WAVES;
-constexpr int kDecodeMinSteps = MIMO_DECODE_MIN_STEPS;
+// least kDecodeMinSteps steps; the partial pass runs kDecodeWaves waves in all
+// (one per SIMD of the 256 CUs).
+constexpr int kDecodeWaves = 1024;
+constexpr int kDecodeMinSteps = 1;
 constexpr int kDecodeMaxCap = 1 << 30;
 struct DecodeArgs {
     const uint16_t *q;

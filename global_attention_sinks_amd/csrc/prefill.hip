@@ -501,7 +501,9 @@ __device__ __forceinline__ float sumsq8(u32x4 x) {
 
 __global__ __launch_bounds__(256) void kv_image_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t vs[kImgNK * kPrepVS];
-    __shared__ float rn[kImgNK];   // squared norm of each rotated key row of the tile
+    // squared norms of each rotated key row's pieces: 4 rotating (row, 8 pairs)
+    // pieces, then the 16 pass-through chunks; summed in this order by one lane
+    __shared__ float rn[kImgNK][4 + 16];
     const int b = blockIdx.y, g = blockIdx.z, tid = threadIdx.x;
     int Tk, tile_base;
     size_t k_tok0;
@@ -520,8 +522,6 @@ __global__ __launch_bounds__(256) void kv_image_kernel(PrefillArgs a) {
     }
     const int ntile = (Tk + kImgNK - 1) / kImgNK;
     const size_t krow = (size_t)a.Hkv * kDqk, vrow = (size_t)a.Hkv * kDv;
-    if (tid < kImgNK) rn[tid] = 0.0f;
-    __syncthreads();
     for (int t = blockIdx.x; t < ntile; t += gridDim.x) {
         const size_t tile_id = (size_t)(tile_base + t) * a.Hkv + g;
         uint16_t *wk = a.kv_img + tile_id * kImgTile;
@@ -538,7 +538,7 @@ __global__ __launch_bounds__(256) void kv_image_kernel(PrefillArgs a) {
             }
             *reinterpret_cast<u32x4 *>(wk + row * KSTR + 8 * cc) = x;
             *reinterpret_cast<u32x4 *>(wk + row * KSTR + 32 + 8 * cc) = y;
-            atomicAdd(&rn[row], sumsq8(x) + sumsq8(y));
+            rn[row][cc] = sumsq8(x) + sumsq8(y);
         }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {   // pass-through chunks 8..23
@@ -546,7 +546,7 @@ __global__ __launch_bounds__(256) void kv_image_kernel(PrefillArgs a) {
             u32x4 x = {0, 0, 0, 0};
             if (j < Tk) x = ldg128(a.k + (k_tok0 + j) * krow + (size_t)g * kDqk + 8 * c);
             *reinterpret_cast<u32x4 *>(wk + row * KSTR + 8 * c) = x;
-            atomicAdd(&rn[row], sumsq8(x));
+            rn[row][4 + (u & 15)] = sumsq8(x);
         }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {   // V rows into LDS
@@ -556,9 +556,11 @@ __global__ __launch_bounds__(256) void kv_image_kernel(PrefillArgs a) {
             *reinterpret_cast<u32x4 *>(vs + row * kPrepVS + 8 * c) = x;
         }
         __syncthreads();
-        if (tid < kImgNK) {   // wave 0: the tile's largest key norm; clear for the next tile
-            float n = sqrtf(rn[tid]);
-            rn[tid] = 0.0f;
+        if (tid < kImgNK) {   // wave 0: the tile's largest key norm, summed in a fixed order
+            float ss = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4 + 16; ++i) ss += rn[tid][i];
+            float n = sqrtf(ss);
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) n = fmaxf(n, __shfl_xor(n, off));
             if (tid == 0) a.kv_norm[tile_id] = n;
@@ -1239,12 +1241,6 @@ static hipError_t launch_variant(PrefillArgs a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Sliding layers with 8 query heads per KV head and a window <= 128 run the
-// band kernel (0: the per-block kernel).
-#ifndef MIMO_PREFILL_BAND
-#define MIMO_PREFILL_BAND 1
-#endif
-
 size_t prefill_image_count(int32_t B, int64_t total_k, int32_t Hkv) {
     return (size_t)((total_k + kImgNK - 1) / kImgNK + B) * Hkv;
 }
@@ -1286,7 +1282,7 @@ hipError_t launch_prefill(PrefillArgs a, hipStream_t stream) {
     // head, window <= 128), else 4 heads x 32-key tiles, two workgroups per CU.
     // Global prefixes are long: 8 heads share each 64-key tile.
     const bool wide = (a.Hq / a.Hkv) % 8 == 0;
-    if (MIMO_PREFILL_BAND && a.window > 0 && a.window <= kBandMaxWindow && a.Hq == 8 * a.Hkv)
+    if (a.window > 0 && a.window <= kBandMaxWindow && a.Hq == 8 * a.Hkv)
         return launch_band(a, stream);
     if (a.window == 0 && wide) return launch_variant<8, 64>(a, stream);
     return launch_variant<4, 32>(a, stream);
