@@ -1,6 +1,9 @@
 """Helpers for the GPU tests: moving bf16 bit arrays to the device and back,
 and the parity bar (max-abs 2e-2, mean-abs 2e-3 on bf16 outputs against the
-fp64 oracle)."""
+fp64 oracle; for gradients, which are not bounded by the values as outputs are,
+2e-2 + 2^-7 |ref| per element: a bf16 gradient near 8 rounds by up to 1.6e-2 on
+its own, and 2^-7 |ref| allows that storage rounding and as much again from the
+bf16 operands)."""
 import sys
 
 import numpy as np
@@ -39,3 +42,16 @@ def assert_parity(got: np.ndarray, ref: np.ndarray, what: str, max_abs=MAX_ABS, 
     mx, mn = float(d.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0
     say(f"  {what}: max-abs {mx:.3e} mean-abs {mn:.3e} over {d.size} values")
     assert mx <= max_abs and mn <= mean_abs, f"{what}: max-abs {mx:.3e} mean-abs {mn:.3e}"
+
+
+def assert_grad_parity(got: np.ndarray, ref: np.ndarray, what: str):
+    """Gradient bar: |got - ref| <= 2e-2 + 2^-7 |ref| per element, mean-abs <= 2e-3."""
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
+    d = np.abs(got - ref)
+    allowed = MAX_ABS + 2.0 ** -7 * np.abs(ref)
+    worst = float(np.max(d / allowed)) if d.size else 0.0
+    mn = float(d.mean()) if d.size else 0.0
+    say(f"  {what}: max-abs {float(d.max()) if d.size else 0.0:.3e} (max |ref| {float(np.abs(ref).max()):.2f}), "
+        f"worst err / (2e-2 + 2^-7 |ref|) {worst:.3f}, mean-abs {mn:.3e}")
+    assert worst <= 1.0 and mn <= MEAN_ABS, f"{what}: worst {worst:.3f} of the bar, mean-abs {mn:.3e}"

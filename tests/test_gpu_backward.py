@@ -1,9 +1,9 @@
 """GPU parity of the prefill backward (dq, dk, dv, d sink) against the fp64
 oracle's chain-rule gradients on the same seeded inputs.  The GPU backward
-takes the GPU forward's output and LSE, as a trainer would.  Bar: the output
-bar (max-abs <= 2e-2, mean-abs <= 2e-3) in units of the gradient's largest
-reference magnitude when that exceeds 1 -- gradients are not bounded by the
-values as outputs are, and a bf16 value near 8 alone rounds by up to 1.6e-2.  d sink_h = -sum_r p_sink(r) D(r) sums every row
+takes the GPU forward's output and LSE, as a trainer would.  Bar for dq, dk,
+dv: |error| <= 2e-2 + 2^-7 |ref| per element and mean-abs <= 2e-3 -- gradients
+are not bounded by the values as outputs are, and a bf16 value near 8 alone
+rounds by up to 1.6e-2.  d sink_h = -sum_r p_sink(r) D(r) sums every row
 of the head, and the backward forms D(r) = <dO(r), O(r)> from the forward's
 stored bf16 output O instead of the exact o, so its bar is that error carried
 through: |error| <= sum_r p_sink(r) <|dO(r)|, |O(r) - o(r)|> + 1 % of the
@@ -17,7 +17,7 @@ import torch
 import oracle
 from global_attention_sinks_amd import binding as Bd
 from global_attention_sinks_amd import inputs as gen
-from tests.gpu_util import assert_parity, dev, dev_bf16, host_bits, host_f64, say
+from tests.gpu_util import assert_grad_parity, dev, dev_bf16, host_bits, host_f64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -63,10 +63,7 @@ def run_fwd_bwd(d, dout, cfg, pos0=0):
 
 def check_grads(got, ref, what, bar=None):
     for name, g, r in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
-        gv = host_f64(g)
-        scale = max(1.0, float(np.abs(r).max()))
-        say(f"    {name}: max |ref| {np.abs(r).max():.3e}")
-        assert_parity(gv, r, f"{what} {name}", max_abs=2e-2 * scale, mean_abs=2e-3 * scale)
+        assert_grad_parity(host_f64(g), r, f"{what} {name}")
     if ref[3] is not None:
         gs = got[3].cpu().numpy().astype(np.float64)
         err = np.abs(gs - ref[3])
