@@ -12,6 +12,14 @@ step's algorithmic attention FLOPs (2*(192+128)*64 per visible query-key pair)
 over the measured step time.  Per-launch durations are taken with HIP events
 on the stream the kernels are launched on (torch's current stream).
 
+After the step, the default run also measures, each in `phases` with its own
+figures: the on-box peaks (a bf16 MFMA loop on N(0,1) operands and on ones, a
+1 GiB HBM copy and read; `peaks`), the sliding-window prefill B=1 x T=512 with
+the Infinity Cache flushed before each call, and the 524288-token global
+prefill in 8 query chunks of 65536 (one warmup and two timed passes, with its
+own roofline object; --no-long skips it).  Every kernel figure is given as a
+fraction of the vendor peaks (2.5 PFLOP/s bf16, 8 TB/s) and of the measured ones.
+
 --workload long_prefill instead times the 524288-token global prefill run as 8
 query chunks of 65536, each against its full causal prefix.
 
@@ -188,69 +196,214 @@ def run_layer_step(ph, Bd, ev=None):
                                                                d["sinks"], d["out"], ws=d["ws"]))
 
 
+# ------------------------------------------------------------ on-box peaks
+
+def _event_ms(torch, fn, reps):
+    """Median over reps of fn's time between HIP events recorded on torch's
+    current stream (the stream the kernels are launched on)."""
+    pairs = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in pairs]))
+
+
+def measure_peaks(torch, Bd):
+    """What a plain bf16 MFMA loop (on N(0,1) operands, like attention's, and on
+    ones) and plain HBM streams (a 1 GiB copy, a 1 GiB read) reach on this card."""
+    waves = Bd.load_peaks().mimo_peak_mfma_waves()
+    sink = torch.empty(waves, dtype=torch.float32, device="cuda")
+    gen_ = torch.Generator(device="cuda")
+    gen_.manual_seed(7)
+    rnd = torch.randn(1 << 22, generator=gen_, device="cuda").to(torch.bfloat16)
+    ones = torch.ones(1 << 22, dtype=torch.bfloat16, device="cuda")
+    # ~2.5 ms launches back to back for about a second, so the clock settles where
+    # sustained MFMA work holds it (the attention calls run 18 ms to seconds); the
+    # median of the second half of the launches
+    iters, reps = 1000, 400
+    flops = Bd.peak_mfma_flops(iters)
+    res = {"mfma_loop": f"{waves} waves x {iters * 64} MFMA 32x32x16 bf16 per launch, 8 chains, operands "
+                        f"changing every MFMA; {reps} launches back to back, median of the last {reps // 2}"}
+    for name, ops in (("randn", rnd), ("ones", ones)):
+        pairs = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            Bd.peak_mfma_bf16(ops, iters, sink)
+            b.record()
+            pairs.append((a, b))
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in pairs[reps // 2:]]))
+        res[f"mfma_bf16_{name}_tflops"] = flops / (ms * 1e-3) / 1e12
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    Bd.peak_copy(src, dst)
+    res["hbm_copy_gbs"] = 2 * n / (_event_ms(torch, lambda: Bd.peak_copy(src, dst), 10) * 1e-3) / 1e9
+    Bd.peak_read(src, out)
+    res["hbm_read_gbs"] = n / (_event_ms(torch, lambda: Bd.peak_read(src, out), 10) * 1e-3) / 1e9
+    del src, dst
+    return res
+
+
+# ------------------------------------------------------------ the two workloads outside the step
+
+def bench_swa_small(torch, gen, Bd, peaks, reps=10):
+    """Sliding-window + sink prefill B=1 x T=512 (64 q / 8 KV heads): it fits in
+    the 256 MB Infinity Cache, so a 512 MiB buffer is written between reps (untimed)
+    and every rep reads its inputs from HBM."""
+    d = gen.prefill_inputs(1, 512, 64, 8, seed=1000, with_sinks=True)
+    cfg = Bd.swa_cfg()
+    q, k, v = _dev_bf16(torch, d["q"]), _dev_bf16(torch, d["k"]), _dev_bf16(torch, d["v"])
+    sinks = torch.from_numpy(d["sinks"]).to("cuda")
+    out = torch.empty((1, 512, 64, 128), dtype=torch.bfloat16, device="cuda")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flops = FLOP_PER_PAIR_HEAD * 64 * swa_pairs(512, 128)
+    nbytes = prefill_bytes(1, 512, 512, 64, 8, True)
+    ts = []
+    for i in range(reps + 2):
+        flush.fill_(i & 255)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        Bd.mimo_attn_prefill_swa(cfg, q, k, v, sinks, out)
+        b.record()
+        ts.append((a, b))
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ts[2:]]))
+    tfl, gbs = flops / (ms * 1e-3) / 1e12, nbytes / (ms * 1e-3) / 1e9
+    return {"ms": ms, "tflops": tfl, "gbs": gbs, "frac_mfma_peak": tfl / PEAK_BF16_TFLOPS,
+            "frac_hbm_peak": gbs / PEAK_HBM_GBS, "frac_measured_hbm_copy": gbs / peaks["hbm_copy_gbs"],
+            "note": f"median of {reps} calls, Infinity Cache flushed before each; launch-latency bound "
+                    f"({flops / 1e9:.2f} GFLOP, {nbytes / 1e6:.1f} MB)"}
+
+
+def bench_long_prefill(torch, gen, Bd, peaks, warmup=1, steps=2):
+    """Global causal prefill of 524288 tokens in 8 query chunks of 65536, each
+    against its whole prefix, one tile-image workspace for all chunks; q is drawn
+    and uploaded chunk by chunk."""
+    T, C = 524288, 65536
+    n_chunks = T // C
+    cfg = Bd.global_cfg()
+    kv = gen.global_prefill_chunk(T, 64, 4, seed=1004, t_lo=T, t_hi=T)
+    k, v = _dev_bf16(torch, kv["k"]), _dev_bf16(torch, kv["v"])
+    del kv
+    q = torch.empty((1, T, 64, 192), dtype=torch.bfloat16, device="cuda")
+    for c in range(n_chunks):
+        q[:, c * C:(c + 1) * C] = _dev_bf16(torch, gen.global_prefill_chunk(T, 64, 4, seed=1004, t_lo=c * C,
+                                                                             t_hi=(c + 1) * C, kv=False)["q"])
+    out = torch.empty((1, T, 64, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(Bd.mimo_attn_prefill_workspace_size(cfg, 1, T), dtype=torch.uint8, device="cuda")
+
+    def chunk(c):
+        Bd.mimo_attn_prefill_global(cfg, q[:, c * C:(c + 1) * C], k[:, :(c + 1) * C], v[:, :(c + 1) * C],
+                                    out[:, c * C:(c + 1) * C], q_pos0=c * C, ws=ws)
+
+    for _ in range(warmup):
+        for c in range(n_chunks):
+            chunk(c)
+    torch.cuda.synchronize()
+    evs = []
+    for i in range(steps):
+        row = []
+        for c in range(n_chunks):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            chunk(c)
+            b.record()
+            row.append((a, b))
+        evs.append(row)
+        torch.cuda.synchronize()
+        log(f"long prefill step {i} done")
+    chunk_ms = [float(np.mean([r[c][0].elapsed_time(r[c][1]) for r in evs])) for c in range(n_chunks)]
+    ms = float(sum(chunk_ms))
+    flops = FLOP_PER_PAIR_HEAD * 64 * causal_pairs(0, T)
+    nbytes = prefill_bytes(1, T, T, 64, 4, False)
+    tfl = flops / (ms * 1e-3) / 1e12
+    del q, k, v, out, ws
+    return {"ms": ms, "tflops": tfl, "gbs": nbytes / (ms * 1e-3) / 1e9, "frac_mfma_peak": tfl / PEAK_BF16_TFLOPS,
+            "chunks_ms": chunk_ms,
+            "roofline": {"bound": "mfma", "kernel": "prefill_image_kernel (8 global causal chunks; their K/V image "
+                                                    "passes are inside the timed calls)",
+                         "achieved": tfl, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tfl / PEAK_BF16_TFLOPS,
+                         "frac_measured_mfma_randn": tfl / peaks["mfma_bf16_randn_tflops"],
+                         "traffic": profiled_traffic("long prefill T524288 (8 chunks)"),
+                         "algorithmic_flops": flops, "algorithmic_bytes": nbytes}}
+
+
 # ------------------------------------------------------------ CPU baseline
 
-def cpu_baseline_layer_step(ph, budget_s: float):
-    """Time the fp64 oracle on a bounded sample of each phase and extrapolate
-    each phase by its FLOP count; returns the oracle's step-equivalent rate.
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    Each prefill phase first runs a small pilot sample, then a sample sized to
-    take about a quarter of budget_s; decode runs whole sequences."""
+
+def cpu_baseline_layer_step(ph, budget_s: float, gen):
+    """Time the fp64 oracle on the host cores: the sliding prefill (B4 x T8192) and
+    the mixed decode (all 64 + 16 sequences) in full; the global prefill (T32768,
+    ~22 TFLOP of fp64 work, hours on a CPU) on query rows sampled to take about
+    half of budget_s, extrapolated by their visible-pair count; and the 512-token
+    sliding prefill in full, reported on its own."""
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    rng = np.random.default_rng(0)
-    parts, desc = [], []
-    share = budget_s / 4
+    per = {}
 
-    def sized(run, n_pilot, n_max):
-        t = run(n_pilot)[0]
-        n = int(min(n_max, max(n_pilot, n_pilot * share / max(t, 1e-3))))
-        return run(n)
-
-    # sliding prefill: random rows of each of the 4 sequences
-    d = ph["swa_prefill"]["host"]
-
-    def swa_rows(n):
-        rows = np.unique(np.concatenate([[0, 127, 128, 8191], rng.integers(0, 8192, n)]))
+    def timed(fn):
         t0 = time.perf_counter()
-        oracle.prefill_swa(d["q"], d["k"], d["v"], d["sinks"], window=128, base=1e4, rows=rows, n_threads=threads)
-        return time.perf_counter() - t0, rows
-    dt, rows = sized(swa_rows, 64, 8192)
-    sample_pairs = 4 * sum(min(int(r) + 1, 128) for r in rows)
-    parts.append((dt, FLOP_PER_PAIR_HEAD * 64 * sample_pairs, ph["swa_prefill"]["flops"]))
-    desc.append(f"sliding prefill {len(rows)} rows x 4 seqs")
-    # global prefill: rows spread over the sequence
+        fn()
+        return time.perf_counter() - t0
+
+    # config 1 (not part of the step), in full
+    d1 = gen.prefill_inputs(1, 512, 64, 8, seed=1000, with_sinks=True)
+    t1 = timed(lambda: oracle.prefill_swa(d1["q"], d1["k"], d1["v"], d1["sinks"], window=128, base=1e4,
+                                          n_threads=threads))
+    f1 = FLOP_PER_PAIR_HEAD * 64 * swa_pairs(512, 128)
+    per["swa_prefill_b1_t512"] = {"s": t1, "tflops": f1 / t1 / 1e12, "kind": "full"}
+    # sliding prefill, in full
+    d = ph["swa_prefill"]["host"]
+    t_swa = timed(lambda: oracle.prefill_swa(d["q"], d["k"], d["v"], d["sinks"], window=128, base=1e4,
+                                             n_threads=threads))
+    per["swa_prefill_b4_t8192"] = {"s": t_swa, "tflops": ph["swa_prefill"]["flops"] / t_swa / 1e12, "kind": "full"}
+    # mixed decode, every sequence
+    t_dec = 0.0
+    for name, window, base in (("swa", 128, 1e4), ("global", 0, 1e7)):
+        dd = ph["decode"][name]["host"]
+        t = timed(lambda: oracle.decode(dd["q"], dd["pos"], dd["k_cache"], dd["v_cache"], sinks=dd["sinks"],
+                                        window=window, base=base, n_threads=threads))
+        per[f"decode_{name}"] = {"s": t, "tflops": ph["decode"][name]["flops"] / t / 1e12, "kind": "full"}
+        t_dec += t
+    # global prefill: a pilot, then rows sized to about half the budget
     g = ph["global_prefill"]["host"]
+    rng = np.random.default_rng(0)
 
     def glob_rows(n):
         rows = np.unique(np.concatenate([[0, 32767], rng.integers(0, 32768, n)]))
-        t0 = time.perf_counter()
-        oracle.prefill_global(g["q"], g["k"], g["v"], base=1e7, rows=rows, n_threads=threads)
-        return time.perf_counter() - t0, rows
-    dt, rows = sized(glob_rows, 16, 32768)
-    parts.append((dt, FLOP_PER_PAIR_HEAD * 64 * int(sum(int(r) + 1 for r in rows)), ph["global_prefill"]["flops"]))
-    desc.append(f"global prefill {len(rows)} rows")
-    # decode: all 64 sliding sequences; global sequences until a quarter of the budget is spent
-    for name, window, base in (("swa", 128, 1e4), ("global", 0, 1e7)):
-        dd = ph["decode"][name]["host"]
-        seqs, dt = [], 0.0
-        for s in range(dd["q"].shape[0]):
-            if name == "global" and dt >= share:
-                break
-            t0 = time.perf_counter()
-            oracle.decode(dd["q"], dd["pos"], dd["k_cache"], dd["v_cache"], sinks=dd["sinks"], window=window,
-                          base=base, seqs=[s], n_threads=threads)
-            dt += time.perf_counter() - t0
-            seqs.append(s)
-        L = [min(int(dd["pos"][s]) + 1, window if window else int(dd["pos"][s]) + 1) for s in seqs]
-        parts.append((dt, FLOP_PER_PAIR_HEAD * 64 * sum(L), ph["decode"][name]["flops"]))
-        desc.append(f"{name} decode {len(seqs)} seqs")
-    total_sample_s = sum(p[0] for p in parts)
-    step_s = sum(dt * full / max(sf, 1) for dt, sf, full in parts)
-    step_flops = sum(full for _, _, full in parts)
+        return timed(lambda: oracle.prefill_global(g["q"], g["k"], g["v"], base=1e7, rows=rows,
+                                                   n_threads=threads)), rows
+    tp, _ = glob_rows(16)
+    dt, rows = glob_rows(int(min(32768, max(16, 16 * (budget_s / 2) / max(tp, 1e-3)))))
+    sample_flops = FLOP_PER_PAIR_HEAD * 64 * int(sum(int(r) + 1 for r in rows))
+    t_glob = dt * ph["global_prefill"]["flops"] / sample_flops
+    per["global_prefill_t32768"] = {"s": t_glob, "tflops": ph["global_prefill"]["flops"] / t_glob / 1e12,
+                                    "kind": f"extrapolated from {len(rows)} rows ({dt:.1f} s)"}
+    step_flops = ph["swa_prefill"]["flops"] + ph["global_prefill"]["flops"] + sum(
+        ph["decode"][n]["flops"] for n in ("swa", "global"))
+    step_s = t_swa + t_dec + t_glob
     return {"value": step_flops / step_s / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "; ".join(desc) + f" ({total_sample_s:.1f} s of fp64 oracle time, each phase "
-                                        f"extrapolated to the full step by its FLOP count)"}
+            "cpu_model": cpu_model(), "logical_cpus": os.cpu_count(),
+            "sample": f"sliding prefill B4xT8192 and mixed decode (64 + 16 sequences) in full; global prefill "
+                      f"T32768 on {len(rows)} sampled rows, extrapolated by visible pairs; "
+                      f"{t1 + t_swa + t_dec + dt:.1f} s of fp64 oracle time",
+            "step_s": step_s, "per_config": per}
 
 
 # ------------------------------------------------------------ main
@@ -263,6 +416,8 @@ def main():
     ap.add_argument("--workload", choices=["layer_step", "long_prefill", "serving_chunks", "spec_decode", "paged_decode",
                                             "backward"], default="layer_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the 524288-token prefill phase of the default run")
     ap.add_argument("--cpu-budget", type=float, default=40.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run three 1 GiB device-to-device copies (a known-size reference "
@@ -353,17 +508,33 @@ def main():
     phases["mixed_decode_step"] = {"ms": mixed_ms, "gbs": gbs(mixed_bytes, mixed_ms),
                                    "frac_hbm_peak": gbs(mixed_bytes, mixed_ms) / PEAK_HBM_GBS}
 
+    log("on-box peaks: bf16 MFMA loop, HBM copy and read")
+    peaks = measure_peaks(torch, Bd)
+    for p in phases.values():
+        if "tflops" in p:
+            p["frac_measured_mfma_randn"] = p["tflops"] / peaks["mfma_bf16_randn_tflops"]
+        if "gbs" in p:
+            p["frac_measured_hbm_copy"] = p["gbs"] / peaks["hbm_copy_gbs"]
+            p["frac_measured_hbm_read"] = p["gbs"] / peaks["hbm_read_gbs"]
+    log("sliding-window prefill B=1 T=512 (cache flushed between calls)")
+    phases["swa_prefill_b1_t512"] = bench_swa_small(torch, gen, Bd, peaks)
+    if not args.no_long:
+        log("long global prefill T=524288 in 8 chunks of 65536")
+        phases["global_prefill_t524288_8chunks"] = bench_long_prefill(torch, gen, Bd, peaks)
+
     achieved = tf(g["flops"], ms["global_prefill"])
     roofline = {"bound": "mfma", "kernel": "prefill_image_kernel (global causal, T=32768; its K/V image pass "
                                            "is inside the timed call)",
                 "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": profiled_traffic("global prefill T32768"),
+                "measured_peak": peaks["mfma_bf16_randn_tflops"],
+                "frac_measured_peak": achieved / peaks["mfma_bf16_randn_tflops"],
                 "algorithmic_flops": g["flops"], "algorithmic_bytes": g["bytes"]}
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("cpu baseline: timing the fp64 oracle on a sample")
-        cpu = cpu_baseline_layer_step(ph, args.cpu_budget)
+        log("cpu baseline: timing the fp64 oracle")
+        cpu = cpu_baseline_layer_step(ph, args.cpu_budget, gen)
 
     out = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
@@ -371,58 +542,22 @@ def main():
            "config": {"workload": "mimo_layer_step = swa_prefill_b4_t8192 + global_prefill_t32768 + "
                                   "mixed_decode_64swa_16global (append + decode)",
                       "step_gflop": step_flops / 1e9},
-           "roofline": roofline, "cpu_baseline": cpu, "phases": phases}
+           "roofline": roofline, "cpu_baseline": cpu, "peaks": peaks, "phases": phases}
     print(json.dumps(out))
 
 
 def main_long_prefill(args, torch, gen, Bd):
-    def dev_bf16(bits):
-        return _dev_bf16(torch, bits)
-
-    T, C = 524288, 65536
-    log("setup: long global prefill T=524288 (k/v full, q per chunk)")
-    kv = gen.global_prefill_chunk(T, 64, 4, seed=1004, t_lo=0, t_hi=T)
-    k, v = dev_bf16(kv["k"]), dev_bf16(kv["v"])
-    q = dev_bf16(kv["q"])
-    del kv
-    out = torch.empty((1, T, 64, 128), dtype=torch.bfloat16, device="cuda")
-    cfg = Bd.global_cfg()
-    n_chunks = T // C
-    ws = torch.empty(Bd.mimo_attn_prefill_workspace_size(cfg, 1, T), dtype=torch.uint8, device="cuda")
-
-    def step(ev=None):
-        for c in range(n_chunks):
-            if ev is not None:
-                ev[c][0].record()
-            Bd.mimo_attn_prefill_global(cfg, q[:, c * C:(c + 1) * C], k[:, :(c + 1) * C], v[:, :(c + 1) * C],
-                                        out[:, c * C:(c + 1) * C], q_pos0=c * C, ws=ws)
-            if ev is not None:
-                ev[c][1].record()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_chunks)]
-           for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-        log(f"step {i} enqueued")
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    flops = FLOP_PER_PAIR_HEAD * 64 * causal_pairs(0, T)
-    chunk_ms = [float(np.mean([e[c][0].elapsed_time(e[c][1]) for e in evs])) for c in range(n_chunks)]
-    value = flops / (ms_step * 1e-3) / 1e12
-    out_j = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-             "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+    log("on-box peaks")
+    peaks = measure_peaks(torch, Bd)
+    log("setup: long global prefill T=524288 (k/v whole, q chunk by chunk)")
+    r = bench_long_prefill(torch, gen, Bd, peaks, warmup=args.warmup, steps=args.steps)
+    flops = r["roofline"]["algorithmic_flops"]
+    out_j = {"metric": METRIC, "value": r["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+             "warmup": args.warmup, "ms_per_step": r["ms"], "higher_is_better": True, "scaling": "weak",
              "vs_baseline": None, "dtype": "bf16", "data": "synthetic: seeded N(0,1) bf16 q/k/v",
-             "config": {"workload": "global_prefill_t524288 in 8 query chunks of 65536 against the full prefix"},
-             "roofline": {"bound": "mfma", "kernel": "prefill_image_kernel (global causal chunks)", "achieved": value,
-                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": value / PEAK_BF16_TFLOPS,
-                          "traffic": None},
-             "cpu_baseline": None,
-             "chunks_ms": chunk_ms}
+             "config": {"workload": "global_prefill_t524288 in 8 query chunks of 65536 against the full prefix",
+                        "step_gflop": flops / 1e9},
+             "roofline": r["roofline"], "cpu_baseline": None, "peaks": peaks, "chunks_ms": r["chunks_ms"]}
     print(json.dumps(out_j))
 
 

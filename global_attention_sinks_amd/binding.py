@@ -330,3 +330,68 @@ def mimo_kv_ring_append(cfg: MimoAttnCfg, k_new, v_new, pos, k_cache, v_cache, s
            lib.mimo_kv_ring_append(ctypes.byref(cfg), S, _p(k_new), _p(v_new), _p(pos), _p(k_cache),
                                    _p(v_cache), cap, _stream(stream)))
     return k_cache, v_cache
+
+
+# ---------------------------------------------------------------- on-box peaks (libmimo_peaks.so)
+# Measurement only: the benchmark reports the attention kernels against what
+# these loops reach on the same card, next to the vendor peaks.
+
+PEAKS_PATH = os.path.join(_PKG, "libmimo_peaks.so")
+_peaks = None
+
+
+def load_peaks(path: str = PEAKS_PATH):
+    global _peaks
+    if _peaks is not None:
+        return _peaks
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with global_attention_sinks_amd.build.build()")
+    lib = ctypes.CDLL(path)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.mimo_peak_mfma_waves.argtypes = []
+    lib.mimo_peak_mfma_bf16.argtypes = [P, I64, I32, P, P]
+    lib.mimo_peak_copy.argtypes = [P, P, I64, P]
+    lib.mimo_peak_read.argtypes = [P, I64, P, P]
+    for fn in ("mimo_peak_mfma_waves", "mimo_peak_mfma_bf16", "mimo_peak_copy", "mimo_peak_read"):
+        getattr(lib, fn).restype = ctypes.c_int
+    _peaks = lib
+    return lib
+
+
+def _hip_ok(fn: str, err: int):
+    if err != 0:
+        raise RuntimeError(f"{fn}: hipError {err}")
+
+
+def peak_mfma_flops(iters: int) -> int:
+    """FLOP of one mimo_peak_mfma_bf16 launch."""
+    return int(load_peaks().mimo_peak_mfma_waves()) * iters * 64 * 32768
+
+
+def peak_mfma_bf16(operands, iters: int, sink, stream=None):
+    """operands: bf16 CUDA tensor (>= 64 values); sink: float32 CUDA tensor of
+    mimo_peak_mfma_waves() values."""
+    lib = load_peaks()
+    _need(operands, torch.bfloat16, "operands")
+    _need(sink, torch.float32, "sink")
+    if sink.numel() < lib.mimo_peak_mfma_waves() or operands.numel() < 64:
+        raise ValueError("sink needs mimo_peak_mfma_waves() floats and operands >= 64 values")
+    _hip_ok("mimo_peak_mfma_bf16", lib.mimo_peak_mfma_bf16(_p(operands), operands.numel(), iters, _p(sink),
+                                                           _stream(stream)))
+
+
+def peak_copy(src, dst, stream=None):
+    lib = load_peaks()
+    n = src.numel() * src.element_size()
+    if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()) or \
+            dst.numel() * dst.element_size() < n:
+        raise ValueError("src and dst must be contiguous CUDA tensors, dst at least as large")
+    _hip_ok("mimo_peak_copy", lib.mimo_peak_copy(_p(src), _p(dst), n, _stream(stream)))
+
+
+def peak_read(src, out, stream=None):
+    lib = load_peaks()
+    if not (src.is_cuda and src.is_contiguous() and out.is_cuda):
+        raise ValueError("src and out must be CUDA tensors")
+    _hip_ok("mimo_peak_read", lib.mimo_peak_read(_p(src), src.numel() * src.element_size(), _p(out),
+                                                 _stream(stream)))

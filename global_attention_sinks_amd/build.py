@@ -1,7 +1,9 @@
-"""Build libmimo_attn.so (gfx950) in-tree with hipcc.
+"""Build libmimo_attn.so (gfx950) in-tree with hipcc, and libmimo_peaks.so,
+the on-box peak loops the benchmark measures beside it.
 
 Each source compiles to its own object in parallel, then one shared library
-links them.  Packed FP32 instructions are disabled for all device code.
+per target links them.  Warnings are errors.  Packed FP32 instructions are
+disabled for all device code.
 """
 from __future__ import annotations
 
@@ -14,12 +16,14 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmimo_attn.so")
+PEAKS_LIB = os.path.join(PKG, "libmimo_peaks.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["rope.hip", "prefill.hip", "decode.hip", "backward.hip", "api.cpp"]
+PEAKS_SOURCES = ["peaks.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Werror",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # MFMA results in VGPRs.  In kernels past 256 registers (dK/dV, multi-query
     # decode) the default form left the allocator copying accumulators between
@@ -36,6 +40,13 @@ def _hipcc() -> str:
 
 
 def build(extra_flags=(), out: str = LIB, verbose: bool = False) -> str:
+    """Build the attention library (returned) and the peak-loop library."""
+    lib = _build_one(SOURCES, out, extra_flags, verbose)
+    _build_one(PEAKS_SOURCES, PEAKS_LIB, extra_flags, verbose)
+    return lib
+
+
+def _build_one(sources, out, extra_flags, verbose):
     os.makedirs(BUILD_DIR, exist_ok=True)
     hipcc = _hipcc()
 
@@ -49,8 +60,8 @@ def build(extra_flags=(), out: str = LIB, verbose: bool = False) -> str:
             sys.stderr.write(r.stderr)
         return obj
 
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
+    with ThreadPoolExecutor(len(sources)) as ex:
+        objs = list(ex.map(compile_one, sources))
     tmp = out + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

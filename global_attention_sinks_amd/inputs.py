@@ -261,17 +261,20 @@ def paged_decode_inputs(S: int, n_q: int, block_size: int, n_q_heads: int, n_kv_
             "sinks": normal_f32(cs, (n_q_heads,)) if with_sinks else None}
 
 
-def global_prefill_chunk(T: int, n_q_heads: int, n_kv_heads: int, seed: int, t_lo: int, t_hi: int) -> dict:
-    """Query rows [t_lo, t_hi) of a B=1 prefill of T tokens and the keys/values
-    0..t_hi-1, drawn exactly as prefill_inputs(1, T, ...) would draw them."""
+def global_prefill_chunk(T: int, n_q_heads: int, n_kv_heads: int, seed: int, t_lo: int, t_hi: int,
+                         kv: bool = True) -> dict:
+    """Query rows [t_lo, t_hi) of a B=1 prefill of T tokens and (kv=True) the
+    keys/values 0..t_hi-1, drawn exactly as prefill_inputs(1, T, ...) would draw them."""
     cq, ck, cv, _, _ = children(seed)
     row_q, row_k, row_v = n_q_heads * D_QK, n_kv_heads * D_QK, n_kv_heads * D_V
     q = normal_bf16_slice(cq, (1, T, n_q_heads, D_QK), t_lo * row_q, t_hi * row_q)
-    k = normal_bf16_slice(ck, (1, T, n_kv_heads, D_QK), 0, t_hi * row_k)
-    v = normal_bf16_slice(cv, (1, T, n_kv_heads, D_V), 0, t_hi * row_v)
-    return {"q": q.reshape(1, t_hi - t_lo, n_q_heads, D_QK),
-            "k": k.reshape(1, t_hi, n_kv_heads, D_QK),
-            "v": v.reshape(1, t_hi, n_kv_heads, D_V)}
+    out = {"q": q.reshape(1, t_hi - t_lo, n_q_heads, D_QK)}
+    if kv:
+        k = normal_bf16_slice(ck, (1, T, n_kv_heads, D_QK), 0, t_hi * row_k)
+        v = normal_bf16_slice(cv, (1, T, n_kv_heads, D_V), 0, t_hi * row_v)
+        out["k"] = k.reshape(1, t_hi, n_kv_heads, D_QK)
+        out["v"] = v.reshape(1, t_hi, n_kv_heads, D_V)
+    return out
 
 
 def varlen_inputs(lens_q, lens_k, n_q_heads: int, n_kv_heads: int, seed: int, with_sinks: bool,
