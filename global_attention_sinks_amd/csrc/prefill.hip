@@ -970,13 +970,19 @@ void prefill_band_kernel(PrefillArgs a) {
     const uint16_t *kbase = a.k + k_tok0 * krow_stride + (size_t)g * kDqk;
     const uint16_t *vbase = a.v + k_tok0 * vrow_stride + (size_t)g * kDv;
 
-    // ---- staging of a tile: threads < 256 rotate K piece (row tid>>3, pairs
+    // ---- staging of a tile: threads < 256 rotate K piece (row rrow, pairs
     // 4*(tid&7)..+3); every thread moves pass-through chunk 8 + (tid&15) of row
-    // tid>>4; threads >= 256 transpose V (key pair u%16, 8-dv chunk u/16, u = tid-256)
+    // tid>>4; threads >= 256 transpose V (key pair u%16, 8-dv chunk u/16, u = tid-256).
+    // LDS banks: the rows a half-wave's rotating pieces land in are 4 apart (starts
+    // 16 dwords apart for the 400-byte row stride), and lanes whose dv chunk has bit 1
+    // set hold their chunk's halves swapped and write its transposed rows in the
+    // order d ^ 4, so the four 16-lane groups of a transposed store hit disjoint banks.
     const bool rot_thr = tid < 256;
-    const int rrow = (tid & 255) >> 3, rq = tid & 7;
+    const int rgrp = (tid & 255) >> 3;
+    const int rrow = (rgrp & 16) | ((rgrp & 3) << 2) | ((rgrp >> 2) & 3), rq = tid & 7;
     const int prow_ = tid >> 4, pch = 8 + (tid & 15);
     const int vu = tid & 255, vkp = vu % 16, vcc = vu / 16;
+    const int vsw = (vcc & 2) ? 4 : 0;             // element offset of the half loaded first
     uint64_t my_turn[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) my_turn[e] = a.rt.turn[4 * rq + e];
@@ -996,8 +1002,13 @@ void prefill_band_kernel(PrefillArgs a) {
             R.ry = *reinterpret_cast<const u32x2 *>(src + 32);
         } else {
             const uint16_t *src = vt + 8 * vcc;
-            R.v[0] = ldg128(src + (size_t)min(2 * vkp, last) * vrow_stride);
-            R.v[1] = ldg128(src + (size_t)min(2 * vkp + 1, last) * vrow_stride);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const uint16_t *row = src + (size_t)min(2 * vkp + i, last) * vrow_stride;
+                const u32x2 h0 = *reinterpret_cast<const u32x2 *>(row + vsw);
+                const u32x2 h1 = *reinterpret_cast<const u32x2 *>(row + (4 - vsw));
+                R.v[i] = u32x4{h0[0], h0[1], h1[0], h1[1]};
+            }
         }
         R.pl = ldg128(kt + (size_t)min(prow_, last) * krow_stride + 8 * pch);
     };
@@ -1020,11 +1031,14 @@ void prefill_band_kernel(PrefillArgs a) {
             *reinterpret_cast<u32x2 *>(Ks + rrow * KSTR + 4 * rq) = x;
             *reinterpret_cast<u32x2 *>(Ks + rrow * KSTR + 4 * rq + 32) = y;
         } else {
+            // word d >> 1 of R.v holds dv 8 vcc + (d ^ vsw) and its neighbour
+            uint16_t *vlo = Vs + (8 * vcc + vsw) * VSTR + 2 * vkp;         // rows of d < 4
+            uint16_t *vhi = Vs + (8 * vcc + 4 - vsw) * VSTR + 2 * vkp;     // rows of d >= 4
 #pragma unroll
             for (int d = 0; d < 8; ++d) {
                 const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
                 const uint32_t wv = __builtin_amdgcn_perm(R.v[1][d >> 1], R.v[0][d >> 1], sel);
-                *reinterpret_cast<uint32_t *>(Vs + (8 * vcc + d) * VSTR + 2 * vkp) = wv;
+                *reinterpret_cast<uint32_t *>((d < 4 ? vlo : vhi) + (d & 3) * VSTR) = wv;
             }
         }
         *reinterpret_cast<u32x4 *>(Ks + prow_ * KSTR + 8 * pch) = R.pl;
