@@ -248,7 +248,23 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 #pragma unroll
         for (int s = 0; s < 8; ++s) DP = mfma32(lds128(Vs + prow * VSTR + 64 * h2 + 8 * s), lds128(dos + 8 * s), DP);
 
-        // element e: key j0 + 16*(e>>3) + 8*h2 + (e&7), query t
+        // element e: key j0 + 16*(e>>3) + 8*h2 + (e&7), query t.  A tile whose every
+        // key every query of the block sees needs no mask; otherwise, less j0 + 8 h2,
+        // the keys query t sees form a range [lo, hi] and key c is in it when
+        // c - lo <= hi - lo as unsigned (c a constant: no per-key registers).
+        // (Rows past T have L = +inf, so their p is 0 either way.)
+        const bool full = (j0 + 32 <= a.T) && (j0 + 31 <= q0) && (q0 + 31 - j0 < win);
+        int lo = 0;
+        uint32_t span = 0xffffffffu;
+        if (!full) {
+            const int hi = min(t, a.T - 1) - j0 - 8 * h2;
+            lo = (int)max((int64_t)t - j0 - 8 * h2 - win + 1, (int64_t)-64);   // keys before the tile: c >= 0 > lo
+            span = (uint32_t)(hi - lo);
+            if (hi < lo) {   // nothing visible
+                lo = 0x40000000;
+                span = 0;
+            }
+        }
         u32x4 dsb[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -256,9 +272,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 #pragma unroll
             for (int x = 0; x < 8; ++x) {
                 const int e = 8 * s + x;
-                const int j = j0 + 16 * s + 8 * h2 + x;
-                const bool vis = tval && j < a.T && j <= t && t - j < win;
-                const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], cl2, -L2)) : 0.0f;
+                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], cl2, -L2));
+                if (!full && (uint32_t)(16 * s + x - lo) > span) p = 0.0f;
                 v8[x] = p * (DP[e] * a.v_scale - Dq);
             }
 #pragma unroll
@@ -452,7 +467,22 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
             for (int s = 0; s < 8; ++s) DP = mfma32(lds128(Os + prow * VSTR + 64 * h2 + 8 * s), vf[s], DP);
 
-            // element e: query q0 + 16*(e>>3) + 8*h2 + (e&7), key j
+            // element e: query q0 + 16*(e>>3) + 8*h2 + (e&7), key j.  A stage whose
+            // every query sees every key of the wave needs no mask; otherwise, less
+            // q0 + 8 h2, the queries key j is seen by form a range [lo, hi] and query c
+            // is in it when c - lo <= hi - lo as unsigned.
+            const bool full = (jw0 + 32 <= a.T) && (q0 + 32 <= a.T) && (jw0 + 31 <= q0) && (q0 + 31 - jw0 < win);
+            int lo = 0;
+            uint32_t span = 0xffffffffu;
+            if (!full) {
+                lo = j - q0 - 8 * h2;
+                const int hi = (int)min((int64_t)j + win - 1, (int64_t)a.T - 1) - q0 - 8 * h2;
+                span = (uint32_t)(hi - lo);
+                if (!jval || hi < lo) {   // nothing visible
+                    lo = 0x40000000;
+                    span = 0;
+                }
+            }
             u32x4 pb[2], dsb[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
@@ -467,9 +497,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
                 for (int x = 0; x < 8; ++x) {
                     const int e = 8 * s + x;
-                    const int q = q0 + 16 * s + 8 * h2 + x;
-                    const bool vis = jval && q < a.T && j <= q && q - j < win;
-                    const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], cl2, -lrow[x])) : 0.0f;
+                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], cl2, -lrow[x]));
+                    if (!full && (uint32_t)(16 * s + x - lo) > span) p = 0.0f;
                     p8[x] = p;
                     d8[x] = p * (DP[e] * a.v_scale - drow[x]);
                 }
