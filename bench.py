@@ -81,7 +81,13 @@ def causal_pairs(q_lo: int, q_hi: int) -> int:
 
 
 def prefill_bytes(B, Tq, Tk, hq, hkv, sinks: bool) -> int:
-    return B * (Tq * hq * 192 * 2 + Tk * hkv * (192 + 128) * 2 + Tq * hq * 128 * 2) + (hq * 4 if sinks else 0)
+    return sum(prefill_rw(B, Tq, Tk, hq, hkv, sinks))
+
+
+def prefill_rw(B, Tq, Tk, hq, hkv, sinks: bool):
+    """Algorithmic (read, written) bytes of a prefill: q, k, v (and sinks) in, out out."""
+    return (B * (Tq * hq * 192 * 2 + Tk * hkv * (192 + 128) * 2) + (hq * 4 if sinks else 0),
+            B * Tq * hq * 128 * 2)
 
 
 # ------------------------------------------------------------ HBM traffic from the committed profile
@@ -247,8 +253,16 @@ def measure_peaks(torch, Bd):
     res["hbm_copy_gbs"] = 2 * n / (_event_ms(torch, lambda: Bd.peak_copy(src, dst), 10) * 1e-3) / 1e9
     Bd.peak_read(src, out)
     res["hbm_read_gbs"] = n / (_event_ms(torch, lambda: Bd.peak_read(src, out), 10) * 1e-3) / 1e9
+    Bd.peak_write(dst, 3)
+    res["hbm_write_gbs"] = n / (_event_ms(torch, lambda: Bd.peak_write(dst, 3), 10) * 1e-3) / 1e9
     del src, dst
     return res
+
+
+def mixed_ceiling_ms(peaks, read_bytes, write_bytes):
+    """Time the measured streams would need for a kernel's algorithmic reads and
+    writes: read bytes at the read rate plus written bytes at the write rate."""
+    return (read_bytes / peaks["hbm_read_gbs"] + write_bytes / peaks["hbm_write_gbs"]) / 1e6
 
 
 # ------------------------------------------------------------ the two workloads outside the step
@@ -277,7 +291,9 @@ def bench_swa_small(torch, gen, Bd, peaks, reps=10):
     ms = float(np.median([a.elapsed_time(b) for a, b in ts[2:]]))
     tfl, gbs = flops / (ms * 1e-3) / 1e12, nbytes / (ms * 1e-3) / 1e9
     return {"ms": ms, "tflops": tfl, "gbs": gbs, "frac_mfma_peak": tfl / PEAK_BF16_TFLOPS,
-            "frac_hbm_peak": gbs / PEAK_HBM_GBS, "frac_measured_hbm_copy": gbs / peaks["hbm_copy_gbs"],
+            "frac_hbm_peak": gbs / PEAK_HBM_GBS,
+            "frac_measured_hbm_mix": (mixed_ceiling_ms(peaks, *prefill_rw(1, 512, 512, 64, 8, True)) / ms
+                                      if peaks else None),
             "note": f"median of {reps} calls, Infinity Cache flushed before each; launch-latency bound "
                     f"({flops / 1e9:.2f} GFLOP, {nbytes / 1e6:.1f} MB)"}
 
@@ -330,7 +346,7 @@ def bench_long_prefill(torch, gen, Bd, peaks, warmup=1, steps=2):
             "roofline": {"bound": "mfma", "kernel": "prefill_image_kernel (8 global causal chunks; their K/V image "
                                                     "passes are inside the timed calls)",
                          "achieved": tfl, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tfl / PEAK_BF16_TFLOPS,
-                         "frac_measured_mfma_randn": tfl / peaks["mfma_bf16_randn_tflops"],
+                         "frac_measured_mfma_randn": tfl / peaks["mfma_bf16_randn_tflops"] if peaks else None,
                          "traffic": profiled_traffic("long prefill T524288 (8 chunks)"),
                          "algorithmic_flops": flops, "algorithmic_bytes": nbytes}}
 
@@ -416,6 +432,8 @@ def main():
     ap.add_argument("--workload", choices=["layer_step", "long_prefill", "serving_chunks", "spec_decode", "paged_decode",
                                             "backward"], default="layer_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the on-box peak loops (profiling passes); fractions of them are then omitted")
     ap.add_argument("--no-long", action="store_true",
                     help="skip the 524288-token prefill phase of the default run")
     ap.add_argument("--cpu-budget", type=float, default=40.0)
@@ -507,15 +525,29 @@ def main():
     mixed_bytes = ds["bytes"] + dg["bytes"] + ds["append_bytes"] + dg["append_bytes"]
     phases["mixed_decode_step"] = {"ms": mixed_ms, "gbs": gbs(mixed_bytes, mixed_ms),
                                    "frac_hbm_peak": gbs(mixed_bytes, mixed_ms) / PEAK_HBM_GBS}
+    # (read, written) algorithmic bytes of each phase, for the measured mixed-stream ceiling
+    def dec_rw(d, S):
+        w = S * 64 * 128 * 2
+        return d["bytes"] - w, w
+    def app_rw(d, S, hkv):
+        w = S * hkv * 320 * 2
+        return d["append_bytes"] - w, w
+    rw = {"swa_prefill_b4_t8192": prefill_rw(4, 8192, 8192, 64, 8, True),
+          "global_prefill_t32768": prefill_rw(1, 32768, 32768, 64, 4, False),
+          "decode_swa_64seqs": dec_rw(ds, 64), "decode_global_16seqs": dec_rw(dg, 16)}
+    rw["mixed_decode_step"] = tuple(a + b + c + e for a, b, c, e in zip(
+        rw["decode_swa_64seqs"], rw["decode_global_16seqs"], app_rw(ds, 64, 8), app_rw(dg, 16, 4)))
 
-    log("on-box peaks: bf16 MFMA loop, HBM copy and read")
-    peaks = measure_peaks(torch, Bd)
-    for p in phases.values():
+    peaks = None
+    if not args.no_peaks:
+        log("on-box peaks: bf16 MFMA loop, HBM copy and read")
+        peaks = measure_peaks(torch, Bd)
+    for name, p in (phases.items() if peaks else ()):
         if "tflops" in p:
             p["frac_measured_mfma_randn"] = p["tflops"] / peaks["mfma_bf16_randn_tflops"]
-        if "gbs" in p:
-            p["frac_measured_hbm_copy"] = p["gbs"] / peaks["hbm_copy_gbs"]
-            p["frac_measured_hbm_read"] = p["gbs"] / peaks["hbm_read_gbs"]
+        if name in rw:
+            # the time the measured read and write streams need for the phase's bytes, over its time
+            p["frac_measured_hbm_mix"] = mixed_ceiling_ms(peaks, *rw[name]) / p["ms"]
     log("sliding-window prefill B=1 T=512 (cache flushed between calls)")
     phases["swa_prefill_b1_t512"] = bench_swa_small(torch, gen, Bd, peaks)
     if not args.no_long:
@@ -527,8 +559,8 @@ def main():
                                            "is inside the timed call)",
                 "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": profiled_traffic("global prefill T32768"),
-                "measured_peak": peaks["mfma_bf16_randn_tflops"],
-                "frac_measured_peak": achieved / peaks["mfma_bf16_randn_tflops"],
+                "measured_peak": peaks["mfma_bf16_randn_tflops"] if peaks else None,
+                "frac_measured_peak": achieved / peaks["mfma_bf16_randn_tflops"] if peaks else None,
                 "algorithmic_flops": g["flops"], "algorithmic_bytes": g["bytes"]}
 
     cpu = None

@@ -352,7 +352,8 @@ def load_peaks(path: str = PEAKS_PATH):
     lib.mimo_peak_mfma_bf16.argtypes = [P, I64, I32, P, P]
     lib.mimo_peak_copy.argtypes = [P, P, I64, P]
     lib.mimo_peak_read.argtypes = [P, I64, P, P]
-    for fn in ("mimo_peak_mfma_waves", "mimo_peak_mfma_bf16", "mimo_peak_copy", "mimo_peak_read"):
+    lib.mimo_peak_write.argtypes = [P, I64, ctypes.c_uint32, P]
+    for fn in ("mimo_peak_mfma_waves", "mimo_peak_mfma_bf16", "mimo_peak_copy", "mimo_peak_read", "mimo_peak_write"):
         getattr(lib, fn).restype = ctypes.c_int
     _peaks = lib
     return lib
@@ -395,3 +396,11 @@ def peak_read(src, out, stream=None):
         raise ValueError("src and out must be CUDA tensors")
     _hip_ok("mimo_peak_read", lib.mimo_peak_read(_p(src), src.numel() * src.element_size(), _p(out),
                                                  _stream(stream)))
+
+
+def peak_write(dst, value: int = 0, stream=None):
+    lib = load_peaks()
+    if not (dst.is_cuda and dst.is_contiguous()):
+        raise ValueError("dst must be a contiguous CUDA tensor")
+    _hip_ok("mimo_peak_write", lib.mimo_peak_write(_p(dst), dst.numel() * dst.element_size(), value,
+                                                   _stream(stream)))

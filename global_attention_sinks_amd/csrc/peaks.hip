@@ -89,6 +89,17 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4 *__restrict__ src
     if (x == 0x9e3779b9u) out[0] = x;   // keeps the loads; practically never stores
 }
 
+__global__ __launch_bounds__(256) void write_kernel(u32x4 *__restrict__ dst, int64_t n, uint32_t value) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const u32x4 v = {value, value, value, value};
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) __builtin_nontemporal_store(v, dst + i + u * stride);
+    }
+    for (; i < n; i += stride) dst[i] = v;
+}
+
 }  // namespace
 
 extern "C" {
@@ -114,6 +125,13 @@ int mimo_peak_read(const void *src, int64_t bytes, uint32_t *out, void *stream) 
     if (!src || !out || bytes < 16 || bytes % 16) return (int)hipErrorInvalidValue;
     hipLaunchKernelGGL(read_kernel, dim3(256 * 16), dim3(256), 0, (hipStream_t)stream,
                        static_cast<const u32x4 *>(src), bytes / 16, out);
+    return (int)hipGetLastError();
+}
+
+int mimo_peak_write(void *dst, int64_t bytes, uint32_t value, void *stream) {
+    if (!dst || bytes < 16 || bytes % 16) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(write_kernel, dim3(256 * 16), dim3(256), 0, (hipStream_t)stream, static_cast<u32x4 *>(dst),
+                       bytes / 16, value);
     return (int)hipGetLastError();
 }
 

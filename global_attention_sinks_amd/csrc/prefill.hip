@@ -1295,8 +1295,12 @@ hipError_t launch_prefill(PrefillArgs a, hipStream_t stream) {
     // windows see a short band of keys: the band kernel (8 query heads per KV
     // head, window <= 128), else 4 heads x 32-key tiles, two workgroups per CU.
     // Global prefixes are long: 8 heads share each 64-key tile.
+    // The band kernel pays when its workgroups walk runs of blocks and fill the
+    // CUs; with fewer 32-query blocks (over sequences and KV heads) than CUs, the
+    // per-block kernel's two workgroups per KV head fill twice as many.
     const bool wide = (a.Hq / a.Hkv) % 8 == 0;
-    if (a.window > 0 && a.window <= kBandMaxWindow && a.Hq == 8 * a.Hkv)
+    const int64_t qblocks = (int64_t)a.B * a.Hkv * ((a.Tq + 31) / 32);
+    if (a.window > 0 && a.window <= kBandMaxWindow && a.Hq == 8 * a.Hkv && qblocks >= 256)
         return launch_band(a, stream);
     if (a.window == 0 && wide) return launch_variant<8, 64>(a, stream);
     return launch_variant<4, 32>(a, stream);

@@ -37,6 +37,9 @@ int mimo_peak_copy(const void *src, void *dst, int64_t bytes, void *stream);
 /* HBM read of `bytes` (a multiple of 16); out: one uint32, practically never written. */
 int mimo_peak_read(const void *src, int64_t bytes, uint32_t *out, void *stream);
 
+/* HBM write of `bytes` (a multiple of 16): dst filled with the 32-bit `value`. */
+int mimo_peak_write(void *dst, int64_t bytes, uint32_t value, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

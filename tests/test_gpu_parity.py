@@ -108,6 +108,14 @@ SWA_CASES = [
     (40, 96, 0, 128, True, (64, 8)),     # 320 (sequence, KV head) pairs: one run each, 3 blocks
     (1, 2000, 0, 128, True, (64, 8)),    # runs of 2 blocks, the last run 1 block
     (1, 500, 7, 64, True, (64, 8)),      # window 64, positions offset by 7
+    # With fewer 32-query blocks than CUs (B x KV heads x blocks < 256) the per-block
+    # kernel runs; the cases below have >= 256 and take the band kernel, so both
+    # kernels see far positions, window 1 and 64, no sink and single tokens.
+    (8, 130, 5000, 128, True, (64, 8)),
+    (8, 128, 0, 1, True, (64, 8)),
+    (8, 140, 7, 64, True, (64, 8)),
+    (8, 129, 3, 128, False, (64, 8)),
+    (32, 1, 0, 128, True, (64, 8)),
 ]
 
 
