@@ -87,3 +87,38 @@ def test_noalloc_decode_rejects_more_than_its_scratch():
     st = lib.mimo_attn_decode_noalloc(ctypes.byref(cfg), 752, fake, fake, fake, fake, 131072, None, fake, None)
     assert st == 3   # MIMO_ERR_WORKSPACE, before any launch
     assert b"scratch" in lib.mimo_last_error()
+
+
+def test_noalloc_decode_in_a_captured_graph():
+    """What the allocation-free call is for: captured into a HIP graph (after one
+    eager call, which also looks the scratch up on this device) and replayed three
+    times, with eager work and new positions between the replays; each replay
+    equals the eager call on the same inputs bit for bit."""
+    cfg = Bd.global_cfg()
+    S, cap = 8, 5000
+    rng = np.random.Generator(np.random.PCG64(7106))
+    pos0 = rng.integers(1, cap, size=S) - 1
+    d = _inputs(S, cap, 4, 0, 7107, np.full(S, cap - 1), False)   # every slot filled
+    q, kc, vc = dev_bf16(d["q"]), dev_bf16(d["k_cache"]), dev_bf16(d["v_cache"])
+    pos = dev(pos0.astype(np.int64))
+    out = torch.empty((S, 64, 128), dtype=torch.bfloat16, device="cuda")
+    eager = torch.empty_like(out)
+    Bd.mimo_attn_decode_noalloc(cfg, q, pos, kc, vc, None, out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            Bd.mimo_attn_decode_noalloc(cfg, q, pos, kc, vc, None, out)
+    torch.cuda.current_stream().wait_stream(s)
+    for r in range(3):
+        pos.copy_(torch.from_numpy(rng.integers(0, cap, size=S).astype(np.int64)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        Bd.mimo_attn_decode_noalloc(cfg, q, pos, kc, vc, None, eager)
+        torch.cuda.synchronize()
+        say(f"  graph replay {r}: max |replay - eager| "
+            f"{(out.float() - eager.float()).abs().max().item():.3e}")
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
