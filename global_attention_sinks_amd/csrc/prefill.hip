@@ -581,8 +581,8 @@ __global__ __launch_bounds__(256) void kv_image_kernel(PrefillArgs a) {
 
 // ---- Global prefill over the tile images: the math of prefill_kernel<8, 64>
 // (same workgroup shape, block mapping, MFMA layout and online softmax), with each
-// tile moved HBM -> LDS by the global_load_lds path: 43 copies of 1 KiB, 16 bytes
-// per lane, straight into LDS.  No staging registers, no RoPE or transpose VALU
+// tile moved HBM -> LDS by buffer loads that write LDS: 43 copies of 1 KiB, 16
+// bytes per lane, straight into LDS.  No staging registers, no RoPE or transpose VALU
 // work and no LDS stores remain in the loop.
 template <int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
@@ -597,7 +597,7 @@ void prefill_image_kernel(PrefillArgs a) {
     constexpr int K_OPS = K_TILE * 2 / 1024, V_OPS = V_TILE * 2 / 1024;   // 25 + 18 copies of 1 KiB
     constexpr int OPS = K_OPS + V_OPS;
     constexpr int OPW = (OPS + NW - 1) / NW;        // per wave
-    constexpr int RQ = 4, RV = 6;                   // K / V^T fragment reads in flight
+    constexpr int RQ = 6, RV = 8;                   // K / V^T fragment reads in flight
     static_assert(K_TILE * 2 % 1024 == 0 && V_TILE * 2 % 1024 == 0, "whole 1 KiB copies");
     static_assert(STAGE == kImgTile && VSTR == kImgVS, "prepared image = LDS stage");
 
@@ -686,17 +686,22 @@ void prefill_image_kernel(PrefillArgs a) {
 
     // ---- a tile's image is STAGE contiguous elements: OPS copies of 1 KiB, op i
     // landing at LDS byte 1024 * i of the stage; wave w issues ops w, w + NW, ...
+    // The copies are buffer loads (a resource spanning the one tile) rather than
+    // global ones: a global load into LDS counts as both a vector-memory and an LDS
+    // access, and while one is in flight every LDS wait is compiled as a full
+    // drain, which would leave the fragment reads below one batch deep.
     auto copy_tile = [&](int jt, int buf) {
         const size_t tile_id = (size_t)(tile_base + jt) * a.Hkv + g;
-        const char *src = reinterpret_cast<const char *>(a.kv_img + tile_id * STAGE) + lane * 16;
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.kv_img + tile_id * STAGE), 0, STAGE * 2,
+                                              0x00020000);
         uint16_t *dst = smem + buf * STAGE;
 #pragma unroll
         for (int m = 0; m < OPW; ++m) {
             const int op = w + NW * m;
             if (op < OPS)
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src + op * 1024),
-                                                 (__attribute__((address_space(3))) void *)(dst + op * 512),
-                                                 16, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)(dst + op * 512),
+                                                         16, lane * 16, op * 1024, 0, 0);
         }
     };
 
