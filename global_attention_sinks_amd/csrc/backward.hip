@@ -382,18 +382,23 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const int q_first = (qlo / 32) * 32;
     const int n_qb = (qhi - q_first) / 32 + 1;
     const int n_stage = G * n_qb;
-    // Staging of a stage (32 query rows of one head): thread u < 64 takes rows
-    // (2*(u%16), +1) x rotating chunks (u/16, u/16 + 4) of Q; every thread takes
-    // rows (2*(t%16), +1) x one pass-through Q chunk 8 + t/16 and x dO chunk t/16.
-    // Holding both rows of a pair, a thread writes its chunks row-major and, two
-    // rows per dword, transposed: no LDS-to-LDS transpose pass.
+    // Staging of a stage (32 query rows of one head).  Every thread takes the row
+    // pair (2 rp, 2 rp + 1), rp = tid % 16, and of Q's rotating dims the pairs
+    // (rd, rd + 1), rd = 8 (tid / 64) + 2 ((tid / 16) % 4), with their partners
+    // rd + 32, rd + 33 (four rotations per thread: the RoPE spread over every
+    // lane), one pass-through Q chunk 8 + tid / 16 and dO chunk tid / 16.  Holding
+    // both rows of a pair, a thread writes its pieces row-major and, two rows per
+    // dword, transposed: no LDS-to-LDS transpose pass.  L and D of row tid % 32
+    // are loaded and written by every lane that maps to that row (same value).
     struct DkStage {
-        u32x4 rq[2][2];   // [row of pair][chunk c, c + 4], threads < 64
-        u32x4 pq[2];      // [row of pair] pass-through Q chunk
-        u32x4 po[2];      // [row of pair] dO chunk
-        float lv, dv;     // L and D of query row tid (threads < 32)
+        uint32_t rx[2], ry[2];   // [row of pair] dims rd, rd + 1 / rd + 32, rd + 33
+        u32x4 pq[2];             // [row of pair] pass-through Q chunk
+        u32x4 po[2];             // [row of pair] dO chunk
+        float lv, dv;            // L and D of query row tid % 32
     };
     const int rp = tid & 15, rc = tid >> 4;
+    const int rd = 8 * (tid >> 6) + 2 * ((tid >> 4) & 3);
+    const uint64_t turn0 = a.rt.turn[rd], turn1 = a.rt.turn[rd + 1];
     auto load_stage = [&](DkStage &st, int s_) {
         s_ = min(s_, n_stage - 1);   // past the last stage: re-read it (unused)
         const int head = g * G + s_ / n_qb, q0 = q_first + 32 * (s_ % n_qb);
@@ -404,18 +409,17 @@ void bwd_dkdv_kernel(BwdArgs a) {
         for (int i = 0; i < 2; ++i) {
             // rows past the end re-read the last valid row: masked out of every product
             const int row = min(2 * rp + i, last);
-            if (tid < 64) {
-                st.rq[i][0] = ldg128(qb_ + row * qrs + 8 * rc);
-                st.rq[i][1] = ldg128(qb_ + row * qrs + 8 * rc + 32);
-            }
-            st.pq[i] = ldg128(qb_ + row * qrs + 8 * (8 + rc));
+            const uint16_t *qrow_ = qb_ + row * qrs;
+            st.rx[i] = *reinterpret_cast<const uint32_t *>(qrow_ + rd);
+            st.ry[i] = *reinterpret_cast<const uint32_t *>(qrow_ + rd + 32);
+            st.pq[i] = ldg128(qrow_ + 8 * (8 + rc));
             st.po[i] = ldg128(ob_ + row * ors + 8 * rc);
         }
-        if (tid < 32) {
-            const bool ok = tid <= last;
-            st.lv = ok ? a.lse[((size_t)b * a.Hq + head) * a.T + q0 + tid] * kLog2e : kPosInf;
-            st.dv = ok ? a.D[((size_t)b * a.T + q0 + tid) * a.Hq + head] : 0.0f;
-        }
+        const int lr = tid & 31, lrc = min(lr, last);   // loads unconditional, past-the-end rows replaced
+        const float lv = a.lse[((size_t)b * a.Hq + head) * a.T + q0 + lrc];
+        const float dv = a.D[((size_t)b * a.T + q0 + lrc) * a.Hq + head];
+        st.lv = lr <= last ? lv * kLog2e : kPosInf;
+        st.dv = lr <= last ? dv : 0.0f;
     };
     // chunk x0 (row 2*rp) and x1 (row 2*rp + 1) of 8 columns starting at col:
     // row-major into d (row stride sstr), transposed into dT (column-major pairs)
@@ -428,20 +432,30 @@ void bwd_dkdv_kernel(BwdArgs a) {
             *reinterpret_cast<uint32_t *>(dT + (col + dd) * TSTR + 2 * rp) = __builtin_amdgcn_perm(x1[dd >> 1], x0[dd >> 1], sel);
         }
     };
-    auto store_stage = [&](DkStage &st, int s_, int buf) {
+    auto store_stage = [&](const DkStage &st, int s_, int buf) {
         const int q0 = q_first + 32 * (s_ % n_qb);
-        if (tid < 64) {
+        uint32_t x[2], y[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) rope_rotate8(st.rq[i][0], st.rq[i][1], a.rt, 8 * rc, a.pos0 + q0 + 2 * rp + i);
-            put2(Qsb[buf], QTsb[buf], RSTR, 8 * rc, st.rq[0][0], st.rq[1][0]);
-            put2(Qsb[buf], QTsb[buf], RSTR, 8 * rc + 32, st.rq[0][1], st.rq[1][1]);
+        for (int i = 0; i < 2; ++i) {
+            const int64_t pos = a.pos0 + q0 + 2 * rp + i;
+            float s0, c0, s1, c1;
+            rope_sincos(turn0, pos, s0, c0);
+            rope_sincos(turn1, pos, s1, c1);
+            const float x0 = bf_lo(st.rx[i]), x1 = bf_hi(st.rx[i]);
+            const float y0 = bf_lo(st.ry[i]), y1 = bf_hi(st.ry[i]);
+            x[i] = pack_bf16(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
+            y[i] = pack_bf16(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
+            *reinterpret_cast<uint32_t *>(Qsb[buf] + (2 * rp + i) * RSTR + rd) = x[i];
+            *reinterpret_cast<uint32_t *>(Qsb[buf] + (2 * rp + i) * RSTR + rd + 32) = y[i];
         }
+        *reinterpret_cast<uint32_t *>(QTsb[buf] + rd * TSTR + 2 * rp) = __builtin_amdgcn_perm(x[1], x[0], 0x05040100u);
+        *reinterpret_cast<uint32_t *>(QTsb[buf] + (rd + 1) * TSTR + 2 * rp) = __builtin_amdgcn_perm(x[1], x[0], 0x07060302u);
+        *reinterpret_cast<uint32_t *>(QTsb[buf] + (rd + 32) * TSTR + 2 * rp) = __builtin_amdgcn_perm(y[1], y[0], 0x05040100u);
+        *reinterpret_cast<uint32_t *>(QTsb[buf] + (rd + 33) * TSTR + 2 * rp) = __builtin_amdgcn_perm(y[1], y[0], 0x07060302u);
         put2(Qsb[buf], QTsb[buf], RSTR, 8 * (8 + rc), st.pq[0], st.pq[1]);
         put2(Osb[buf], OTsb[buf], VSTR, 8 * rc, st.po[0], st.po[1]);
-        if (tid < 32) {
-            Lsb[buf][tid] = st.lv;
-            Dsb[buf][tid] = st.dv;
-        }
+        Lsb[buf][tid & 31] = st.lv;
+        Dsb[buf][tid & 31] = st.dv;
     };
     DkStage st;
     load_stage(st, 0);
@@ -462,10 +476,32 @@ void bwd_dkdv_kernel(BwdArgs a) {
                 S[e] = 0.0f;
                 DP[e] = 0.0f;
             }
+            {
+                // S (12 MFMAs) and dP (8) interleaved, RS fragment reads in flight
+                constexpr int RS = 4;
+                auto order = [](int i) { return i < 16 ? ((i & 1) ? 12 + (i >> 1) : (i >> 1)) : i - 8; };
+                auto faddr = [&](int i) {
+                    const int u = order(i);
+                    return u < 12 ? Qs + prow * RSTR + 96 * h2 + 8 * u : Os + prow * VSTR + 64 * h2 + 8 * (u - 12);
+                };
+                u32x4 fr[RS];
 #pragma unroll
-            for (int s = 0; s < 12; ++s) S = mfma32(lds128(Qs + prow * RSTR + 96 * h2 + 8 * s), kf[s], S);
+                for (int i = 0; i < RS; ++i) fr[i] = lds128(faddr(i));
 #pragma unroll
-            for (int s = 0; s < 8; ++s) DP = mfma32(lds128(Os + prow * VSTR + 64 * h2 + 8 * s), vf[s], DP);
+                for (int i = 0; i < 20; ++i) {
+                    const int u = order(i);
+                    if (u < 12) S = mfma32(fr[i % RS], kf[u], S);
+                    else DP = mfma32(fr[i % RS], vf[u - 12], DP);
+                    if (i + RS < 20) fr[i % RS] = lds128(faddr(i + RS));
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, RS, 0);
+#pragma unroll
+                for (int i = 0; i < 20 - RS; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, RS, 0);
+            }
 
             // element e: query q0 + 16*(e>>3) + 8*h2 + (e&7), key j.  A stage whose
             // every query sees every key of the wave needs no mask; otherwise, less
@@ -508,17 +544,32 @@ void bwd_dkdv_kernel(BwdArgs a) {
                     dsb[s][x] = pack_bf16(d8[2 * x], d8[2 * x + 1]);
                 }
             }
-            // dV^T (128 x 32 keys) += dO^T P;  dK~^T (192 x 32 keys) += Q~^T dS
+            // dV^T (128 x 32 keys) += dO^T P;  dK~^T (192 x 32 keys) += Q~^T dS: 20 MFMAs,
+            // each accumulator's two steps apart, RD fragment reads in flight
+            __builtin_amdgcn_sched_barrier(0);
+            {
+                constexpr int RD = 4;
+                auto faddr = [&](int i) {
+                    const int s = i < 8 ? i >> 2 : (i - 8) / 6, mb = i < 8 ? i & 3 : (i - 8) % 6;
+                    return (i < 8 ? OTs : QTs) + (32 * mb + l32) * TSTR + 16 * s + 8 * h2;
+                };
+                u32x4 fr[RD];
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
+                for (int i = 0; i < RD; ++i) fr[i] = lds128(faddr(i));
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    dV[mb] = mfma32(lds128(OTs + (32 * mb + l32) * TSTR + 16 * s + 8 * h2), pb[s], dV[mb]);
+                for (int i = 0; i < 20; ++i) {
+                    if (i < 8) dV[i & 3] = mfma32(fr[i % RD], pb[i >> 2], dV[i & 3]);
+                    else dK[(i - 8) % 6] = mfma32(fr[i % RD], dsb[(i - 8) / 6], dK[(i - 8) % 6]);
+                    if (i + RD < 20) fr[i % RD] = lds128(faddr(i + RD));
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, RD, 1);
 #pragma unroll
-            for (int mb = 0; mb < 6; ++mb)
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    dK[mb] = mfma32(lds128(QTs + (32 * mb + l32) * TSTR + 16 * s + 8 * h2), dsb[s], dK[mb]);
+                for (int i = 0; i < 20 - RD; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, RD, 1);
+            }
         }
         // the next stage goes to the other buffer, read last in the previous stage
         store_stage(st, s_ + 1 < n_stage ? s_ + 1 : s_, buf ^ 1);
