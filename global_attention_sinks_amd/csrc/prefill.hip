@@ -377,6 +377,17 @@ void prefill_kernel(PrefillArgs a) {
                 S[i % KB] = mfma32(kf[i % RING], qr[i / KB], S[i % KB]);
                 if (i + RING < 12 * KB) kf[i % RING] = lds128(kaddr(i + RING));
             }
+            // keep RING reads in flight (the 64-key shape has no registers to spare for
+            // it: pinned there, it spills)
+            if constexpr (NK == 32) {
+                __builtin_amdgcn_sched_group_barrier(0x100, RING, 0);   // LDS reads
+    #pragma unroll
+                for (int i = 0; i < 12 * KB - RING; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, RING, 0);
+            }
         }
 
         // ---- mask on edge tiles only (offsets are small there, so 32-bit)
@@ -451,6 +462,15 @@ void prefill_kernel(PrefillArgs a) {
             for (int i = 0; i < 8 * KB; ++i) {
                 O[i / (2 * KB)] = mfma32(vf[i % RING], P[(i / 2) % KB][i & 1], O[i / (2 * KB)]);
                 if (i + RING < 8 * KB) vf[i % RING] = lds128(vaddr(i + RING));
+            }
+            if constexpr (NK == 32) {
+                __builtin_amdgcn_sched_group_barrier(0x100, RING, 1);
+    #pragma unroll
+                for (int i = 0; i < 8 * KB - RING; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, RING, 1);
             }
         }
 
