@@ -16,16 +16,16 @@
 //                      dQ~^T = K~^T dS^T in registers
 //   bwd_sink_kernel    one workgroup per head sums the sink partials (fixed order)
 //   bwd_dkdv_kernel    key-major: a workgroup owns 128 keys of one KV head (one
-//                      wave per 32 keys, the keys' K~ and V held in registers);
-//                      it walks every query head of the group and every 32-query
-//                      block that sees its keys (Q~, Q~^T, dO, dO^T staged in
-//                      LDS, double-buffered) and accumulates dK~^T = Q~^T dS
-//                      and dV^T = dO^T P
-// Both contractions reuse the forward's layout trick: the A-operand rows of the
-// first product are read with bits 2 and 3 of the row index swapped, so each
-// lane's accumulators are directly the B operand of the second product.  The
-// dk/dv stages are written transposed straight from registers: a staging
-// thread holds both rows of a row pair and stores each column pair as a dword.
+//                      wave per 16 keys, two waves per SIMD, 16x16x32 MFMAs, the
+//                      keys' K~ and V held in registers); it walks every query
+//                      head of the group and every 32-query block that sees its
+//                      keys (Q~, Q~^T, dO, dO^T staged in LDS, double-buffered)
+//                      and accumulates dK~^T = Q~^T dS and dV^T = dO^T P
+// Both kernels reuse the forward's layout trick: the A-operand rows of the first
+// product are read in a permuted order, so each lane's accumulators are directly
+// the B operand of the second product.  The dk/dv stages are written transposed
+// straight from registers: a staging thread holds both rows of a row pair and
+// stores each column pair as a dword.
 // Nothing is accumulated across workgroups, so the results are deterministic.
 #include "kernels.hpp"
 
@@ -41,6 +41,10 @@ constexpr int TSTR = 32 + 8;     // LDS row stride of a transposed 32-column til
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
 __device__ __forceinline__ u32x4 lds128(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
@@ -314,9 +318,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
         }
 }
 
-// ---- dk, dv: 128 keys of one KV head per workgroup (one wave per 32 keys)
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+// ---- dk, dv: 128 keys of one KV head per workgroup, one wave per 16 keys (two
+// waves per SIMD), 16x16x32 MFMAs.  Lane (g4 = lane / 16, l16 = lane % 16) holds,
+// for key kw0 + l16 of its wave, dims 32 c + 8 g4 .. + 7 of K~ and V (B operands of
+// S = Q~ K~^T and dP = dO V^T).  The A operands of S and dP are Q~ / dO rows read
+// in the order pi: in query block qb of the stage's 32 queries, MFMA row 4 u + i
+// is query 8 u + 4 qb + i, so that a lane's accumulators of the two blocks hold
+// queries 8 g4 .. 8 g4 + 7 of its key: exactly the B operand (8 consecutive
+// queries) of dV^T = dO^T P and dK~^T = Q~^T dS.
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdArgs a) {
+    constexpr int KPW = 16;   // keys per wave (8 waves)
     // two stage buffers: one is computed on while the next is written
     __shared__ __attribute__((aligned(16))) uint16_t Qsb[2][32 * RSTR];
     __shared__ __attribute__((aligned(16))) uint16_t QTsb[2][kDqk * TSTR];
@@ -325,101 +337,91 @@ void bwd_dkdv_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) float Lsb[2][32], Dsb[2][32];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int h2 = lane >> 5, l32 = lane & 31;
+    const int g4 = lane >> 4, l16 = lane & 15;
     const int per_b = a.Hkv * a.n_kblk;
     const int b = blockIdx.x / per_b;
     const int r = blockIdx.x - b * per_b;
     const int g = r % a.Hkv;
     const int kb = a.n_kblk - 1 - r / a.Hkv;          // later keys see fewer queries under a causal mask
     const int jb0 = kb * 128;
-    const int jw0 = jb0 + 32 * w;                      // this wave's keys
-    const int j = jw0 + l32;
+    const int kw0 = jb0 + KPW * w;                     // this wave's keys
+    const int j = kw0 + l16;
     const bool jval = j < a.T;
     const int G = a.Hq / a.Hkv;
     const size_t qrs = (size_t)a.Hq * kDqk, ors = (size_t)a.Hq * kDv;
 
-    // per lane: K~ (B operand of S = Q~ K~^T), V (B operand of dP = dO V^T) of key j
-    const size_t krow = ((size_t)b * a.T + j) * a.Hkv + g;
-    u32x4 kf[12], vf[8];
-    if (jval) {
-        const uint16_t *src = a.k + krow * kDqk + 96 * h2;
+    const size_t krow = ((size_t)b * a.T + (jval ? j : a.T - 1)) * a.Hkv + g;
+    u32x4 kf[6], vf[4];
+    {
+        const uint16_t *src = a.k + krow * kDqk + 8 * g4;
 #pragma unroll
-        for (int s = 0; s < 12; ++s) kf[s] = ldg128(src + 8 * s);
-        if (h2 == 0) {
+        for (int c = 0; c < 6; ++c) kf[c] = ldg128(src + 32 * c);
+        rope_rotate8(kf[0], kf[1], a.rt, 8 * g4, a.pos0 + (jval ? j : a.T - 1));
+        const uint16_t *vs = a.v + krow * kDv + 8 * g4;
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) rope_rotate8(kf[cc], kf[cc + 4], a.rt, 8 * cc, a.pos0 + j);
-        }
-        const uint16_t *vs = a.v + krow * kDv + 64 * h2;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) vf[s] = ldg128(vs + 8 * s);
-    } else {
-#pragma unroll
-        for (int s = 0; s < 12; ++s) kf[s] = u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int s = 0; s < 8; ++s) vf[s] = u32x4{0, 0, 0, 0};
+        for (int c = 0; c < 4; ++c) vf[c] = ldg128(vs + 32 * c);
     }
 
-    f32x16 dK[6], dV[4];
+    f32x4 dK[12], dV[8];
 #pragma unroll
-    for (int mb = 0; mb < 6; ++mb)
+    for (int mb = 0; mb < 12; ++mb) dK[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 16; ++e) dK[mb][e] = 0.0f;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) dV[mb][e] = 0.0f;
+    for (int mb = 0; mb < 8; ++mb) dV[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int prow = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
     const float cl2 = a.scale_log2;
     const int win = a.window > 0 ? a.window : 0x7fffffff;
     // queries that see some key of the workgroup, and of this wave
     const int qlo = jb0;
     const int qhi = a.window > 0 ? min(a.T - 1, jb0 + 127 + a.window - 1) : a.T - 1;
-    const int wq_hi = a.window > 0 ? jw0 + 31 + a.window - 1 : 0x7fffffff;
+    const int wq_hi = a.window > 0 ? kw0 + KPW - 1 + a.window - 1 : 0x7fffffff;
+    // query row of MFMA row l16 in query block qb (the order pi above)
+    const int prow0 = 8 * (l16 >> 2) + (l16 & 3);
 
     // stages (query head, 32-query block), head-major; the next stage's rows are
     // loaded into registers while this one is computed
     const int q_first = (qlo / 32) * 32;
     const int n_qb = (qhi - q_first) / 32 + 1;
     const int n_stage = G * n_qb;
-    // Staging of a stage (32 query rows of one head).  Every thread takes the row
-    // pair (2 rp, 2 rp + 1), rp = tid % 16, and of Q's rotating dims the pairs
-    // (rd, rd + 1), rd = 8 (tid / 64) + 2 ((tid / 16) % 4), with their partners
-    // rd + 32, rd + 33 (four rotations per thread: the RoPE spread over every
-    // lane), one pass-through Q chunk 8 + tid / 16 and dO chunk tid / 16.  Holding
-    // both rows of a pair, a thread writes its pieces row-major and, two rows per
-    // dword, transposed: no LDS-to-LDS transpose pass.  L and D of row tid % 32
-    // are loaded and written by every lane that maps to that row (same value).
-    struct DkStage {
-        uint32_t rx[2], ry[2];   // [row of pair] dims rd, rd + 1 / rd + 32, rd + 33
-        u32x4 pq[2];             // [row of pair] pass-through Q chunk
-        u32x4 po[2];             // [row of pair] dO chunk
-        float lv, dv;            // L and D of query row tid % 32
-    };
-    const int rp = tid & 15, rc = tid >> 4;
-    const int rd = 8 * (tid >> 6) + 2 * ((tid >> 4) & 3);
+    // Staging of a stage (32 query rows of one head): threads < 256 take the row
+    // pair (2 rp, 2 rp + 1), rp = t % 16, the rotating pairs (rd, rd + 1) with
+    // rd = 8 (t / 64) + 2 ((t / 16) % 4) and their partners rd + 32, rd + 33 (four
+    // rotations each), and Q pass-through chunk 8 + t / 16; threads >= 256 take the
+    // row pair's dO chunk t / 16 (t = tid - 256) and the rows' L and D.  Waves w
+    // and w + 4 share a SIMD, so every SIMD stages as much.  Holding both rows of a
+    // pair, a thread writes its pieces row-major and, two rows per dword, transposed.
+    const bool qthr = tid < 256;
+    const int t8 = tid & 255, rp = t8 & 15, rc = t8 >> 4;
+    const int rd = 8 * (t8 >> 6) + 2 * ((t8 >> 4) & 3);
     const uint64_t turn0 = a.rt.turn[rd], turn1 = a.rt.turn[rd + 1];
+    struct DkStage {
+        uint32_t rx[2], ry[2];   // [row of pair] dims rd, rd + 1 / rd + 32, rd + 33 (Q threads)
+        u32x4 ch[2];             // [row of pair] Q pass-through chunk (Q threads) or dO chunk
+        float lv, dv;            // L and D of query row t8 % 32 (dO threads)
+    };
     auto load_stage = [&](DkStage &st, int s_) {
         s_ = min(s_, n_stage - 1);   // past the last stage: re-read it (unused)
         const int head = g * G + s_ / n_qb, q0 = q_first + 32 * (s_ % n_qb);
         const int last = min(32, a.T - q0) - 1;
-        const uint16_t *qb_ = a.q + ((size_t)b * a.T + q0) * qrs + (size_t)head * kDqk;
-        const uint16_t *ob_ = a.dout + ((size_t)b * a.T + q0) * ors + (size_t)head * kDv;
+        if (qthr) {
+            const uint16_t *qb_ = a.q + ((size_t)b * a.T + q0) * qrs + (size_t)head * kDqk;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            // rows past the end re-read the last valid row: masked out of every product
-            const int row = min(2 * rp + i, last);
-            const uint16_t *qrow_ = qb_ + row * qrs;
-            st.rx[i] = *reinterpret_cast<const uint32_t *>(qrow_ + rd);
-            st.ry[i] = *reinterpret_cast<const uint32_t *>(qrow_ + rd + 32);
-            st.pq[i] = ldg128(qrow_ + 8 * (8 + rc));
-            st.po[i] = ldg128(ob_ + row * ors + 8 * rc);
+            for (int i = 0; i < 2; ++i) {
+                // rows past the end re-read the last valid row: masked out of every product
+                const uint16_t *qrow_ = qb_ + min(2 * rp + i, last) * qrs;
+                st.rx[i] = *reinterpret_cast<const uint32_t *>(qrow_ + rd);
+                st.ry[i] = *reinterpret_cast<const uint32_t *>(qrow_ + rd + 32);
+                st.ch[i] = ldg128(qrow_ + 8 * (8 + rc));
+            }
+        } else {
+            const uint16_t *ob_ = a.dout + ((size_t)b * a.T + q0) * ors + (size_t)head * kDv;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) st.ch[i] = ldg128(ob_ + min(2 * rp + i, last) * ors + 8 * rc);
+            const int lr = t8 & 31, lrc = min(lr, last);
+            const float lv = a.lse[((size_t)b * a.Hq + head) * a.T + q0 + lrc];
+            const float dv = a.D[((size_t)b * a.T + q0 + lrc) * a.Hq + head];
+            st.lv = lr <= last ? lv * kLog2e : kPosInf;
+            st.dv = lr <= last ? dv : 0.0f;
         }
-        const int lr = tid & 31, lrc = min(lr, last);   // loads unconditional, past-the-end rows replaced
-        const float lv = a.lse[((size_t)b * a.Hq + head) * a.T + q0 + lrc];
-        const float dv = a.D[((size_t)b * a.T + q0 + lrc) * a.Hq + head];
-        st.lv = lr <= last ? lv * kLog2e : kPosInf;
-        st.dv = lr <= last ? dv : 0.0f;
     };
     // chunk x0 (row 2*rp) and x1 (row 2*rp + 1) of 8 columns starting at col:
     // row-major into d (row stride sstr), transposed into dT (column-major pairs)
@@ -434,28 +436,31 @@ void bwd_dkdv_kernel(BwdArgs a) {
     };
     auto store_stage = [&](const DkStage &st, int s_, int buf) {
         const int q0 = q_first + 32 * (s_ % n_qb);
-        uint32_t x[2], y[2];
+        if (qthr) {
+            uint32_t x[2], y[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int64_t pos = a.pos0 + q0 + 2 * rp + i;
-            float s0, c0, s1, c1;
-            rope_sincos(turn0, pos, s0, c0);
-            rope_sincos(turn1, pos, s1, c1);
-            const float x0 = bf_lo(st.rx[i]), x1 = bf_hi(st.rx[i]);
-            const float y0 = bf_lo(st.ry[i]), y1 = bf_hi(st.ry[i]);
-            x[i] = pack_bf16(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
-            y[i] = pack_bf16(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
-            *reinterpret_cast<uint32_t *>(Qsb[buf] + (2 * rp + i) * RSTR + rd) = x[i];
-            *reinterpret_cast<uint32_t *>(Qsb[buf] + (2 * rp + i) * RSTR + rd + 32) = y[i];
+            for (int i = 0; i < 2; ++i) {
+                const int64_t pos = a.pos0 + q0 + 2 * rp + i;
+                float s0, c0, s1, c1;
+                rope_sincos(turn0, pos, s0, c0);
+                rope_sincos(turn1, pos, s1, c1);
+                const float x0 = bf_lo(st.rx[i]), x1 = bf_hi(st.rx[i]);
+                const float y0 = bf_lo(st.ry[i]), y1 = bf_hi(st.ry[i]);
+                x[i] = pack_bf16(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
+                y[i] = pack_bf16(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
+                *reinterpret_cast<uint32_t *>(Qsb[buf] + (2 * rp + i) * RSTR + rd) = x[i];
+                *reinterpret_cast<uint32_t *>(Qsb[buf] + (2 * rp + i) * RSTR + rd + 32) = y[i];
+            }
+            *reinterpret_cast<uint32_t *>(QTsb[buf] + rd * TSTR + 2 * rp) = __builtin_amdgcn_perm(x[1], x[0], 0x05040100u);
+            *reinterpret_cast<uint32_t *>(QTsb[buf] + (rd + 1) * TSTR + 2 * rp) = __builtin_amdgcn_perm(x[1], x[0], 0x07060302u);
+            *reinterpret_cast<uint32_t *>(QTsb[buf] + (rd + 32) * TSTR + 2 * rp) = __builtin_amdgcn_perm(y[1], y[0], 0x05040100u);
+            *reinterpret_cast<uint32_t *>(QTsb[buf] + (rd + 33) * TSTR + 2 * rp) = __builtin_amdgcn_perm(y[1], y[0], 0x07060302u);
+            put2(Qsb[buf], QTsb[buf], RSTR, 8 * (8 + rc), st.ch[0], st.ch[1]);
+        } else {
+            put2(Osb[buf], OTsb[buf], VSTR, 8 * rc, st.ch[0], st.ch[1]);
+            Lsb[buf][t8 & 31] = st.lv;
+            Dsb[buf][t8 & 31] = st.dv;
         }
-        *reinterpret_cast<uint32_t *>(QTsb[buf] + rd * TSTR + 2 * rp) = __builtin_amdgcn_perm(x[1], x[0], 0x05040100u);
-        *reinterpret_cast<uint32_t *>(QTsb[buf] + (rd + 1) * TSTR + 2 * rp) = __builtin_amdgcn_perm(x[1], x[0], 0x07060302u);
-        *reinterpret_cast<uint32_t *>(QTsb[buf] + (rd + 32) * TSTR + 2 * rp) = __builtin_amdgcn_perm(y[1], y[0], 0x05040100u);
-        *reinterpret_cast<uint32_t *>(QTsb[buf] + (rd + 33) * TSTR + 2 * rp) = __builtin_amdgcn_perm(y[1], y[0], 0x07060302u);
-        put2(Qsb[buf], QTsb[buf], RSTR, 8 * (8 + rc), st.pq[0], st.pq[1]);
-        put2(Osb[buf], OTsb[buf], VSTR, 8 * rc, st.po[0], st.po[1]);
-        Lsb[buf][tid & 31] = st.lv;
-        Dsb[buf][tid & 31] = st.dv;
     };
     DkStage st;
     load_stage(st, 0);
@@ -468,31 +473,33 @@ void bwd_dkdv_kernel(BwdArgs a) {
         const uint16_t *Qs = Qsb[buf], *QTs = QTsb[buf], *Os = Osb[buf], *OTs = OTsb[buf];
         const float *Ls = Lsb[buf], *Ds = Dsb[buf];
         // does this wave's key range meet the block's queries? (wave-uniform)
-        if (!(jw0 > q0 + 31 || q0 > wq_hi)) {
-
-            f32x16 S, DP;
+        if (!(kw0 > q0 + 31 || q0 > wq_hi)) {
+            f32x4 S[2], DP[2];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                S[e] = 0.0f;
-                DP[e] = 0.0f;
+            for (int qb = 0; qb < 2; ++qb) {
+                S[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                DP[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
             {
-                // S (12 MFMAs) and dP (8) interleaved, RS fragment reads in flight
-                constexpr int RS = 4;
-                auto order = [](int i) { return i < 16 ? ((i & 1) ? 12 + (i >> 1) : (i >> 1)) : i - 8; };
-                auto faddr = [&](int i) {
-                    const int u = order(i);
-                    return u < 12 ? Qs + prow * RSTR + 96 * h2 + 8 * u : Os + prow * VSTR + 64 * h2 + 8 * (u - 12);
+                // S (2 query blocks x 6 chunks) and dP (2 x 4) interleaved, RS fragment
+                // reads in flight
+                constexpr int RS = 8;
+                auto faddr = [&](int i) {   // i < 12: S (qb, c); else dP
+                    const int u = i < 12 ? i : i - 12;
+                    const int qb = i < 12 ? u / 6 : u / 4, c = i < 12 ? u % 6 : u % 4;
+                    const int row = prow0 + 4 * qb;
+                    return i < 12 ? Qs + row * RSTR + 32 * c + 8 * g4 : Os + row * VSTR + 32 * c + 8 * g4;
                 };
+                auto order = [](int i) { return i < 16 ? ((i & 1) ? 12 + (i >> 1) : (i >> 1)) : i - 8; };
                 u32x4 fr[RS];
 #pragma unroll
-                for (int i = 0; i < RS; ++i) fr[i] = lds128(faddr(i));
+                for (int i = 0; i < RS; ++i) fr[i] = lds128(faddr(order(i)));
 #pragma unroll
                 for (int i = 0; i < 20; ++i) {
                     const int u = order(i);
-                    if (u < 12) S = mfma32(fr[i % RS], kf[u], S);
-                    else DP = mfma32(fr[i % RS], vf[u - 12], DP);
-                    if (i + RS < 20) fr[i % RS] = lds128(faddr(i + RS));
+                    if (u < 12) S[u / 6] = mfma16(fr[i % RS], kf[u % 6], S[u / 6]);
+                    else DP[(u - 12) / 4] = mfma16(fr[i % RS], vf[(u - 12) % 4], DP[(u - 12) / 4]);
+                    if (i + RS < 20) fr[i % RS] = lds128(faddr(order(i + RS)));
                 }
                 __builtin_amdgcn_sched_group_barrier(0x100, RS, 0);
 #pragma unroll
@@ -503,63 +510,61 @@ void bwd_dkdv_kernel(BwdArgs a) {
                 __builtin_amdgcn_sched_group_barrier(0x008, RS, 0);
             }
 
-            // element e: query q0 + 16*(e>>3) + 8*h2 + (e&7), key j.  A stage whose
+            // element i of block qb: query q0 + 8 g4 + 4 qb + i, key j.  A stage whose
             // every query sees every key of the wave needs no mask; otherwise, less
-            // q0 + 8 h2, the queries key j is seen by form a range [lo, hi] and query c
+            // q0 + 8 g4, the queries key j is seen by form a range [lo, hi] and query c
             // is in it when c - lo <= hi - lo as unsigned.
-            const bool full = (jw0 + 32 <= a.T) && (q0 + 32 <= a.T) && (jw0 + 31 <= q0) && (q0 + 31 - jw0 < win);
+            const bool full = (kw0 + KPW <= a.T) && (q0 + 32 <= a.T) && (kw0 + KPW - 1 <= q0) && (q0 + 31 - kw0 < win);
             int lo = 0;
             uint32_t span = 0xffffffffu;
             if (!full) {
-                lo = j - q0 - 8 * h2;
-                const int hi = (int)min((int64_t)j + win - 1, (int64_t)a.T - 1) - q0 - 8 * h2;
+                lo = j - q0 - 8 * g4;
+                const int hi = (int)min((int64_t)j + win - 1, (int64_t)a.T - 1) - q0 - 8 * g4;
                 span = (uint32_t)(hi - lo);
                 if (!jval || hi < lo) {   // nothing visible
                     lo = 0x40000000;
                     span = 0;
                 }
             }
-            u32x4 pb[2], dsb[2];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                float p8[8], d8[8];
+            u32x4 pb, dsb;
+            {
                 // the lane's 8 query rows are consecutive: their L and D in two 16-byte reads each
-                const float4 l0 = *reinterpret_cast<const float4 *>(Ls + 16 * s + 8 * h2);
-                const float4 l1 = *reinterpret_cast<const float4 *>(Ls + 16 * s + 8 * h2 + 4);
-                const float4 d0 = *reinterpret_cast<const float4 *>(Ds + 16 * s + 8 * h2);
-                const float4 d1 = *reinterpret_cast<const float4 *>(Ds + 16 * s + 8 * h2 + 4);
+                const float4 l0 = *reinterpret_cast<const float4 *>(Ls + 8 * g4);
+                const float4 l1 = *reinterpret_cast<const float4 *>(Ls + 8 * g4 + 4);
+                const float4 d0 = *reinterpret_cast<const float4 *>(Ds + 8 * g4);
+                const float4 d1 = *reinterpret_cast<const float4 *>(Ds + 8 * g4 + 4);
                 const float lrow[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
                 const float drow[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+                float p8[8], d8[8];
 #pragma unroll
                 for (int x = 0; x < 8; ++x) {
-                    const int e = 8 * s + x;
-                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], cl2, -lrow[x]));
-                    if (!full && (uint32_t)(16 * s + x - lo) > span) p = 0.0f;
+                    const float sx = S[x >> 2][x & 3], dpx = DP[x >> 2][x & 3];
+                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sx, cl2, -lrow[x]));
+                    if (!full && (uint32_t)(x - lo) > span) p = 0.0f;
                     p8[x] = p;
-                    d8[x] = p * (DP[e] * a.v_scale - drow[x]);
+                    d8[x] = p * (dpx * a.v_scale - drow[x]);
                 }
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
-                    pb[s][x] = pack_bf16(p8[2 * x], p8[2 * x + 1]);
-                    dsb[s][x] = pack_bf16(d8[2 * x], d8[2 * x + 1]);
+                    pb[x] = pack_bf16(p8[2 * x], p8[2 * x + 1]);
+                    dsb[x] = pack_bf16(d8[2 * x], d8[2 * x + 1]);
                 }
             }
-            // dV^T (128 x 32 keys) += dO^T P;  dK~^T (192 x 32 keys) += Q~^T dS: 20 MFMAs,
-            // each accumulator's two steps apart, RD fragment reads in flight
+            // dV^T (128 x 16 keys) += dO^T P;  dK~^T (192 x 16 keys) += Q~^T dS: 20
+            // MFMAs, RD fragment reads in flight
             __builtin_amdgcn_sched_barrier(0);
             {
-                constexpr int RD = 4;
-                auto faddr = [&](int i) {
-                    const int s = i < 8 ? i >> 2 : (i - 8) / 6, mb = i < 8 ? i & 3 : (i - 8) % 6;
-                    return (i < 8 ? OTs : QTs) + (32 * mb + l32) * TSTR + 16 * s + 8 * h2;
+                constexpr int RD = 8;
+                auto faddr = [&](int i) {   // i < 8: dV block i; else dK block i - 8
+                    return (i < 8 ? OTs + (16 * i + l16) * TSTR : QTs + (16 * (i - 8) + l16) * TSTR) + 8 * g4;
                 };
                 u32x4 fr[RD];
 #pragma unroll
                 for (int i = 0; i < RD; ++i) fr[i] = lds128(faddr(i));
 #pragma unroll
                 for (int i = 0; i < 20; ++i) {
-                    if (i < 8) dV[i & 3] = mfma32(fr[i % RD], pb[i >> 2], dV[i & 3]);
-                    else dK[(i - 8) % 6] = mfma32(fr[i % RD], dsb[(i - 8) / 6], dK[(i - 8) % 6]);
+                    if (i < 8) dV[i] = mfma16(fr[i % RD], pb, dV[i]);
+                    else dK[i - 8] = mfma16(fr[i % RD], dsb, dK[i - 8]);
                     if (i + RD < 20) fr[i % RD] = lds128(faddr(i + RD));
                 }
                 __builtin_amdgcn_sched_group_barrier(0x100, RD, 1);
@@ -577,40 +582,37 @@ void bwd_dkdv_kernel(BwdArgs a) {
         __syncthreads();
     }
 
-    // ---- epilogue: dK[mb][e] / dV[mb][e] hold dim 32*mb + 8*(e/4) + 4*h2 + (e%4) of key j
+    // ---- epilogue: dK[mb][i] / dV[mb][i] hold dim 16 mb + 4 g4 + i of key j
     if (!jval) return;
 #pragma unroll
-    for (int mb = 0; mb < 6; ++mb)
+    for (int mb = 0; mb < 12; ++mb) dK[mb] *= a.scale;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) dK[mb][e] *= a.scale;
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int d = 8 * (e / 4) + 4 * h2 + (e % 4);
-        float x = dK[0][e], y = dK[1][e];
-        rope_back(x, y, a.rt.turn[d], a.pos0 + j);
-        dK[0][e] = x;
-        dK[1][e] = y;
+        for (int i = 0; i < 4; ++i) {
+            const int d = 16 * mb + 4 * g4 + i;   // < 32: rotary pair (d, d + 32) = blocks mb, mb + 2
+            float x = dK[mb][i], y = dK[mb + 2][i];
+            rope_back(x, y, a.rt.turn[d], a.pos0 + j);
+            dK[mb][i] = x;
+            dK[mb + 2][i] = y;
+        }
+    const size_t orow = ((size_t)b * a.T + j) * a.Hkv + g;
+    uint16_t *dk = a.dk + orow * kDqk + 4 * g4;
+    uint16_t *dv = a.dv + orow * kDv + 4 * g4;
+#pragma unroll
+    for (int mb = 0; mb < 12; ++mb) {
+        u32x2 o;
+        o[0] = pack_bf16(dK[mb][0], dK[mb][1]);
+        o[1] = pack_bf16(dK[mb][2], dK[mb][3]);
+        *reinterpret_cast<u32x2 *>(dk + 16 * mb) = o;
     }
-    uint16_t *dk = a.dk + krow * kDqk;
-    uint16_t *dv = a.dv + krow * kDv;
 #pragma unroll
-    for (int mb = 0; mb < 6; ++mb)
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-            u32x2 o;
-            o[0] = pack_bf16(dK[mb][4 * e4], dK[mb][4 * e4 + 1]);
-            o[1] = pack_bf16(dK[mb][4 * e4 + 2], dK[mb][4 * e4 + 3]);
-            *reinterpret_cast<u32x2 *>(dk + 32 * mb + 8 * e4 + 4 * h2) = o;
-        }
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-            u32x2 o;
-            o[0] = pack_bf16(dV[mb][4 * e4] * a.v_scale, dV[mb][4 * e4 + 1] * a.v_scale);
-            o[1] = pack_bf16(dV[mb][4 * e4 + 2] * a.v_scale, dV[mb][4 * e4 + 3] * a.v_scale);
-            *reinterpret_cast<u32x2 *>(dv + 32 * mb + 8 * e4 + 4 * h2) = o;
-        }
+    for (int mb = 0; mb < 8; ++mb) {
+        u32x2 o;
+        o[0] = pack_bf16(dV[mb][0] * a.v_scale, dV[mb][1] * a.v_scale);
+        o[1] = pack_bf16(dV[mb][2] * a.v_scale, dV[mb][3] * a.v_scale);
+        *reinterpret_cast<u32x2 *>(dv + 16 * mb) = o;
+    }
 }
 
 size_t backward_workspace_bytes(int32_t B, int32_t T, int32_t Hq) {
@@ -635,7 +637,7 @@ hipError_t launch_backward(BwdArgs a, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     const int64_t kblocks = (int64_t)a.B * a.Hkv * a.n_kblk;
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kblocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kblocks), dim3(512), 0, stream, a);
     return hipGetLastError();
 }
 
