@@ -45,13 +45,18 @@ def assert_parity(got: np.ndarray, ref: np.ndarray, what: str, max_abs=MAX_ABS, 
 
 
 def assert_grad_parity(got: np.ndarray, ref: np.ndarray, what: str):
-    """Gradient bar: |got - ref| <= 2e-2 + 2^-7 |ref| per element, mean-abs <= 2e-3."""
+    """Gradient bar: |got - ref| <= 2e-2 + 2^-7 |ref| per element and mean-abs <= 2e-3 +
+    2^-8 mean |ref|.  The relative terms are two bf16 roundings of up to 2^-8 |value| each
+    (P and dS as MFMA operands, the stored gradient); the mean bar takes half of the
+    per-element one, which only matters where gradients are sums of a few O(1) terms
+    (a sequence of one token)."""
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
     d = np.abs(got - ref)
     allowed = MAX_ABS + 2.0 ** -7 * np.abs(ref)
     worst = float(np.max(d / allowed)) if d.size else 0.0
     mn = float(d.mean()) if d.size else 0.0
+    mean_bar = MEAN_ABS + 2.0 ** -8 * (float(np.abs(ref).mean()) if d.size else 0.0)
     say(f"  {what}: max-abs {float(d.max()) if d.size else 0.0:.3e} (max |ref| {float(np.abs(ref).max()):.2f}), "
-        f"worst err / (2e-2 + 2^-7 |ref|) {worst:.3f}, mean-abs {mn:.3e}")
-    assert worst <= 1.0 and mn <= MEAN_ABS, f"{what}: worst {worst:.3f} of the bar, mean-abs {mn:.3e}"
+        f"worst err / (2e-2 + 2^-7 |ref|) {worst:.3f}, mean-abs {mn:.3e} (bar {mean_bar:.3e})")
+    assert worst <= 1.0 and mn <= mean_bar, f"{what}: worst {worst:.3f} of the bar, mean-abs {mn:.3e} > {mean_bar:.3e}"
