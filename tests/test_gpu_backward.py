@@ -91,7 +91,7 @@ def test_backward_sliding(B, T, window, sinks, pos0):
     check_grads(got, ref, "sliding", bar)
 
 
-@pytest.mark.parametrize("hq,hkv,T", [(64, 4, 300), (16, 4, 130), (8, 2, 70)])
+@pytest.mark.parametrize("hq,hkv,T", [(64, 4, 300), (16, 4, 130), (8, 2, 70), (64, 1, 90)])
 def test_backward_global(hq, hkv, T):
     d = gen.prefill_inputs(1, T, hq, hkv, seed=10101 + T, with_sinks=False)
     dout = gen.normal_bf16(np.random.SeedSequence(10102 + T), (1, T, hq, 128))

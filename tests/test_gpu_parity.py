@@ -108,6 +108,7 @@ SWA_CASES = [
     (40, 96, 0, 128, True, (64, 8)),     # 320 (sequence, KV head) pairs: one run each, 3 blocks
     (1, 2000, 0, 128, True, (64, 8)),    # runs of 2 blocks, the last run 1 block
     (1, 500, 7, 64, True, (64, 8)),      # window 64, positions offset by 7
+    (1, 150, 0, 128, True, (32, 1)),     # one KV head for 32 query heads
     # With fewer 32-query blocks than CUs (B x KV heads x blocks < 256) the per-block
     # kernel runs; the cases below have >= 256 and take the band kernel, so both
     # kernels see far positions, window 1 and 64, no sink and single tokens.
@@ -163,6 +164,7 @@ GLOBAL_CASES = [
     (2, 257, 0, (64, 4)),
     (1, 300, 128, (32, 8)),      # GQA group of 4
     (1, 1, 0, (64, 4)),
+    (1, 200, 50, (64, 1)),       # one KV head for all 64 query heads
 ]
 
 
