@@ -242,7 +242,10 @@ mimo_status mimo_attn_prefill_backward(const mimo_attn_cfg *cfg, const uint16_t 
                     ws ? ws_bytes : (size_t)0);
     BwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse; a.sinks = sinks;
-    a.D = (float *)ws; a.csink = a.D + (size_t)B * T * cfg->num_q_heads;
+    const size_t rows = (size_t)B * T * cfg->num_q_heads;
+    a.qrot = (uint16_t *)ws;
+    a.D = (float *)((char *)ws + rows * 64 * sizeof(uint16_t));
+    a.csink = a.D + rows;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dsinks = sinks ? dsinks : nullptr;
     a.B = B; a.T = T; a.Hq = cfg->num_q_heads; a.Hkv = cfg->num_kv_heads; a.window = cfg->window; a.pos0 = pos0;
     a.scale = cfg->softmax_scale; a.scale_log2 = scale_log2(cfg); a.v_scale = cfg->v_scale;

@@ -10,22 +10,23 @@
 //
 //   bwd_dq_kernel      query-major: a workgroup owns 32 queries x 4 heads of a
 //                      GQA group; it forms D per (row, head) from O and dO and
-//                      per head the sum of its rows' sink terms, then per 32-key
+//                      per head the sum of its rows' sink terms, writes D and
+//                      the rotated dims 0..63 of Q~ for dk/dv, then per 32-key
 //                      tile (K rotated, K^T and V staged in LDS, shared by the 4
 //                      heads) rebuilds S^T and dP^T and accumulates
 //                      dQ~^T = K~^T dS^T in registers
 //   bwd_sink_kernel    one workgroup per head sums the sink partials (fixed order)
-//   bwd_dkdv_kernel    key-major: a workgroup owns 128 keys of one KV head (one
-//                      wave per 16 keys, two waves per SIMD, 16x16x32 MFMAs, the
-//                      keys' K~ and V held in registers); it walks every query
+//   bwd_dkdv_kernel    key-major: a workgroup owns 64 keys of one KV head (one
+//                      wave per 16 keys, 16x16x32 MFMAs, the keys' K~ and V held
+//                      in registers; two workgroups per CU); it walks every query
 //                      head of the group and every 32-query block that sees its
-//                      keys (Q~, Q~^T, dO, dO^T staged in LDS, double-buffered)
-//                      and accumulates dK~^T = Q~^T dS and dV^T = dO^T P
+//                      keys (Q~ and dO rows copied into LDS by buffer loads that
+//                      write LDS, double-buffered; the rotated dims of Q~ come
+//                      from the dq pass) and accumulates dK~^T = Q~^T dS and
+//                      dV^T = dO^T P, reading Q~^T and dO^T with LDS transpose loads
 // Both kernels reuse the forward's layout trick: the A-operand rows of the first
 // product are read in a permuted order, so each lane's accumulators are directly
-// the B operand of the second product.  The dk/dv stages are written transposed
-// straight from registers: a staging thread holds both rows of a row pair and
-// stores each column pair as a dword.
+// the B operand of the second product.
 // Nothing is accumulated across workgroups, so the results are deterministic.
 #include "kernels.hpp"
 
@@ -204,7 +205,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     Dq = sum_xor32(Dq);
 #pragma unroll
     for (int s = 0; s < 8; ++s) *reinterpret_cast<u32x4 *>(dos + 8 * s) = dof[s];
-    if (tval && h2 == 0) a.D[qrow] = Dq;   // for the dk/dv pass
+    if (tval && h2 == 0) {
+        // for the dk/dv pass, head-major so that a 32-query stage is contiguous: D and
+        // the rotated dims 0..63 of Q~ (this lane's qf[0..7])
+        const size_t hrow = ((size_t)b * a.Hq + head) * a.T + t;
+        a.D[hrow] = Dq;
+        uint16_t *qr = a.qrot + hrow * kRope;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) stg128(qr + 8 * s, qf[s]);
+    }
     if (a.sinks) {
         // this head's sink terms -exp(sink - L) D summed over the block's 32 rows
         // (fixed order), one partial per (batch, query block, head)
@@ -318,23 +327,62 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
         }
 }
 
-// ---- dk, dv: 128 keys of one KV head per workgroup, one wave per 16 keys (two
+// ---- dk, dv: 16 NWV keys of one KV head per workgroup, one wave per 16 keys (two
 // waves per SIMD), 16x16x32 MFMAs.  Lane (g4 = lane / 16, l16 = lane % 16) holds,
 // for key kw0 + l16 of its wave, dims 32 c + 8 g4 .. + 7 of K~ and V (B operands of
 // S = Q~ K~^T and dP = dO V^T).  The A operands of S and dP are Q~ / dO rows read
 // in the order pi: in query block qb of the stage's 32 queries, MFMA row 4 u + i
 // is query 8 u + 4 qb + i, so that a lane's accumulators of the two blocks hold
 // queries 8 g4 .. 8 g4 + 7 of its key: exactly the B operand (8 consecutive
-// queries) of dV^T = dO^T P and dK~^T = Q~^T dS.
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+// queries) of dV^T = dO^T P and dK~^T = Q~^T dS.  The A operands of those two
+// (dO^T, Q~^T: 16 dims x 8 consecutive queries per lane) are read from the same
+// row-major stage with LDS transpose loads (ds_read_b64_tr_b16: within each 16
+// lanes, output lane 16 G + r, element e comes from element r % 4 of the 8 bytes
+// that lane 16 G + 4 e + r / 4 addresses).
+//
+// A stage (32 queries of one head) is copied into LDS by buffer loads that write
+// LDS directly, gathering its rows from q, dout, lse and the dq pass's workspace
+// (rotated dims of Q~ and D): no staging registers, no RoPE, no transpose.  Stage
+// layout in bytes, per buffer: Q~ dims 0..63 rows of 144 (64 + 8 pad), Q dims
+// 64..191 rows of 272, dO rows of 272, L and D 32 floats each; each region is
+// whole 1 KiB copies (16 bytes per lane; lanes past the region's rows re-read
+// the last row into slack).
+namespace {
+constexpr int kQaStr = 72, kQbStr = 136, kObStr = 136;   // row strides (elements)
+constexpr int kQaOff = 0, kQbOff = 5120, kObOff = 14336, kLOff = 23552, kDOff = 23808;   // bytes
+constexpr int kStageBytes = 24064;
+constexpr int kQaCopies = 5, kQbCopies = 9, kObCopies = 9;
+constexpr int kStageCopies = kQaCopies + kQbCopies + kObCopies + 2;   // + L, D (4 bytes per lane)
+constexpr uint32_t kRsrcFlags = 0x00020000u;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ void lds_copy(__amdgpu_buffer_rsrc_t rsrc, const unsigned char *lds_dst, int bytes,
+                                         int voffset) {
+    auto *d = (__attribute__((address_space(3))) void *)(const_cast<unsigned char *>(lds_dst));
+    if (bytes == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, d, 16, voffset, 0, 0, 0);
+    else __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, d, 4, voffset, 0, 0, 0);
+}
+
+// 8 consecutive rows (queries) x this lane's column of a row-major bf16 stage, as
+// one MFMA operand: two transpose loads, rows row0 .. row0 + 3 and row0 + 4 .. + 7
+// of the lane group.  p0 is this lane's address for the first four rows.
+__device__ __forceinline__ u32x4 lds_tr8(const uint16_t *p0, int str) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(const_cast<uint16_t *>(p0)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(const_cast<uint16_t *>(p0 + 4 * str)));
+    const u32x2 a = __builtin_bit_cast(u32x2, lo), c = __builtin_bit_cast(u32x2, hi);
+    return u32x4{a[0], a[1], c[0], c[1]};
+}
+}  // namespace
+
+template <int NWV>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NWV, 64 * NWV), amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdArgs a) {
-    constexpr int KPW = 16;   // keys per wave (8 waves)
-    // two stage buffers: one is computed on while the next is written
-    __shared__ __attribute__((aligned(16))) uint16_t Qsb[2][32 * RSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t QTsb[2][kDqk * TSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t Osb[2][32 * VSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t OTsb[2][kDv * TSTR];
-    __shared__ __attribute__((aligned(16))) float Lsb[2][32], Dsb[2][32];
+    constexpr int KPW = 16;   // keys per wave
+    constexpr int KPB = KPW * NWV;
+    // two stage buffers: one is computed on while the next is copied in
+    __shared__ __attribute__((aligned(1024))) unsigned char stg[2][kStageBytes];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g4 = lane >> 4, l16 = lane & 15;
@@ -343,12 +391,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const int r = blockIdx.x - b * per_b;
     const int g = r % a.Hkv;
     const int kb = a.n_kblk - 1 - r / a.Hkv;          // later keys see fewer queries under a causal mask
-    const int jb0 = kb * 128;
+    const int jb0 = kb * KPB;
     const int kw0 = jb0 + KPW * w;                     // this wave's keys
     const int j = kw0 + l16;
     const bool jval = j < a.T;
     const int G = a.Hq / a.Hkv;
-    const size_t qrs = (size_t)a.Hq * kDqk, ors = (size_t)a.Hq * kDv;
 
     const size_t krow = ((size_t)b * a.T + (jval ? j : a.T - 1)) * a.Hkv + g;
     u32x4 kf[6], vf[4];
@@ -372,106 +419,64 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const int win = a.window > 0 ? a.window : 0x7fffffff;
     // queries that see some key of the workgroup, and of this wave
     const int qlo = jb0;
-    const int qhi = a.window > 0 ? min(a.T - 1, jb0 + 127 + a.window - 1) : a.T - 1;
+    const int qhi = a.window > 0 ? min(a.T - 1, jb0 + KPB - 1 + a.window - 1) : a.T - 1;
     const int wq_hi = a.window > 0 ? kw0 + KPW - 1 + a.window - 1 : 0x7fffffff;
     // query row of MFMA row l16 in query block qb (the order pi above)
     const int prow0 = 8 * (l16 >> 2) + (l16 & 3);
+    // transpose loads: this lane addresses row 8 (lane / 16) + (lane % 16) / 4 and
+    // the 4 columns from 4 (lane % 4) of a 16-column block
+    const int trow = 8 * g4 + (l16 >> 2), tcol = 4 * (lane & 3);
 
-    // stages (query head, 32-query block), head-major; the next stage's rows are
-    // loaded into registers while this one is computed
+    // stages (query head, 32-query block), head-major
     const int q_first = (qlo / 32) * 32;
     const int n_qb = (qhi - q_first) / 32 + 1;
     const int n_stage = G * n_qb;
-    // Staging of a stage (32 query rows of one head): threads < 256 take the row
-    // pair (2 rp, 2 rp + 1), rp = t % 16, the rotating pairs (rd, rd + 1) with
-    // rd = 8 (t / 64) + 2 ((t / 16) % 4) and their partners rd + 32, rd + 33 (four
-    // rotations each), and Q pass-through chunk 8 + t / 16; threads >= 256 take the
-    // row pair's dO chunk t / 16 (t = tid - 256) and the rows' L and D.  Waves w
-    // and w + 4 share a SIMD, so every SIMD stages as much.  Holding both rows of a
-    // pair, a thread writes its pieces row-major and, two rows per dword, transposed.
-    const bool qthr = tid < 256;
-    const int t8 = tid & 255, rp = t8 & 15, rc = t8 >> 4;
-    const int rd = 8 * (t8 >> 6) + 2 * ((t8 >> 4) & 3);
-    const uint64_t turn0 = a.rt.turn[rd], turn1 = a.rt.turn[rd + 1];
-    struct DkStage {
-        uint32_t rx[2], ry[2];   // [row of pair] dims rd, rd + 1 / rd + 32, rd + 33 (Q threads)
-        u32x4 ch[2];             // [row of pair] Q pass-through chunk (Q threads) or dO chunk
-        float lv, dv;            // L and D of query row t8 % 32 (dO threads)
-    };
-    auto load_stage = [&](DkStage &st, int s_) {
-        s_ = min(s_, n_stage - 1);   // past the last stage: re-read it (unused)
+    const int Hq = a.Hq;
+    auto copy_stage = [&](int s_, int buf) {
         const int head = g * G + s_ / n_qb, q0 = q_first + 32 * (s_ % n_qb);
-        const int last = min(32, a.T - q0) - 1;
-        if (qthr) {
-            const uint16_t *qb_ = a.q + ((size_t)b * a.T + q0) * qrs + (size_t)head * kDqk;
+        const int last = min(32, a.T - q0) - 1;   // rows past it re-read it: masked out of every product
+        const size_t hrow = ((size_t)b * Hq + head) * a.T + q0;
+        const size_t trow0 = ((size_t)b * a.T + q0) * Hq + head;
+        const unsigned char *dst = stg[buf];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                // rows past the end re-read the last valid row: masked out of every product
-                const uint16_t *qrow_ = qb_ + min(2 * rp + i, last) * qrs;
-                st.rx[i] = *reinterpret_cast<const uint32_t *>(qrow_ + rd);
-                st.ry[i] = *reinterpret_cast<const uint32_t *>(qrow_ + rd + 32);
-                st.ch[i] = ldg128(qrow_ + 8 * (8 + rc));
+        for (int m = 0; m < (kStageCopies + NWV - 1) / NWV; ++m) {
+            const int id = w + NWV * m;   // wave-uniform
+            if (id < kQaCopies) {
+                const int c = 64 * id + lane, row = c / 9, piece = c - 9 * row;
+                const auto rs = __builtin_amdgcn_make_buffer_rsrc(a.qrot + hrow * kRope, 0, (last + 1) * 128, kRsrcFlags);
+                lds_copy(rs, dst + kQaOff + 1024 * id, 16, min(row, last) * 128 + 16 * min(piece, 7));
+            } else if (id < kQaCopies + kQbCopies) {
+                const int c = 64 * (id - kQaCopies) + lane, row = c / 17, piece = c - 17 * row;
+                const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.q + trow0 * kDqk), 0,
+                                                                  last * Hq * 384 + 384, kRsrcFlags);
+                lds_copy(rs, dst + kQbOff + 1024 * (id - kQaCopies), 16, min(row, last) * Hq * 384 + 128 + 16 * min(piece, 15));
+            } else if (id < kQaCopies + kQbCopies + kObCopies) {
+                const int c = 64 * (id - kQaCopies - kQbCopies) + lane, row = c / 17, piece = c - 17 * row;
+                const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.dout + trow0 * kDv), 0,
+                                                                  last * Hq * 256 + 256, kRsrcFlags);
+                lds_copy(rs, dst + kObOff + 1024 * (id - kQaCopies - kQbCopies), 16,
+                         min(row, last) * Hq * 256 + 16 * min(piece, 15));
+            } else if (id < kStageCopies) {
+                const bool isL = id == kStageCopies - 2;
+                const float *src = isL ? a.lse + hrow : a.D + hrow;
+                const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(src), 0, (last + 1) * 4, kRsrcFlags);
+                lds_copy(rs, dst + (isL ? kLOff : kDOff), 4, min(lane, last) * 4);
             }
-        } else {
-            const uint16_t *ob_ = a.dout + ((size_t)b * a.T + q0) * ors + (size_t)head * kDv;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) st.ch[i] = ldg128(ob_ + min(2 * rp + i, last) * ors + 8 * rc);
-            const int lr = t8 & 31, lrc = min(lr, last);
-            const float lv = a.lse[((size_t)b * a.Hq + head) * a.T + q0 + lrc];
-            const float dv = a.D[((size_t)b * a.T + q0 + lrc) * a.Hq + head];
-            st.lv = lr <= last ? lv * kLog2e : kPosInf;
-            st.dv = lr <= last ? dv : 0.0f;
         }
     };
-    // chunk x0 (row 2*rp) and x1 (row 2*rp + 1) of 8 columns starting at col:
-    // row-major into d (row stride sstr), transposed into dT (column-major pairs)
-    auto put2 = [&](uint16_t *d, uint16_t *dT, int sstr, int col, const u32x4 &x0, const u32x4 &x1) {
-        *reinterpret_cast<u32x4 *>(d + (2 * rp) * sstr + col) = x0;
-        *reinterpret_cast<u32x4 *>(d + (2 * rp + 1) * sstr + col) = x1;
-#pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-            const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-            *reinterpret_cast<uint32_t *>(dT + (col + dd) * TSTR + 2 * rp) = __builtin_amdgcn_perm(x1[dd >> 1], x0[dd >> 1], sel);
-        }
-    };
-    auto store_stage = [&](const DkStage &st, int s_, int buf) {
-        const int q0 = q_first + 32 * (s_ % n_qb);
-        if (qthr) {
-            uint32_t x[2], y[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int64_t pos = a.pos0 + q0 + 2 * rp + i;
-                float s0, c0, s1, c1;
-                rope_sincos(turn0, pos, s0, c0);
-                rope_sincos(turn1, pos, s1, c1);
-                const float x0 = bf_lo(st.rx[i]), x1 = bf_hi(st.rx[i]);
-                const float y0 = bf_lo(st.ry[i]), y1 = bf_hi(st.ry[i]);
-                x[i] = pack_bf16(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
-                y[i] = pack_bf16(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
-                *reinterpret_cast<uint32_t *>(Qsb[buf] + (2 * rp + i) * RSTR + rd) = x[i];
-                *reinterpret_cast<uint32_t *>(Qsb[buf] + (2 * rp + i) * RSTR + rd + 32) = y[i];
-            }
-            *reinterpret_cast<uint32_t *>(QTsb[buf] + rd * TSTR + 2 * rp) = __builtin_amdgcn_perm(x[1], x[0], 0x05040100u);
-            *reinterpret_cast<uint32_t *>(QTsb[buf] + (rd + 1) * TSTR + 2 * rp) = __builtin_amdgcn_perm(x[1], x[0], 0x07060302u);
-            *reinterpret_cast<uint32_t *>(QTsb[buf] + (rd + 32) * TSTR + 2 * rp) = __builtin_amdgcn_perm(y[1], y[0], 0x05040100u);
-            *reinterpret_cast<uint32_t *>(QTsb[buf] + (rd + 33) * TSTR + 2 * rp) = __builtin_amdgcn_perm(y[1], y[0], 0x07060302u);
-            put2(Qsb[buf], QTsb[buf], RSTR, 8 * (8 + rc), st.ch[0], st.ch[1]);
-        } else {
-            put2(Osb[buf], OTsb[buf], VSTR, 8 * rc, st.ch[0], st.ch[1]);
-            Lsb[buf][t8 & 31] = st.lv;
-            Dsb[buf][t8 & 31] = st.dv;
-        }
-    };
-    DkStage st;
-    load_stage(st, 0);
-    store_stage(st, 0, 0);
-    load_stage(st, 1);
-    __syncthreads();
+
+    copy_stage(0, 0);
+    __syncthreads();   // also waits for this wave's copies
     for (int s_ = 0; s_ < n_stage; ++s_) {
         const int q0 = q_first + 32 * (s_ % n_qb);
         const int buf = s_ & 1;
-        const uint16_t *Qs = Qsb[buf], *QTs = QTsb[buf], *Os = Osb[buf], *OTs = OTsb[buf];
-        const float *Ls = Lsb[buf], *Ds = Dsb[buf];
+        // the next stage goes to the other buffer, last read in the previous stage
+        if (s_ + 1 < n_stage) copy_stage(s_ + 1, buf ^ 1);
+        const uint16_t *Qa = reinterpret_cast<const uint16_t *>(stg[buf] + kQaOff);
+        const uint16_t *Qb = reinterpret_cast<const uint16_t *>(stg[buf] + kQbOff);
+        const uint16_t *Ob = reinterpret_cast<const uint16_t *>(stg[buf] + kObOff);
+        const float *Ls = reinterpret_cast<const float *>(stg[buf] + kLOff);
+        const float *Ds = reinterpret_cast<const float *>(stg[buf] + kDOff);
         // does this wave's key range meet the block's queries? (wave-uniform)
         if (!(kw0 > q0 + 31 || q0 > wq_hi)) {
             f32x4 S[2], DP[2];
@@ -488,7 +493,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
                     const int u = i < 12 ? i : i - 12;
                     const int qb = i < 12 ? u / 6 : u / 4, c = i < 12 ? u % 6 : u % 4;
                     const int row = prow0 + 4 * qb;
-                    return i < 12 ? Qs + row * RSTR + 32 * c + 8 * g4 : Os + row * VSTR + 32 * c + 8 * g4;
+                    return i < 12 ? (c < 2 ? Qa + row * kQaStr + 32 * c : Qb + row * kQbStr + 32 * (c - 2)) + 8 * g4
+                                  : Ob + row * kObStr + 32 * c + 8 * g4;
                 };
                 auto order = [](int i) { return i < 16 ? ((i & 1) ? 12 + (i >> 1) : (i >> 1)) : i - 8; };
                 u32x4 fr[RS];
@@ -539,7 +545,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
                 for (int x = 0; x < 8; ++x) {
                     const float sx = S[x >> 2][x & 3], dpx = DP[x >> 2][x & 3];
-                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sx, cl2, -lrow[x]));
+                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sx, cl2, -lrow[x] * kLog2e));
                     if (!full && (uint32_t)(x - lo) > span) p = 0.0f;
                     p8[x] = p;
                     d8[x] = p * (dpx * a.v_scale - drow[x]);
@@ -551,35 +557,35 @@ void bwd_dkdv_kernel(BwdArgs a) {
                 }
             }
             // dV^T (128 x 16 keys) += dO^T P;  dK~^T (192 x 16 keys) += Q~^T dS: 20
-            // MFMAs, RD fragment reads in flight
+            // MFMAs, RD fragments (two transpose loads each) in flight
             __builtin_amdgcn_sched_barrier(0);
             {
                 constexpr int RD = 8;
-                auto faddr = [&](int i) {   // i < 8: dV block i; else dK block i - 8
-                    return (i < 8 ? OTs + (16 * i + l16) * TSTR : QTs + (16 * (i - 8) + l16) * TSTR) + 8 * g4;
+                auto fload = [&](int i) {   // i < 8: dV block i; else dK block i - 8
+                    if (i < 8) return lds_tr8(Ob + trow * kObStr + 16 * i + tcol, kObStr);
+                    const int mb = i - 8;
+                    return mb < 4 ? lds_tr8(Qa + trow * kQaStr + 16 * mb + tcol, kQaStr)
+                                  : lds_tr8(Qb + trow * kQbStr + 16 * (mb - 4) + tcol, kQbStr);
                 };
                 u32x4 fr[RD];
 #pragma unroll
-                for (int i = 0; i < RD; ++i) fr[i] = lds128(faddr(i));
+                for (int i = 0; i < RD; ++i) fr[i] = fload(i);
 #pragma unroll
                 for (int i = 0; i < 20; ++i) {
                     if (i < 8) dV[i] = mfma16(fr[i % RD], pb, dV[i]);
                     else dK[i - 8] = mfma16(fr[i % RD], dsb, dK[i - 8]);
-                    if (i + RD < 20) fr[i % RD] = lds128(faddr(i + RD));
+                    if (i + RD < 20) fr[i % RD] = fload(i + RD);
                 }
-                __builtin_amdgcn_sched_group_barrier(0x100, RD, 1);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * RD, 1);
 #pragma unroll
                 for (int i = 0; i < 20 - RD; ++i) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, RD, 1);
             }
         }
-        // the next stage goes to the other buffer, read last in the previous stage
-        store_stage(st, s_ + 1 < n_stage ? s_ + 1 : s_, buf ^ 1);
-        load_stage(st, s_ + 2);
-        __syncthreads();
+        __syncthreads();   // this stage's reads are done; also waits for this wave's copies of the next
     }
 
     // ---- epilogue: dK[mb][i] / dV[mb][i] hold dim 16 mb + 4 g4 + i of key j
@@ -617,7 +623,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
 
 size_t backward_workspace_bytes(int32_t B, int32_t T, int32_t Hq) {
     const size_t rows = (size_t)B * T * Hq;
-    return (rows + (size_t)B * ((T + 31) / 32) * Hq) * sizeof(float);
+    return rows * kRope * sizeof(uint16_t) + (rows + (size_t)B * ((T + 31) / 32) * Hq) * sizeof(float);
 }
 
 hipError_t launch_backward(BwdArgs a, hipStream_t stream) {
@@ -625,7 +631,8 @@ hipError_t launch_backward(BwdArgs a, hipStream_t stream) {
     if (G % 4 != 0) return hipErrorInvalidValue;
     a.n_qblk = (a.T + 31) / 32;
     a.n_hgrp = G / 4;
-    a.n_kblk = (a.T + 127) / 128;
+    constexpr int kDkdvWaves = 4;
+    a.n_kblk = (a.T + 16 * kDkdvWaves - 1) / (16 * kDkdvWaves);
     // dq also forms D and the sink partials; d sink and dk/dv read them
     const int64_t qblocks = (int64_t)a.B * a.Hkv * a.n_hgrp * a.n_qblk;
     hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)qblocks), dim3(256), 0, stream, a);
@@ -637,7 +644,7 @@ hipError_t launch_backward(BwdArgs a, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     const int64_t kblocks = (int64_t)a.B * a.Hkv * a.n_kblk;
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kblocks), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<kDkdvWaves>, dim3((unsigned)kblocks), dim3(64 * kDkdvWaves), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -67,7 +67,8 @@ struct BwdArgs {
     const uint16_t *q, *k, *v, *out, *dout;   // [B, T, H, D] bf16, q/k unrotated
     const float *lse;                         // [B, Hq, T] natural-log LSE of the forward
     const float *sinks;                       // nullable
-    float *D;                                 // workspace [B, T, Hq]: rowsum(dO o O)
+    uint16_t *qrot;                           // workspace [B, Hq, T, 64]: the rotated dims of Q~ (bf16)
+    float *D;                                 // workspace [B, Hq, T]: rowsum(dO o O)
     float *csink;                             // workspace [B * 32-query blocks, Hq]: sink-term partials
     uint16_t *dq, *dk, *dv;
     float *dsinks;                            // [Hq], written when sinks != NULL
