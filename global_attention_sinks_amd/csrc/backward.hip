@@ -159,8 +159,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     const int combos = a.B * a.Hkv * a.n_hgrp;
     const int qb = a.n_qblk - 1 - (int)(blockIdx.x / combos);   // longest key range first
     const int c = blockIdx.x % combos;
-    const int b = c % a.B, pair = c / a.B;
-    const int hg = pair % a.n_hgrp, g = pair / a.n_hgrp;
+    // consecutive workgroups land on different XCDs (each with its own L2): the
+    // head groups of one (sequence, KV head) sit combos / n_hgrp apart, a multiple
+    // of 8 when B * Hkv is, so they share an XCD and its copy of the K/V tiles
+    const int bg = c % (a.B * a.Hkv), hg = c / (a.B * a.Hkv);
+    const int b = bg % a.B, g = bg / a.B;
     const int G = a.Hq / a.Hkv;
     const int head = g * G + hg * NW + w;
     const int q0 = qb * 32;
@@ -384,7 +387,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
     // two stage buffers: one is computed on while the next is copied in
     __shared__ __attribute__((aligned(1024))) unsigned char stg[2][kStageBytes];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // w through readfirstlane: the compiler then knows it (and the copies' choice of
+    // source and LDS region) to be wave-uniform
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = lane >> 4, l16 = lane & 15;
     const int per_b = a.Hkv * a.n_kblk;
     const int b = blockIdx.x / per_b;
@@ -534,13 +539,21 @@ void bwd_dkdv_kernel(BwdArgs a) {
             }
             u32x4 pb, dsb;
             {
-                // the lane's 8 query rows are consecutive: their L and D in two 16-byte reads each
-                const float4 l0 = *reinterpret_cast<const float4 *>(Ls + 8 * g4);
-                const float4 l1 = *reinterpret_cast<const float4 *>(Ls + 8 * g4 + 4);
-                const float4 d0 = *reinterpret_cast<const float4 *>(Ds + 8 * g4);
-                const float4 d1 = *reinterpret_cast<const float4 *>(Ds + 8 * g4 + 4);
-                const float lrow[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-                const float drow[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+                // the lane's 8 query rows are consecutive: their L and D in two 16-byte reads
+                // each, read as integer vectors (as float vectors the compiler could not tell
+                // them from the next stage's copies in flight and waited for those first)
+                const u32x4 l0 = *reinterpret_cast<const u32x4 *>(Ls + 8 * g4);
+                const u32x4 l1 = *reinterpret_cast<const u32x4 *>(Ls + 8 * g4 + 4);
+                const u32x4 d0 = *reinterpret_cast<const u32x4 *>(Ds + 8 * g4);
+                const u32x4 d1 = *reinterpret_cast<const u32x4 *>(Ds + 8 * g4 + 4);
+                float lrow[8], drow[8];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    lrow[x] = __uint_as_float(l0[x]);
+                    lrow[4 + x] = __uint_as_float(l1[x]);
+                    drow[x] = __uint_as_float(d0[x]);
+                    drow[4 + x] = __uint_as_float(d1[x]);
+                }
                 float p8[8], d8[8];
 #pragma unroll
                 for (int x = 0; x < 8; ++x) {
