@@ -219,7 +219,7 @@ struct PagedLayout {
 
 size_t mimo_attn_backward_workspace_size(const mimo_attn_cfg *cfg, int32_t B, int32_t T) {
     if (!cfg || B <= 0 || T <= 0 || cfg->num_q_heads <= 0) return 0;
-    return backward_workspace_bytes(B, T, cfg->num_q_heads);
+    return backward_workspace_bytes(B, T, cfg->num_q_heads, cfg->num_kv_heads);
 }
 
 mimo_status mimo_attn_prefill_backward(const mimo_attn_cfg *cfg, const uint16_t *q, const uint16_t *k,
@@ -236,15 +236,16 @@ mimo_status mimo_attn_prefill_backward(const mimo_attn_cfg *cfg, const uint16_t 
     if (!out || !lse || !dout || !dk || !dv)
         return fail(MIMO_ERR_INVALID_ARGUMENT, "out, lse, dout, dq, dk and dv must be non-NULL");
     if (sinks && !dsinks) return fail(MIMO_ERR_INVALID_ARGUMENT, "dsinks must be non-NULL when sinks are given");
-    const size_t need = backward_workspace_bytes(B, T, cfg->num_q_heads);
+    const size_t need = backward_workspace_bytes(B, T, cfg->num_q_heads, cfg->num_kv_heads);
     if (!ws || ws_bytes < need)
         return fail(MIMO_ERR_WORKSPACE, "backward workspace needs %zu bytes (got %zu)", need,
                     ws ? ws_bytes : (size_t)0);
     BwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse; a.sinks = sinks;
-    const size_t rows = (size_t)B * T * cfg->num_q_heads;
+    const size_t rows = (size_t)B * T * cfg->num_q_heads, krows = (size_t)B * T * cfg->num_kv_heads;
     a.qrot = (uint16_t *)ws;
-    a.D = (float *)((char *)ws + rows * 64 * sizeof(uint16_t));
+    a.krot = a.qrot + rows * 64;
+    a.D = (float *)(a.krot + krows * 64);
     a.csink = a.D + rows;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dsinks = sinks ? dsinks : nullptr;
     a.B = B; a.T = T; a.Hq = cfg->num_q_heads; a.Hkv = cfg->num_kv_heads; a.window = cfg->window; a.pos0 = pos0;

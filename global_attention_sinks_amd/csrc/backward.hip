@@ -36,9 +36,6 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kPosInf = __builtin_inff();
-constexpr int RSTR = kDqk + 8;   // LDS row stride of a 192-dim tile (bf16)
-constexpr int VSTR = kDv + 8;    // LDS row stride of a 128-dim tile
-constexpr int TSTR = 32 + 8;     // LDS row stride of a transposed 32-column tile
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
@@ -49,71 +46,6 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 __device__ __forceinline__ u32x4 lds128(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
-
-// Transpose a staged 32-row tile (row stride sstr, nch chunks of 8 columns) into
-// dst[col][row] (row stride TSTR): each unit takes two rows x 8 columns and
-// writes 8 dwords of two rows each.
-__device__ __forceinline__ void transpose32(uint16_t *dst, const uint16_t *src, int sstr, int nch, int tid,
-                                            int nthreads) {
-    for (int u = tid; u < 16 * nch; u += nthreads) {
-        const int rp = u % 16, c = u / 16;
-        const u32x4 a = lds128(src + (2 * rp) * sstr + 8 * c);
-        const u32x4 b = lds128(src + (2 * rp + 1) * sstr + 8 * c);
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-            const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
-            *reinterpret_cast<uint32_t *>(dst + (8 * c + d) * TSTR + 2 * rp) = __builtin_amdgcn_perm(b[d >> 1], a[d >> 1], sel);
-        }
-    }
-}
-
-// One 32-row stage held in registers between its global loads and its LDS
-// stores (256 threads): a 192-dim row piece that rotates (threads < 128), two
-// pass-through 192-dim chunks and two 128-dim chunks per thread.
-struct StageRegs {
-    u32x4 rx, ry;
-    u32x4 pl[2];
-    u32x4 r128[2];
-};
-
-__device__ __forceinline__ void stage_load(StageRegs &st, const uint16_t *src192, size_t s192,
-                                           const uint16_t *src128, size_t s128, int nvalid, int tid) {
-    // rows past the end re-read the last valid row: they are masked out of every
-    // product (zero probability), and finite values keep 0 * value = 0; the loads
-    // stay unconditional so that they are all in flight together
-    const int last = nvalid - 1;
-    if (tid < 128) {
-        const int row = min(tid >> 2, last), cc = tid & 3;
-        st.rx = ldg128(src192 + row * s192 + 8 * cc);
-        st.ry = ldg128(src192 + row * s192 + 8 * cc + 32);
-    }
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int u = tid + 256 * r;
-        const int row = min(u >> 4, last), c = 8 + (u & 15), c2 = u & 15;
-        st.pl[r] = ldg128(src192 + row * s192 + 8 * c);
-        st.r128[r] = ldg128(src128 + row * s128 + 8 * c2);
-    }
-}
-
-// Rotate (rows at positions pos0 + row) and store a loaded stage into LDS.
-__device__ __forceinline__ void stage_store(const StageRegs &st, uint16_t *d192, uint16_t *d128, int64_t pos0,
-                                            const RopeTurns &rt, int tid) {
-    if (tid < 128) {
-        const int row = tid >> 2, cc = tid & 3;
-        u32x4 x = st.rx, y = st.ry;
-        rope_rotate8(x, y, rt, 8 * cc, pos0 + row);
-        *reinterpret_cast<u32x4 *>(d192 + row * RSTR + 8 * cc) = x;
-        *reinterpret_cast<u32x4 *>(d192 + row * RSTR + 8 * cc + 32) = y;
-    }
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int u = tid + 256 * r;
-        const int row = u >> 4, c = 8 + (u & 15), c2 = u & 15;
-        *reinterpret_cast<u32x4 *>(d192 + row * RSTR + 8 * c) = st.pl[r];
-        *reinterpret_cast<u32x4 *>(d128 + row * VSTR + 8 * c2) = st.r128[r];
-    }
-}
 
 // Turn a rotated-space gradient held as (dims d, d + 32) pairs back: the
 // transpose of the rotation by pos * theta_d.
@@ -126,6 +58,58 @@ __device__ __forceinline__ void rope_back(float &x, float &y, uint64_t turn, int
     y = ny;
 }
 
+}  // namespace
+
+namespace {
+// Both kernels copy their LDS tiles with buffer loads that write LDS (a buffer
+// resource per source, 16 or 4 bytes per lane landing at lds + bytes * lane).
+// A tile's rows are split by source: the rotated dims 0..63 (rows of 64 + 8 pad
+// elements, 144 bytes, 9 copies of 16 bytes per row) and 128-dim rows (pass-
+// through dims of q / k, dO, V: 128 + 8 pad, 272 bytes, 17 copies per row), each
+// region whole 1 KiB copies (lanes past the region's rows re-read the last row
+// into slack).  Rows past the sequence re-read its last row: the masks zero them.
+constexpr int kRotStr = 72, kRowStr = 136;   // row strides (elements)
+constexpr int kRotBytes = 5120, kRowBytes = 9216;   // 32-row regions, whole 1 KiB copies
+constexpr int kRotCopies = 5, kRowCopies = 9;
+constexpr uint32_t kRsrcFlags = 0x00020000u;
+
+// dk/dv stage: Q~ dims 0..63, Q dims 64..191, dO, then L and D (32 floats each)
+constexpr int kQaOff = 0, kQbOff = kRotBytes, kObOff = kRotBytes + kRowBytes, kLOff = kRotBytes + 2 * kRowBytes;
+constexpr int kDOff = kLOff + 256, kStageBytes = kDOff + 256;
+constexpr int kStageCopies = kRotCopies + 2 * kRowCopies + 2;   // + L, D (4 bytes per lane)
+// dq tile: K~ dims 0..63, K dims 64..191, V
+constexpr int kKaOff = 0, kKbOff = kRotBytes, kVOff = kRotBytes + kRowBytes, kTileBytes = kRotBytes + 2 * kRowBytes;
+constexpr int kTileCopies = kRotCopies + 2 * kRowCopies;
+
+// Lane offsets of copy k of a region (c = 64 k + lane): rotated rows and 128-dim rows.
+__device__ __forceinline__ int rot_voff(int k, int lane, int last) {
+    const int c = 64 * k + lane, row = c / 9, piece = c - 9 * row;
+    return min(row, last) * 128 + 16 * min(piece, 7);
+}
+__device__ __forceinline__ int row_voff(int k, int lane, int last, int row_bytes) {
+    const int c = 64 * k + lane, row = c / 17, piece = c - 17 * row;
+    return min(row, last) * row_bytes + 16 * min(piece, 15);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ void lds_copy(__amdgpu_buffer_rsrc_t rsrc, const unsigned char *lds_dst, int bytes,
+                                         int voffset) {
+    auto *d = (__attribute__((address_space(3))) void *)(const_cast<unsigned char *>(lds_dst));
+    if (bytes == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, d, 16, voffset, 0, 0, 0);
+    else __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, d, 4, voffset, 0, 0, 0);
+}
+
+// 8 consecutive rows (queries) x this lane's column of a row-major bf16 stage, as
+// one MFMA operand: two transpose loads, rows row0 .. row0 + 3 and row0 + 4 .. + 7
+// of the lane group.  p0 is this lane's address for the first four rows.
+__device__ __forceinline__ u32x4 lds_tr8(const uint16_t *p0, int str) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(const_cast<uint16_t *>(p0)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(const_cast<uint16_t *>(p0 + 4 * str)));
+    const u32x2 a = __builtin_bit_cast(u32x2, lo), c = __builtin_bit_cast(u32x2, hi);
+    return u32x4{a[0], a[1], c[0], c[1]};
+}
 }  // namespace
 
 // ---- d sink_h: one workgroup per head, fixed-order tree sum over the workgroup partials
@@ -144,17 +128,38 @@ __global__ __launch_bounds__(256) void bwd_sink_kernel(BwdArgs a) {
     if (threadIdx.x == 0) a.dsinks[h] = red[0];
 }
 
-// ---- dq: 4 heads x 32 queries per workgroup, 32-key tiles
+// ---- rotated dims 0..63 of K for dq: krot [B, Hkv, T, 64], one thread per (key
+// row, KV head, 8 rotary pairs)
+__global__ __launch_bounds__(256) void bwd_krot_kernel(BwdArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)a.B * a.T * a.Hkv * 4) return;
+    const int cc = (int)(i & 3);
+    const int64_t rg = i >> 2;   // (b * T + t) * Hkv + g
+    const int g = (int)(rg % a.Hkv);
+    const int64_t bt = rg / a.Hkv;
+    const int t = (int)(bt % a.T), b = (int)(bt / a.T);
+    const uint16_t *src = a.k + rg * kDqk;
+    u32x4 x = ldg128(src + 8 * cc), y = ldg128(src + 32 + 8 * cc);
+    rope_rotate8(x, y, a.rt, 8 * cc, a.pos0 + t);
+    uint16_t *dst = a.krot + (((size_t)b * a.Hkv + g) * a.T + t) * kRope;
+    stg128(dst + 8 * cc, x);
+    stg128(dst + 32 + 8 * cc, y);
+}
+
+// ---- dq: 4 heads x 32 queries per workgroup, 32-key tiles copied into LDS (double-
+// buffered) by buffer loads: K~ dims 0..63 from krot, K dims 64..191, V.  S^T = K~ Q~^T
+// and dP^T = V dO^T read the key rows in the bit-2/3-swapped order prow, so dS^T packs
+// straight into the B operand of dQ~^T = K~^T dS^T, whose A operand (a dim x 8
+// consecutive keys per lane) comes from the row-major tile by LDS transpose loads.
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(BwdArgs a) {
     constexpr int NW = 4;
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[32 * RSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t KTs[kDqk * TSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[32 * VSTR];
-    // each wave's dO rows: the B operand of dP^T, parked in LDS (each lane reads
-    // back only what it wrote) to keep the kernel at two waves per SIMD
-    __shared__ __attribute__((aligned(16))) uint16_t DOs[NW][32 * VSTR];
+    __shared__ __attribute__((aligned(1024))) unsigned char tiles[2][kTileBytes];
+    // each wave's dO rows: the B operand of dP^T, parked in LDS (each lane reads back
+    // only what it wrote) to keep the kernel at two waves per SIMD; the 16-byte chunks
+    // of row r are XOR-swizzled by r % 16 so that 16 rows read at once hit distinct banks
+    __shared__ __attribute__((aligned(16))) uint16_t DOs[NW][32 * kDv];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h2 = lane >> 5, l32 = lane & 31;
     const int combos = a.B * a.Hkv * a.n_hgrp;
     const int qb = a.n_qblk - 1 - (int)(blockIdx.x / combos);   // longest key range first
@@ -177,7 +182,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     // per lane: Q~ (B operand of S^T = K~ Q~^T, dims 96*h2 + 8*s), dO (B operand of dP^T = V dO^T)
     const size_t qrow = ((size_t)b * a.T + t) * a.Hq + head;
     u32x4 qf[12], dof[8];
-    uint16_t *dos = DOs[w] + l32 * VSTR + 64 * h2;
+    uint16_t *dos = DOs[w] + l32 * kDv;
     float L2 = kPosInf, Dq = 0.0f;
     if (tval) {
         const uint16_t *src = a.q + qrow * kDqk + 96 * h2;
@@ -207,7 +212,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     }
     Dq = sum_xor32(Dq);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) *reinterpret_cast<u32x4 *>(dos + 8 * s) = dof[s];
+    for (int s = 0; s < 8; ++s) *reinterpret_cast<u32x4 *>(dos + 8 * ((8 * h2 + s) ^ (l32 & 15))) = dof[s];
     if (tval && h2 == 0) {
         // for the dk/dv pass, head-major so that a 32-query stage is contiguous: D and
         // the rotated dims 0..63 of Q~ (this lane's qf[0..7])
@@ -235,23 +240,50 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     const int prow = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
     const float cl2 = a.scale_log2;
     const int win = a.window > 0 ? a.window : 0x7fffffff;
-    const size_t krs = (size_t)a.Hkv * kDqk, vrs = (size_t)a.Hkv * kDv;
+    const int Hkv = a.Hkv;
+    // transpose loads: this lane addresses key row 8 (lane / 32) + (lane % 16) / 4 and
+    // the 4 dims from 16 ((lane / 16) % 2) + 4 (lane % 4) of a 32-dim block
+    const int trow = 8 * h2 + ((lane & 15) >> 2), tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-    // the next tile's K / V rows are loaded into registers while this one is computed
-    auto load_tile = [&](StageRegs &st, int j0) {
-        stage_load(st, a.k + ((size_t)b * a.T + j0) * krs + (size_t)g * kDqk, krs,
-                   a.v + ((size_t)b * a.T + j0) * vrs + (size_t)g * kDv, vrs, min(32, a.T - j0), tid);
+    auto copy_tile = [&](int j0, int buf) {
+        const int last = min(32, a.T - j0) - 1;
+        const unsigned char *dst = tiles[buf];
+        const size_t trow0 = ((size_t)b * a.T + j0) * Hkv + g;
+#pragma unroll
+        for (int m = 0; m < (kTileCopies + NW - 1) / NW; ++m) {
+            const int id = w + NW * m;   // wave-uniform
+            if (id < kRotCopies) {
+                const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+                    a.krot + (((size_t)b * Hkv + g) * a.T + j0) * kRope, 0, (last + 1) * 128, kRsrcFlags);
+                lds_copy(rs, dst + kKaOff + 1024 * id, 16, rot_voff(id, lane, last));
+            } else if (id < kRotCopies + kRowCopies) {
+                const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.k + trow0 * kDqk), 0,
+                                                                  last * Hkv * 384 + 384, kRsrcFlags);
+                const int k = id - kRotCopies;
+                lds_copy(rs, dst + kKbOff + 1024 * k, 16, row_voff(k, lane, last, Hkv * 384) + 128);
+            } else if (id < kTileCopies) {
+                const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.v + trow0 * kDv), 0,
+                                                                  last * Hkv * 256 + 256, kRsrcFlags);
+                const int k = id - kRotCopies - kRowCopies;
+                lds_copy(rs, dst + kVOff + 1024 * k, 16, row_voff(k, lane, last, Hkv * 256));
+            }
+        }
     };
+
     const int j_first = (jlo / 32) * 32;
-    StageRegs st;
-    load_tile(st, j_first);
+    copy_tile(j_first, 0);
+    // Q~ is complete here (its loads are older than the copies): no wait of the
+    // compiler's for it inside the loop, where copies would be in flight
+    asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]),
+                 "v"(qf[7]), "v"(qf[8]), "v"(qf[9]), "v"(qf[10]), "v"(qf[11]));
+    __syncthreads();   // also waits for this wave's copies
+    int buf = 0;
     for (int j0 = j_first; j0 <= jhi; j0 += 32) {
-        __syncthreads();   // the previous tile's reads are done
-        stage_store(st, Ks, Vs, a.pos0 + j0, a.rt, tid);
-        if (j0 + 32 <= jhi) load_tile(st, j0 + 32);
-        __syncthreads();
-        transpose32(KTs, Ks, RSTR, kDqk / 8, tid, 64 * NW);
-        __syncthreads();
+        // the next tile goes to the other buffer, last read before the previous barrier
+        if (j0 + 32 <= jhi) copy_tile(j0 + 32, buf ^ 1);
+        const uint16_t *Ka = reinterpret_cast<const uint16_t *>(tiles[buf] + kKaOff);
+        const uint16_t *Kb = reinterpret_cast<const uint16_t *>(tiles[buf] + kKbOff);
+        const uint16_t *Vs = reinterpret_cast<const uint16_t *>(tiles[buf] + kVOff);
 
         f32x16 S, DP;
 #pragma unroll
@@ -259,10 +291,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
             S[e] = 0.0f;
             DP[e] = 0.0f;
         }
+        // S^T: chunk s of this lane is dims 96 h2 + 8 s .. + 7 of key row prow
+        const uint16_t *klo = h2 ? Kb + prow * kRowStr + 32 : Ka + prow * kRotStr;        // s < 8
+        const uint16_t *khi = h2 ? Kb + prow * kRowStr + 32 : Kb + prow * kRowStr - 64;   // s >= 8
 #pragma unroll
-        for (int s = 0; s < 12; ++s) S = mfma32(lds128(Ks + prow * RSTR + 96 * h2 + 8 * s), qf[s], S);
+        for (int s = 0; s < 12; ++s) S = mfma32(lds128((s < 8 ? klo : khi) + 8 * s), qf[s], S);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) DP = mfma32(lds128(Vs + prow * VSTR + 64 * h2 + 8 * s), lds128(dos + 8 * s), DP);
+        for (int s = 0; s < 8; ++s)
+            DP = mfma32(lds128(Vs + prow * kRowStr + 64 * h2 + 8 * s), lds128(dos + 8 * ((8 * h2 + s) ^ (l32 & 15))), DP);
 
         // element e: key j0 + 16*(e>>3) + 8*h2 + (e&7), query t.  A tile whose every
         // key every query of the block sees needs no mask; otherwise, less j0 + 8 h2,
@@ -295,12 +331,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 #pragma unroll
             for (int x = 0; x < 4; ++x) dsb[s][x] = pack_bf16(v8[2 * x], v8[2 * x + 1]);
         }
-        // dQ~^T (192 x 32 queries) += K~^T (192 x 32 keys) dS^T
+        // dQ~^T (192 x 32 queries) += K~^T (192 x 32 keys) dS^T; A operand of block
+        // (mb, s): dims 32 mb + l32, keys 16 s + 8 h2 .. + 7 (transpose loads)
 #pragma unroll
         for (int mb = 0; mb < 6; ++mb)
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
-                acc[mb] = mfma32(lds128(KTs + (32 * mb + l32) * TSTR + 16 * s + 8 * h2), dsb[s], acc[mb]);
+            for (int s = 0; s < 2; ++s) {
+                const u32x4 kt = mb < 2 ? lds_tr8(Ka + (16 * s + trow) * kRotStr + 32 * mb + tcol, kRotStr)
+                                        : lds_tr8(Kb + (16 * s + trow) * kRowStr + 32 * (mb - 2) + tcol, kRowStr);
+                acc[mb] = mfma32(kt, dsb[s], acc[mb]);
+            }
+        __syncthreads();   // this tile's reads are done; also waits for this wave's copies of the next
+        buf ^= 1;
     }
 
     // ---- epilogue: acc[mb][e] holds dim 32*mb + 8*(e/4) + 4*h2 + (e%4) of query t
@@ -350,34 +392,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 // 64..191 rows of 272, dO rows of 272, L and D 32 floats each; each region is
 // whole 1 KiB copies (16 bytes per lane; lanes past the region's rows re-read
 // the last row into slack).
-namespace {
-constexpr int kQaStr = 72, kQbStr = 136, kObStr = 136;   // row strides (elements)
-constexpr int kQaOff = 0, kQbOff = 5120, kObOff = 14336, kLOff = 23552, kDOff = 23808;   // bytes
-constexpr int kStageBytes = 24064;
-constexpr int kQaCopies = 5, kQbCopies = 9, kObCopies = 9;
-constexpr int kStageCopies = kQaCopies + kQbCopies + kObCopies + 2;   // + L, D (4 bytes per lane)
-constexpr uint32_t kRsrcFlags = 0x00020000u;
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-__device__ __forceinline__ void lds_copy(__amdgpu_buffer_rsrc_t rsrc, const unsigned char *lds_dst, int bytes,
-                                         int voffset) {
-    auto *d = (__attribute__((address_space(3))) void *)(const_cast<unsigned char *>(lds_dst));
-    if (bytes == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, d, 16, voffset, 0, 0, 0);
-    else __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, d, 4, voffset, 0, 0, 0);
-}
-
-// 8 consecutive rows (queries) x this lane's column of a row-major bf16 stage, as
-// one MFMA operand: two transpose loads, rows row0 .. row0 + 3 and row0 + 4 .. + 7
-// of the lane group.  p0 is this lane's address for the first four rows.
-__device__ __forceinline__ u32x4 lds_tr8(const uint16_t *p0, int str) {
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(const_cast<uint16_t *>(p0)));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(const_cast<uint16_t *>(p0 + 4 * str)));
-    const u32x2 a = __builtin_bit_cast(u32x2, lo), c = __builtin_bit_cast(u32x2, hi);
-    return u32x4{a[0], a[1], c[0], c[1]};
-}
-}  // namespace
 
 template <int NWV>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NWV, 64 * NWV), amdgpu_waves_per_eu(2, 2)))
@@ -446,21 +460,19 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int m = 0; m < (kStageCopies + NWV - 1) / NWV; ++m) {
             const int id = w + NWV * m;   // wave-uniform
-            if (id < kQaCopies) {
-                const int c = 64 * id + lane, row = c / 9, piece = c - 9 * row;
+            if (id < kRotCopies) {
                 const auto rs = __builtin_amdgcn_make_buffer_rsrc(a.qrot + hrow * kRope, 0, (last + 1) * 128, kRsrcFlags);
-                lds_copy(rs, dst + kQaOff + 1024 * id, 16, min(row, last) * 128 + 16 * min(piece, 7));
-            } else if (id < kQaCopies + kQbCopies) {
-                const int c = 64 * (id - kQaCopies) + lane, row = c / 17, piece = c - 17 * row;
+                lds_copy(rs, dst + kQaOff + 1024 * id, 16, rot_voff(id, lane, last));
+            } else if (id < kRotCopies + kRowCopies) {
                 const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.q + trow0 * kDqk), 0,
                                                                   last * Hq * 384 + 384, kRsrcFlags);
-                lds_copy(rs, dst + kQbOff + 1024 * (id - kQaCopies), 16, min(row, last) * Hq * 384 + 128 + 16 * min(piece, 15));
-            } else if (id < kQaCopies + kQbCopies + kObCopies) {
-                const int c = 64 * (id - kQaCopies - kQbCopies) + lane, row = c / 17, piece = c - 17 * row;
+                const int k = id - kRotCopies;
+                lds_copy(rs, dst + kQbOff + 1024 * k, 16, row_voff(k, lane, last, Hq * 384) + 128);
+            } else if (id < kRotCopies + 2 * kRowCopies) {
                 const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.dout + trow0 * kDv), 0,
                                                                   last * Hq * 256 + 256, kRsrcFlags);
-                lds_copy(rs, dst + kObOff + 1024 * (id - kQaCopies - kQbCopies), 16,
-                         min(row, last) * Hq * 256 + 16 * min(piece, 15));
+                const int k = id - kRotCopies - kRowCopies;
+                lds_copy(rs, dst + kObOff + 1024 * k, 16, row_voff(k, lane, last, Hq * 256));
             } else if (id < kStageCopies) {
                 const bool isL = id == kStageCopies - 2;
                 const float *src = isL ? a.lse + hrow : a.D + hrow;
@@ -498,8 +510,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
                     const int u = i < 12 ? i : i - 12;
                     const int qb = i < 12 ? u / 6 : u / 4, c = i < 12 ? u % 6 : u % 4;
                     const int row = prow0 + 4 * qb;
-                    return i < 12 ? (c < 2 ? Qa + row * kQaStr + 32 * c : Qb + row * kQbStr + 32 * (c - 2)) + 8 * g4
-                                  : Ob + row * kObStr + 32 * c + 8 * g4;
+                    return i < 12 ? (c < 2 ? Qa + row * kRotStr + 32 * c : Qb + row * kRowStr + 32 * (c - 2)) + 8 * g4
+                                  : Ob + row * kRowStr + 32 * c + 8 * g4;
                 };
                 auto order = [](int i) { return i < 16 ? ((i & 1) ? 12 + (i >> 1) : (i >> 1)) : i - 8; };
                 u32x4 fr[RS];
@@ -575,10 +587,10 @@ void bwd_dkdv_kernel(BwdArgs a) {
             {
                 constexpr int RD = 8;
                 auto fload = [&](int i) {   // i < 8: dV block i; else dK block i - 8
-                    if (i < 8) return lds_tr8(Ob + trow * kObStr + 16 * i + tcol, kObStr);
+                    if (i < 8) return lds_tr8(Ob + trow * kRowStr + 16 * i + tcol, kRowStr);
                     const int mb = i - 8;
-                    return mb < 4 ? lds_tr8(Qa + trow * kQaStr + 16 * mb + tcol, kQaStr)
-                                  : lds_tr8(Qb + trow * kQbStr + 16 * (mb - 4) + tcol, kQbStr);
+                    return mb < 4 ? lds_tr8(Qa + trow * kRotStr + 16 * mb + tcol, kRotStr)
+                                  : lds_tr8(Qb + trow * kRowStr + 16 * (mb - 4) + tcol, kRowStr);
                 };
                 u32x4 fr[RD];
 #pragma unroll
@@ -634,9 +646,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
 }
 
-size_t backward_workspace_bytes(int32_t B, int32_t T, int32_t Hq) {
-    const size_t rows = (size_t)B * T * Hq;
-    return rows * kRope * sizeof(uint16_t) + (rows + (size_t)B * ((T + 31) / 32) * Hq) * sizeof(float);
+size_t backward_workspace_bytes(int32_t B, int32_t T, int32_t Hq, int32_t Hkv) {
+    const size_t rows = (size_t)B * T * Hq, krows = (size_t)B * T * Hkv;
+    return (rows + krows) * kRope * sizeof(uint16_t) + (rows + (size_t)B * ((T + 31) / 32) * Hq) * sizeof(float);
 }
 
 hipError_t launch_backward(BwdArgs a, hipStream_t stream) {
@@ -646,10 +658,14 @@ hipError_t launch_backward(BwdArgs a, hipStream_t stream) {
     a.n_hgrp = G / 4;
     constexpr int kDkdvWaves = 4;
     a.n_kblk = (a.T + 16 * kDkdvWaves - 1) / (16 * kDkdvWaves);
+    const int64_t krot_threads = (int64_t)a.B * a.T * a.Hkv * 4;
+    hipLaunchKernelGGL(bwd_krot_kernel, dim3((unsigned)((krot_threads + 255) / 256)), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     // dq also forms D and the sink partials; d sink and dk/dv read them
     const int64_t qblocks = (int64_t)a.B * a.Hkv * a.n_hgrp * a.n_qblk;
     hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)qblocks), dim3(256), 0, stream, a);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.sinks) {
         hipLaunchKernelGGL(bwd_sink_kernel, dim3(a.Hq), dim3(256), 0, stream, a);

@@ -68,6 +68,7 @@ struct BwdArgs {
     const float *lse;                         // [B, Hq, T] natural-log LSE of the forward
     const float *sinks;                       // nullable
     uint16_t *qrot;                           // workspace [B, Hq, T, 64]: the rotated dims of Q~ (bf16)
+    uint16_t *krot;                           // workspace [B, Hkv, T, 64]: the rotated dims of K~ (bf16)
     float *D;                                 // workspace [B, Hq, T]: rowsum(dO o O)
     float *csink;                             // workspace [B * 32-query blocks, Hq]: sink-term partials
     uint16_t *dq, *dk, *dv;
@@ -78,7 +79,7 @@ struct BwdArgs {
     RopeTurns rt;
     int32_t n_qblk, n_hgrp, n_kblk;           // filled by the launcher
 };
-size_t backward_workspace_bytes(int32_t B, int32_t T, int32_t Hq);
+size_t backward_workspace_bytes(int32_t B, int32_t T, int32_t Hq, int32_t Hkv);
 hipError_t launch_backward(BwdArgs a, hipStream_t stream);
 
 // ---- decode (decode.hip)

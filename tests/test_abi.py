@@ -295,8 +295,10 @@ def test_backward_contract(lib):
     assert bwd(lib, c, ws=None, ws_bytes=0) == WS
     need = lib.mimo_attn_backward_workspace_size(ctypes.byref(c), 2, 64)
     rows = 2 * 64 * 64                          # (token, query head) pairs
-    # per pair the 64 rotated q dims (bf16) and D; sink partials per (batch row, 32-token block, head)
-    assert need == rows * 64 * 2 + (rows + 2 * 2 * 64) * 4
+    # per pair the 64 rotated q dims (bf16) and D; per (token, KV head) the 64 rotated k dims;
+    # sink partials per (batch row, 32-token block, head)
+    krows = 2 * 64 * c.num_kv_heads
+    assert need == (rows + krows) * 64 * 2 + (rows + 2 * 2 * 64) * 4
     assert bwd(lib, c, ws_bytes=need - 1) == WS
     assert bwd(lib, cfg_swa(num_q_heads=16, num_kv_heads=8)) == UNSUP    # group of 2
     assert bwd(lib, c, T=0, lse=None) == OK
