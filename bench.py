@@ -17,7 +17,8 @@ figures: the on-box peaks (a bf16 MFMA loop on N(0,1) operands and on ones, a
 1 GiB HBM copy and read; `peaks`), the sliding-window prefill B=1 x T=512 with
 the Infinity Cache flushed before each call, and the 524288-token global
 prefill in 8 query chunks of 65536 (one warmup and two timed passes, with its
-own roofline object; --no-long skips it).  Every kernel figure is given as a
+own roofline object; --no-long skips it), and the sliding-window + sink backward
+of the B=4 x T=8192 prefill (--no-backward skips it).  Every kernel figure is given as a
 fraction of the vendor peaks (2.5 PFLOP/s bf16, 8 TB/s) and of the measured ones.
 
 --workload long_prefill instead times the 524288-token global prefill run as 8
@@ -436,6 +437,8 @@ def main():
                     help="skip the on-box peak loops (profiling passes); fractions of them are then omitted")
     ap.add_argument("--no-long", action="store_true",
                     help="skip the 524288-token prefill phase of the default run")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward phase of the default run")
     ap.add_argument("--cpu-budget", type=float, default=40.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run three 1 GiB device-to-device copies (a known-size reference "
@@ -553,6 +556,9 @@ def main():
     if not args.no_long:
         log("long global prefill T=524288 in 8 chunks of 65536")
         phases["global_prefill_t524288_8chunks"] = bench_long_prefill(torch, gen, Bd, peaks)
+    if not args.no_backward:
+        log("sliding-window + sink backward B=4 T=8192")
+        phases["swa_backward_b4_t8192"] = bench_backward(torch, gen, Bd, 2, 10, src=ph["swa_prefill"])
 
     achieved = tf(g["flops"], ms["global_prefill"])
     roofline = {"bound": "mfma", "kernel": "prefill_image_kernel (global causal, T=32768; its K/V image pass "
@@ -817,14 +823,20 @@ def main_paged_decode(args, torch, gen, Bd):
     print(json.dumps(out_j))
 
 
-def main_backward(args, torch, gen, Bd):
+def bench_backward(torch, gen, Bd, warmup, steps, src=None):
+    """The sliding-window + sink backward at B=4, T=8192 (one call = k rotation, dq, d sink, dk/dv),
+    timed with events on the current stream.  src: the layer step's sliding-prefill inputs on the
+    device (the same seeded draw), reused when given."""
     B, T = 4, 8192
-    log("setup: sliding-window prefill B=4 T=8192, forward once for its output and LSE")
-    d = gen.prefill_inputs(B, T, 64, 8, seed=1001, with_sinks=True)
     cfg = Bd.swa_cfg()
-    q, k, v = _dev_bf16(torch, d["q"]), _dev_bf16(torch, d["k"]), _dev_bf16(torch, d["v"])
-    sinks = torch.from_numpy(d["sinks"]).to("cuda")
-    del d
+    if src is None:
+        log("setup: sliding-window prefill B=4 T=8192, forward once for its output and LSE")
+        d = gen.prefill_inputs(B, T, 64, 8, seed=1001, with_sinks=True)
+        q, k, v = _dev_bf16(torch, d["q"]), _dev_bf16(torch, d["k"]), _dev_bf16(torch, d["v"])
+        sinks = torch.from_numpy(d["sinks"]).to("cuda")
+        del d
+    else:
+        q, k, v, sinks = src["q"], src["k"], src["v"], src["sinks"]
     dout = _dev_bf16(torch, gen.normal_bf16(np.random.SeedSequence(1012), (B, T, 64, 128)))
     out = torch.empty((B, T, 64, 128), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, 64, T), dtype=torch.float32, device="cuda")
@@ -836,19 +848,18 @@ def main_backward(args, torch, gen, Bd):
     def step():
         Bd.mimo_attn_prefill_backward(cfg, q, k, v, sinks, out, lse, dout, dq, dk, dv, dsinks, ws=ws)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     s_ev.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     e_ev.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    ms_ev = s_ev.elapsed_time(e_ev) / args.steps
+    ms_ev = s_ev.elapsed_time(e_ev) / steps
     pairs = B * swa_pairs(T, 128)
     # one recompute of S, then dP, dV, dK, dQ: 2 * (3 * 192 + 2 * 128) FLOP per visible pair and head
     flops = 2 * (3 * 192 + 2 * 128) * 64 * pairs
@@ -857,16 +868,25 @@ def main_backward(args, torch, gen, Bd):
     nbytes = B * T * (64 * (192 + 128 + 128 + 192) * 2 + 8 * (192 + 128) * 2 * 2) + B * 64 * T * 4
     tflops = flops / (ms_ev * 1e-3) / 1e12
     gbs = nbytes / (ms_ev * 1e-3) / 1e9
-    out_j = {"metric": METRIC, "value": flops / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
-             "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-             "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+    return {"ms": ms_ev, "ms_wall": wall * 1e3 / steps, "tflops": tflops, "gbs": gbs,
+            "frac_hbm_peak": gbs / PEAK_HBM_GBS, "frac_mfma_peak": tflops / PEAK_BF16_TFLOPS,
+            "algorithmic_flops": flops, "algorithmic_bytes": nbytes}
+
+
+def main_backward(args, torch, gen, Bd):
+    r = bench_backward(torch, gen, Bd, args.warmup, args.steps)
+    ms_step = r["ms_wall"]
+    out_j = {"metric": METRIC, "value": r["algorithmic_flops"] / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s",
+             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
              "data": "synthetic: seeded N(0,1) bf16 q/k/v/dO, N(0,1) fp32 sinks",
              "config": {"workload": "swa_backward_b4_t8192 (dq, dk, dv, d sink from the forward's output and LSE)"},
-             "roofline": {"bound": "hbm", "kernel": "bwd_dq + bwd_sink + bwd_dkdv (one call)",
-                          "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-                          "traffic": None, "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
-                          "tflops": tflops, "frac_mfma_peak": tflops / PEAK_BF16_TFLOPS},
-             "cpu_baseline": None, "ms_per_call_events": ms_ev}
+             "roofline": {"bound": "hbm", "kernel": "bwd_krot + bwd_dq + bwd_sink + bwd_dkdv (one call)",
+                          "achieved": r["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": r["frac_hbm_peak"],
+                          "traffic": None, "algorithmic_flops": r["algorithmic_flops"],
+                          "algorithmic_bytes": r["algorithmic_bytes"], "tflops": r["tflops"],
+                          "frac_mfma_peak": r["frac_mfma_peak"]},
+             "cpu_baseline": None, "ms_per_call_events": r["ms"]}
     print(json.dumps(out_j))
 
 
