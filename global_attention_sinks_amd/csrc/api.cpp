@@ -9,6 +9,8 @@
 #include "../../include/mimo_attn.h"
 #include "kernels.hpp"
 
+#include <initializer_list>
+
 using namespace mimo;
 
 namespace {
@@ -31,6 +33,16 @@ mimo_status ok() {
 mimo_status from_hip(hipError_t e, const char *what) {
     if (e == hipSuccess) return ok();
     return fail(MIMO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// The kernels move bf16 and fp8 rows and workspaces in 16-byte pieces (vector loads,
+// and buffer loads that write LDS): every such pointer must be 16-byte aligned.
+// NULL pointers pass (their own checks report them).
+mimo_status check_aligned(const char *names, std::initializer_list<const void *> ptrs) {
+    for (const void *p : ptrs)
+        if (p && (reinterpret_cast<uintptr_t>(p) & 15u) != 0)
+            return fail(MIMO_ERR_INVALID_ARGUMENT, "%s must be 16-byte aligned", names);
+    return MIMO_OK;
 }
 
 // Shared checks of the layer configuration.
@@ -91,6 +103,7 @@ mimo_status mimo_rope_partial(const mimo_attn_cfg *cfg, const uint16_t *x_in, ui
         return fail(MIMO_ERR_INVALID_ARGUMENT, "n_tokens must be >= 0 and n_heads > 0");
     if (n_tokens == 0) return ok();
     if (!x_in || !x_out || !pos) return fail(MIMO_ERR_INVALID_ARGUMENT, "x_in, x_out and pos must be non-NULL");
+    if (check_aligned("x_in and x_out", {x_in, x_out}) != MIMO_OK) return MIMO_ERR_INVALID_ARGUMENT;
     const size_t bytes = (size_t)n_tokens * n_heads * kDqk * 2;
     if (x_in != x_out && overlap(x_in, bytes, x_out, bytes))
         return fail(MIMO_ERR_INVALID_ARGUMENT, "x_out must equal x_in or not overlap it");
@@ -111,6 +124,7 @@ static mimo_status prefill_common(const mimo_attn_cfg *cfg, const uint16_t *q, c
                     cfg->num_q_heads / cfg->num_kv_heads);
     if (B == 0 || Tq == 0) return ok();
     if (!q || !k || !v || !out) return fail(MIMO_ERR_INVALID_ARGUMENT, "q, k, v and out must be non-NULL");
+    if (check_aligned("q, k, v and out", {q, k, v, out}) != MIMO_OK) return MIMO_ERR_INVALID_ARGUMENT;
     return ok();
 }
 
@@ -148,6 +162,7 @@ static mimo_status attach_images(PrefillArgs &a, const mimo_attn_cfg *cfg, int32
                                  void *ws, size_t ws_bytes) {
     const size_t need = image_bytes(cfg, B, total_k);
     if (!ws || need == 0) return ok();
+    if (check_aligned("ws", {ws}) != MIMO_OK) return MIMO_ERR_INVALID_ARGUMENT;
     if (ws_bytes < need)
         return fail(MIMO_ERR_WORKSPACE, "prefill workspace needs %zu bytes (got %zu)", need, ws_bytes);
     a.kv_img = static_cast<uint16_t *>(ws);
@@ -197,6 +212,7 @@ mimo_status mimo_attn_prefill_varlen(const mimo_attn_cfg *cfg, const uint16_t *q
     if (B == 0 || max_seqlen_q == 0) return ok();
     if (!q || !k || !v || !out || !cu_seqlens_q || !cu_seqlens_k)
         return fail(MIMO_ERR_INVALID_ARGUMENT, "q, k, v, out, cu_seqlens_q and cu_seqlens_k must be non-NULL");
+    if (check_aligned("q, k, v and out", {q, k, v, out}) != MIMO_OK) return MIMO_ERR_INVALID_ARGUMENT;
     PrefillArgs a{};
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.sinks = sinks;
     a.B = B; a.Tq = max_seqlen_q; a.Hq = cfg->num_q_heads; a.Hkv = cfg->num_kv_heads;
@@ -236,6 +252,8 @@ mimo_status mimo_attn_prefill_backward(const mimo_attn_cfg *cfg, const uint16_t 
     if (!out || !lse || !dout || !dk || !dv)
         return fail(MIMO_ERR_INVALID_ARGUMENT, "out, lse, dout, dq, dk and dv must be non-NULL");
     if (sinks && !dsinks) return fail(MIMO_ERR_INVALID_ARGUMENT, "dsinks must be non-NULL when sinks are given");
+    if (check_aligned("out, dout, dq, dk, dv and ws", {out, dout, dq, dk, dv, ws}) != MIMO_OK)
+        return MIMO_ERR_INVALID_ARGUMENT;
     const size_t need = backward_workspace_bytes(B, T, cfg->num_q_heads, cfg->num_kv_heads);
     if (!ws || ws_bytes < need)
         return fail(MIMO_ERR_WORKSPACE, "backward workspace needs %zu bytes (got %zu)", need,
@@ -278,6 +296,8 @@ static mimo_status decode_prepare(const mimo_attn_cfg *cfg, int32_t S, int32_t n
     if (S == 0) return ok();
     if (!q || !q_pos || !k_cache || !v_cache || !out)
         return fail(MIMO_ERR_INVALID_ARGUMENT, "q, q_pos, the caches and out must be non-NULL");
+    if (check_aligned("q, the caches and out", {q, k_cache, v_cache, out}) != MIMO_OK)
+        return MIMO_ERR_INVALID_ARGUMENT;
     a = DecodeArgs{};
     a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.pos = q_pos; a.sinks = sinks; a.out = out;
     a.S = S; a.Hq = cfg->num_q_heads; a.Hkv = cfg->num_kv_heads; a.cap = cap; a.window = cfg->window;
@@ -304,6 +324,7 @@ static mimo_status decode_common(const mimo_attn_cfg *cfg, int32_t S, int32_t n_
     if (!ws || ws_bytes < need)
         return fail(MIMO_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu)", need,
                     ws ? ws_bytes : (size_t)0);
+    if (check_aligned("ws", {ws}) != MIMO_OK) return MIMO_ERR_INVALID_ARGUMENT;
     a.ws_o = (float *)ws;
     return from_hip(launch_decode(a, (hipStream_t)stream), "decode launch");
 }
@@ -421,6 +442,8 @@ mimo_status mimo_kv_paged_append(const mimo_attn_cfg *cfg, int32_t S, const uint
     if (S == 0) return ok();
     if (!k_new || !v_new || !pos || !k_pool || !v_pool || !block_table)
         return fail(MIMO_ERR_INVALID_ARGUMENT, "k_new, v_new, pos, the pools and block_table must be non-NULL");
+    if (check_aligned("k_new, v_new and the pools", {k_new, v_new, k_pool, v_pool}) != MIMO_OK)
+        return MIMO_ERR_INVALID_ARGUMENT;
     PagedAppendArgs a{};
     a.k_new = k_new; a.v_new = v_new; a.pos = pos; a.k_pool = k_pool; a.v_pool = v_pool; a.table = block_table;
     a.S = S; a.Hkv = cfg->num_kv_heads; a.n_blocks = n_blocks; a.block_shift = pl.block_shift;
@@ -440,6 +463,8 @@ mimo_status mimo_kv_ring_append(const mimo_attn_cfg *cfg, int32_t S, const uint1
     if (S == 0) return ok();
     if (!k_new || !v_new || !pos || !k_cache || !v_cache)
         return fail(MIMO_ERR_INVALID_ARGUMENT, "k_new, v_new, pos, k_cache and v_cache must be non-NULL");
+    if (check_aligned("k_new, v_new and the caches", {k_new, v_new, k_cache, v_cache}) != MIMO_OK)
+        return MIMO_ERR_INVALID_ARGUMENT;
     return from_hip(launch_kv_ring_append(rope_turns(cfg->rope_base), S, cfg->num_kv_heads, k_new,
                                           v_new, pos, k_cache, v_cache, cap, (hipStream_t)stream),
                     "kv_ring_append launch");

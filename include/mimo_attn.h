@@ -26,6 +26,11 @@
  *   - Every pointer is a DEVICE pointer owned by the caller, except cfg, which is
  *     a host pointer read during the call only.  The library allocates nothing
  *     and keeps no state between calls.
+ *   - Every bf16 or fp8 tensor and every workspace must be 16-byte aligned (the
+ *     kernels move rows in 16-byte pieces; a tensor PyTorch allocates, and any
+ *     view of it that starts on a token or slot row, is); otherwise the call
+ *     returns MIMO_ERR_INVALID_ARGUMENT.  fp32 and integer arrays need only
+ *     their natural alignment.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Success means the
  *     work is enqueued on that stream; no call synchronises the host, so every
  *     call can be captured into a HIP graph.
@@ -52,7 +57,7 @@ extern "C" {
 
 typedef enum mimo_status {
     MIMO_OK = 0,
-    MIMO_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, inconsistent sizes */
+    MIMO_ERR_INVALID_ARGUMENT = 1, /* null or misaligned pointer, negative size, inconsistent sizes */
     MIMO_ERR_UNSUPPORTED = 2,      /* head geometry the kernels are not built for */
     MIMO_ERR_WORKSPACE = 3,        /* workspace missing or too small */
     MIMO_ERR_HIP = 4               /* the HIP runtime refused a launch */

@@ -319,6 +319,32 @@ def test_rope_and_append_contract(lib):
     assert lib.mimo_kv_ring_append(ctypes.byref(c), 0, None, None, None, None, None, 128, None) == OK
 
 
+ODD = ctypes.c_void_p(0x10008)   # 8-byte aligned, not 16
+
+
+def test_misaligned_pointers_are_rejected(lib):
+    """bf16 / fp8 tensors and workspaces move in 16-byte pieces: a pointer that is not
+    16-byte aligned is an invalid argument, caught on the host before any launch."""
+    calls = {
+        "swa q": lambda: swa(lib, cfg_swa(), q=ODD),
+        "swa out": lambda: swa(lib, cfg_swa(), out=ODD),
+        "global ws": lambda: glob(lib, cfg_glob(), ws=ODD, ws_bytes=1 << 30),
+        "varlen q": lambda: varlen(lib, cfg_swa(), q=ODD),
+        "decode q": lambda: dec(lib, cfg_glob(), q=ODD),
+        "decode ws": lambda: dec(lib, cfg_glob(), ws=ODD),
+        "decode_multi q": lambda: decm(lib, cfg_glob(), q=ODD),
+        "backward ws": lambda: bwd(lib, cfg_swa(), ws=ODD),
+        "rope": lambda: lib.mimo_rope_partial(ctypes.byref(cfg_swa()), ODD, ODD, 4, 8, FAKE, None),
+        "ring append": lambda: lib.mimo_kv_ring_append(ctypes.byref(cfg_swa()), 2, ODD, FAKE, FAKE, FAKE, FAKE,
+                                                       128, None),
+    }
+    for name, call in calls.items():
+        assert call() == INVAL, name
+        assert "16-byte aligned" in err(lib), name
+    # empty work is still valid whatever the pointers
+    assert swa(lib, cfg_swa(), q=ODD, T=0) == OK
+
+
 def test_error_message_cleared_on_success(lib):
     assert swa(lib, cfg_swa(), q=None) == INVAL
     assert err(lib) != ""
