@@ -8,13 +8,15 @@
 // and dq, dk are dQ~, dK~ turned back by the transpose of the partial RoPE
 // rotation (the same angle, negated).
 //
+//   bwd_krot_kernel    writes the rotated dims 0..63 of K~ into the workspace
 //   bwd_dq_kernel      query-major: a workgroup owns 32 queries x 4 heads of a
 //                      GQA group; it forms D per (row, head) from O and dO and
 //                      per head the sum of its rows' sink terms, writes D and
 //                      the rotated dims 0..63 of Q~ for dk/dv, then per 32-key
-//                      tile (K rotated, K^T and V staged in LDS, shared by the 4
-//                      heads) rebuilds S^T and dP^T and accumulates
-//                      dQ~^T = K~^T dS^T in registers
+//                      tile (K~ and V rows copied into LDS by buffer loads that
+//                      write LDS, double-buffered, shared by the 4 heads)
+//                      rebuilds S^T and dP^T and accumulates dQ~^T = K~^T dS^T
+//                      in registers, reading K~^T with LDS transpose loads
 //   bwd_sink_kernel    one workgroup per head sums the sink partials (fixed order)
 //   bwd_dkdv_kernel    key-major: a workgroup owns 64 keys of one KV head (one
 //                      wave per 16 keys, 16x16x32 MFMAs, the keys' K~ and V held
