@@ -79,7 +79,10 @@ def check_grads(got, ref, what, bar=None):
                                                    # dk/dv takes keys 16 to a wave: a window and a
                                                    # length that end inside a wave, a single token
                                                    (1, 17, 7, True, 0), (3, 48, 33, True, 0),
-                                                   (1, 1, 128, True, 3)])
+                                                   (1, 1, 128, True, 3),
+                                                   # long enough for many stages per dk/dv workgroup
+                                                   # and of dq's double-buffered key tiles
+                                                   (2, 2048, 128, True, 4096)])
 def test_backward_sliding(B, T, window, sinks, pos0):
     d = gen.prefill_inputs(B, T, 64, 8, seed=10001 + T, with_sinks=sinks)
     dout = gen.normal_bf16(np.random.SeedSequence(10002 + T), (B, T, 64, 128))
@@ -91,7 +94,8 @@ def test_backward_sliding(B, T, window, sinks, pos0):
     check_grads(got, ref, "sliding", bar)
 
 
-@pytest.mark.parametrize("hq,hkv,T", [(64, 4, 300), (16, 4, 130), (8, 2, 70), (64, 1, 90)])
+@pytest.mark.parametrize("hq,hkv,T", [(64, 4, 300), (16, 4, 130), (8, 2, 70), (64, 1, 90),
+                                      (16, 4, 2048)])   # 64 key tiles per dq block at the end
 def test_backward_global(hq, hkv, T):
     d = gen.prefill_inputs(1, T, hq, hkv, seed=10101 + T, with_sinks=False)
     dout = gen.normal_bf16(np.random.SeedSequence(10102 + T), (1, T, hq, 128))
