@@ -105,6 +105,47 @@ def test_backward_global(hq, hkv, T):
     check_grads(got, ref, "global")
 
 
+def test_backward_window1_without_sink():
+    """Window 1 and no sink: every query sees only its own key, P = 1 and dS = dP - D with
+    D = dP, so the exact dq and dk are zero.  The kernels form D from the forward's stored
+    bf16 output (reading r21), so their dS is that output's rounding carried through
+    <dO, O>: |dS_gpu| <= sum |dO| |O_gpu - o| per (row, head), o the oracle's output.  dq
+    and dk are held element by element to scale * that bound * the norm of the rotated key
+    (query) pair the element mixes with its partner, with 2^-7 for the bf16 rounding of dS
+    and of the result; dv = v_scale dO at the usual bar."""
+    T, pos0, hq, hkv = 324, 63783, 64, 8
+    d = gen.prefill_inputs(1, T, hq, hkv, seed=10301, with_sinks=False)
+    dout = gen.normal_bf16(np.random.SeedSequence(10302), (1, T, hq, 128))
+    cfg = cfg_for(hq, hkv, 1, 1e4)
+    say(f"backward window 1, no sink: T={T} pos0={pos0}")
+    got = run_fwd_bwd(d, dout, cfg, pos0=pos0)
+    ref = oracle.prefill_backward(d["q"], d["k"], d["v"], dout, sinks=None, pos0=pos0, window=1, base=1e4)
+    assert_grad_parity(host_f64(got[2]), ref[2], "window-1 dv")
+    pos = pos0 + np.arange(T, dtype=np.int64)
+    o = oracle.attention(d["q"][0], pos, d["k"][0], pos, d["v"][0], window=1, base=1e4)
+    dO = np.abs(gen.bf16_bits_to_f32(dout[0]).astype(np.float64))
+    ds_bound = np.sum(dO * np.abs(host_f64(got[4][0]) - o), axis=2)          # [T, Hq]
+    qr = oracle.rope_partial(d["q"][0], pos, 1e4)                            # [T, Hq, 192] rotated
+    kr = oracle.rope_partial(d["k"][0], pos, 1e4)                            # [T, Hkv, 192]
+
+    def pair_norm(x):   # per element: |(x_d, x_partner)| for rotated dims, |x_d| past them
+        n = np.abs(x).copy()
+        r = np.sqrt(x[..., :32] ** 2 + x[..., 32:64] ** 2)
+        n[..., :32] = r
+        n[..., 32:64] = r
+        return n
+
+    scale, slack = cfg.softmax_scale, 1.0 + 2.0 ** -7
+    G = hq // hkv
+    allow_dq = slack * scale * ds_bound[:, :, None] * np.repeat(pair_norm(kr), G, axis=1) + 1e-6
+    allow_dk = slack * scale * np.sum((ds_bound[:, :, None] * pair_norm(qr)).reshape(T, hkv, G, 192), axis=2) + 1e-6
+    for name, g, r, allow in (("dq", got[0], ref[0], allow_dq), ("dk", got[1], ref[1], allow_dk)):
+        err = np.abs(host_f64(g)[0] - r[0])
+        assert np.max(np.abs(r)) < 1e-9, name                                 # exactly zero up to fp64 rounding
+        say(f"  {name}: max-abs {err.max():.3e}, worst error / allowed {np.max(err / allow):.3f}")
+        assert np.all(err <= allow), name
+
+
 def test_backward_is_deterministic():
     d = gen.prefill_inputs(1, 256, 64, 8, seed=10201, with_sinks=True)
     dout = gen.normal_bf16(np.random.SeedSequence(10202), (1, 256, 64, 128))
