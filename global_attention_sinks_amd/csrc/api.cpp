@@ -234,7 +234,7 @@ struct PagedLayout {
 };
 
 size_t mimo_attn_backward_workspace_size(const mimo_attn_cfg *cfg, int32_t B, int32_t T) {
-    if (!cfg || B <= 0 || T <= 0 || cfg->num_q_heads <= 0) return 0;
+    if (check_cfg(cfg) != MIMO_OK || B <= 0 || T <= 0) return 0;
     return backward_workspace_bytes(B, T, cfg->num_q_heads, cfg->num_kv_heads);
 }
 

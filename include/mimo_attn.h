@@ -272,7 +272,8 @@ mimo_status mimo_attn_prefill_backward(const mimo_attn_cfg *cfg, const uint16_t 
 
 /* Workspace bytes of mimo_attn_prefill_backward: per (token, query head) the 64 rotated dims
  * of q (bf16) and one fp32 value, per (token, KV head) the 64 rotated dims of k (bf16), and
- * one fp32 value per (batch row, block of 32 tokens, query head). */
+ * one fp32 value per (batch row, block of 32 tokens, query head); 0 for an invalid cfg or
+ * B, T <= 0. */
 size_t mimo_attn_backward_workspace_size(const mimo_attn_cfg *cfg, int32_t B, int32_t T);
 
 /* Element type of a paged KV cache. */

@@ -299,6 +299,9 @@ def test_backward_contract(lib):
     # sink partials per (batch row, 32-token block, head)
     krows = 2 * 64 * c.num_kv_heads
     assert need == (rows + krows) * 64 * 2 + (rows + 2 * 2 * 64) * 4
+    for bad in (cfg_swa(num_kv_heads=0), cfg_swa(num_kv_heads=-8), cfg_swa(num_q_heads=60)):
+        assert lib.mimo_attn_backward_workspace_size(ctypes.byref(bad), 2, 64) == 0
+    assert lib.mimo_attn_backward_workspace_size(ctypes.byref(c), 0, 64) == 0
     assert bwd(lib, c, ws_bytes=need - 1) == WS
     assert bwd(lib, cfg_swa(num_q_heads=16, num_kv_heads=8)) == UNSUP    # group of 2
     assert bwd(lib, c, T=0, lse=None) == OK
