@@ -116,12 +116,28 @@ def _need(t, dtype, name, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
 
 
+def _shape(t, name, *dims):
+    """Every tensor's full shape is checked against the call's sizes, so that no kernel
+    indexes past a tensor the caller made too small."""
+    if t is not None and tuple(t.shape) != dims:
+        raise ValueError(f"{name} must have shape {dims}, got {tuple(t.shape)}")
+
+
+def _ws(ws):
+    if ws is None:
+        return 0
+    if not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("ws must be a contiguous CUDA tensor")
+    return ws.numel() * ws.element_size()
+
+
 def mimo_rope_partial(cfg: MimoAttnCfg, x_in, x_out, pos, stream=None):
     """x_in/x_out [n_tokens, n_heads, 192] bf16 (may be the same tensor), pos [n_tokens] int64."""
     lib = load_library()
     _need(x_in, torch.bfloat16, "x_in", 3); _need(x_out, torch.bfloat16, "x_out", 3)
     _need(pos, torch.int64, "pos", 1)
     n, h, _ = x_in.shape
+    _shape(x_in, "x_in", n, h, 192); _shape(x_out, "x_out", n, h, 192); _shape(pos, "pos", n)
     _check("mimo_rope_partial", lib.mimo_rope_partial(ctypes.byref(cfg), _p(x_in), _p(x_out), n, h,
                                                       _p(pos), _stream(stream)))
     return x_out
@@ -134,6 +150,9 @@ def mimo_attn_prefill_swa(cfg: MimoAttnCfg, q, k, v, sinks, out, pos0: int = 0, 
         _need(t, torch.bfloat16, n, 4)
     _need(sinks, torch.float32, "sinks", 1); _need(lse, torch.float32, "lse", 3)
     B, T = q.shape[:2]
+    Hq, Hkv = cfg.num_q_heads, cfg.num_kv_heads
+    _shape(q, "q", B, T, Hq, 192); _shape(k, "k", B, T, Hkv, 192); _shape(v, "v", B, T, Hkv, 128)
+    _shape(out, "out", B, T, Hq, 128); _shape(sinks, "sinks", Hq); _shape(lse, "lse", B, Hq, T)
     _check("mimo_attn_prefill_swa",
            lib.mimo_attn_prefill_swa(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(sinks), B, T, pos0,
                                      _p(out), _p(lse), _stream(stream)))
@@ -154,7 +173,7 @@ def _prefill_ws(cfg, B, total_k, ws, device):
         if n == 0:
             return None, 0
         ws = torch.empty(n, dtype=torch.uint8, device=device)
-    return ws, ws.numel() * ws.element_size()
+    return ws, _ws(ws)
 
 
 def mimo_attn_prefill_global(cfg: MimoAttnCfg, q, k, v, out, q_pos0: int = 0, lse=None, ws=None, stream=None):
@@ -165,6 +184,9 @@ def mimo_attn_prefill_global(cfg: MimoAttnCfg, q, k, v, out, q_pos0: int = 0, ls
     _need(lse, torch.float32, "lse", 3)
     B, Tq = q.shape[:2]
     Tk = k.shape[1]
+    Hq, Hkv = cfg.num_q_heads, cfg.num_kv_heads
+    _shape(q, "q", B, Tq, Hq, 192); _shape(k, "k", B, Tk, Hkv, 192); _shape(v, "v", B, Tk, Hkv, 128)
+    _shape(out, "out", B, Tq, Hq, 128); _shape(lse, "lse", B, Hq, Tq)
     ws, ws_bytes = _prefill_ws(cfg, B, B * Tk, ws, q.device)
     _check("mimo_attn_prefill_global",
            lib.mimo_attn_prefill_global(ctypes.byref(cfg), _p(q), _p(k), _p(v), B, Tq, Tk, q_pos0,
@@ -183,6 +205,10 @@ def mimo_attn_prefill_varlen(cfg: MimoAttnCfg, q, k, v, sinks, cu_seqlens_q, cu_
     _need(k_pos0, torch.int64, "k_pos0", 1); _need(sinks, torch.float32, "sinks", 1)
     _need(lse, torch.float32, "lse", 2)
     B = cu_seqlens_q.shape[0] - 1
+    Hq, Hkv, tq, tk = cfg.num_q_heads, cfg.num_kv_heads, q.shape[0], k.shape[0]
+    _shape(q, "q", tq, Hq, 192); _shape(k, "k", tk, Hkv, 192); _shape(v, "v", tk, Hkv, 128)
+    _shape(out, "out", tq, Hq, 128); _shape(cu_seqlens_k, "cu_seqlens_k", B + 1); _shape(k_pos0, "k_pos0", B)
+    _shape(sinks, "sinks", Hq); _shape(lse, "lse", Hq, tq)
     ws, ws_bytes = _prefill_ws(cfg, B, k.shape[0], ws, q.device)
     _check("mimo_attn_prefill_varlen",
            lib.mimo_attn_prefill_varlen(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(sinks), B, _p(cu_seqlens_q),
@@ -206,14 +232,28 @@ def mimo_attn_prefill_backward(cfg: MimoAttnCfg, q, k, v, sinks, out, lse, dout,
     _need(lse, torch.float32, "lse", 3); _need(sinks, torch.float32, "sinks", 1)
     _need(dsinks, torch.float32, "dsinks", 1)
     B, T = q.shape[:2]
+    Hq, Hkv = cfg.num_q_heads, cfg.num_kv_heads
+    for t, n, h, d in ((q, "q", Hq, 192), (k, "k", Hkv, 192), (v, "v", Hkv, 128), (out, "out", Hq, 128),
+                       (dout, "dout", Hq, 128), (dq, "dq", Hq, 192), (dk, "dk", Hkv, 192), (dv, "dv", Hkv, 128)):
+        _shape(t, n, B, T, h, d)
+    _shape(lse, "lse", B, Hq, T); _shape(sinks, "sinks", Hq); _shape(dsinks, "dsinks", Hq)
     if ws is None:
         ws = torch.empty(max(1, mimo_attn_backward_workspace_size(cfg, B, T)), dtype=torch.uint8, device=q.device)
-    ws_bytes = ws.numel() * ws.element_size()
+    ws_bytes = _ws(ws)
     _check("mimo_attn_prefill_backward",
            lib.mimo_attn_prefill_backward(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(sinks), B, T, pos0, _p(out),
                                           _p(lse), _p(dout), _p(dq), _p(dk), _p(dv), _p(dsinks), _p(ws), ws_bytes,
                                           _stream(stream)))
     return dq, dk, dv, dsinks
+
+
+def _decode_shapes(cfg, S, n_q, cap, q, q_pos, k_cache, v_cache, sinks, out):
+    """Shapes of a decode over per-sequence caches (n_q None: one query per sequence)."""
+    Hq, Hkv = cfg.num_q_heads, cfg.num_kv_heads
+    lead = (S,) if n_q is None else (S, n_q)
+    _shape(q, "q", *lead, Hq, 192); _shape(out, "out", *lead, Hq, 128); _shape(q_pos, "q_pos", S)
+    _shape(k_cache, "k_cache", S, cap, Hkv, 192); _shape(v_cache, "v_cache", S, cap, Hkv, 128)
+    _shape(sinks, "sinks", Hq)
 
 
 def mimo_attn_decode_workspace_size(cfg: MimoAttnCfg, S: int, cap: int) -> int:
@@ -230,7 +270,8 @@ def mimo_attn_decode(cfg: MimoAttnCfg, q, q_pos, k_cache, v_cache, sinks, out, w
     _need(q_pos, torch.int64, "q_pos", 1); _need(sinks, torch.float32, "sinks", 1)
     S = q.shape[0]
     cap = k_cache.shape[1]
-    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _decode_shapes(cfg, S, None, cap, q, q_pos, k_cache, v_cache, sinks, out)
+    ws_bytes = _ws(ws)
     _check("mimo_attn_decode",
            lib.mimo_attn_decode(ctypes.byref(cfg), S, _p(q), _p(q_pos), _p(k_cache), _p(v_cache), cap,
                                 _p(sinks), _p(out), _p(ws), ws_bytes, _stream(stream)))
@@ -246,6 +287,7 @@ def mimo_attn_decode_noalloc(cfg: MimoAttnCfg, q, q_pos, k_cache, v_cache, sinks
     _need(q_pos, torch.int64, "q_pos", 1); _need(sinks, torch.float32, "sinks", 1)
     S = q.shape[0]
     cap = k_cache.shape[1]
+    _decode_shapes(cfg, S, None, cap, q, q_pos, k_cache, v_cache, sinks, out)
     _check("mimo_attn_decode_noalloc",
            lib.mimo_attn_decode_noalloc(ctypes.byref(cfg), S, _p(q), _p(q_pos), _p(k_cache), _p(v_cache), cap,
                                         _p(sinks), _p(out), _stream(stream)))
@@ -264,7 +306,8 @@ def mimo_attn_decode_multi(cfg: MimoAttnCfg, q, q_pos, k_cache, v_cache, sinks, 
     _need(q_pos, torch.int64, "q_pos", 1); _need(sinks, torch.float32, "sinks", 1)
     S, n_q = q.shape[:2]
     cap = k_cache.shape[1]
-    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _decode_shapes(cfg, S, n_q, cap, q, q_pos, k_cache, v_cache, sinks, out)
+    ws_bytes = _ws(ws)
     _check("mimo_attn_decode_multi",
            lib.mimo_attn_decode_multi(ctypes.byref(cfg), S, n_q, _p(q), _p(q_pos), _p(k_cache), _p(v_cache), cap,
                                       _p(sinks), _p(out), _p(ws), ws_bytes, _stream(stream)))
@@ -294,7 +337,11 @@ def mimo_attn_decode_paged(cfg: MimoAttnCfg, q, q_pos, k_pool, v_pool, block_tab
         raise ValueError("k_pool and v_pool must have the same element type")
     S, n_q = q.shape[:2]
     n_blocks, block_size = k_pool.shape[:2]
-    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    Hq, Hkv = cfg.num_q_heads, cfg.num_kv_heads
+    _shape(q, "q", S, n_q, Hq, 192); _shape(out, "out", S, n_q, Hq, 128); _shape(q_pos, "q_pos", S)
+    _shape(k_pool, "k_pool", n_blocks, block_size, Hkv, 192); _shape(v_pool, "v_pool", n_blocks, block_size, Hkv, 128)
+    _shape(block_table, "block_table", S, block_table.shape[1]); _shape(sinks, "sinks", Hq)
+    ws_bytes = _ws(ws)
     _check("mimo_attn_decode_paged",
            lib.mimo_attn_decode_paged(ctypes.byref(cfg), S, n_q, _p(q), _p(q_pos), _p(k_pool), _p(v_pool), n_blocks,
                                       block_size, KV_DTYPE[kd], k_scale, v_scale, _p(block_table),
@@ -312,6 +359,10 @@ def mimo_kv_paged_append(cfg: MimoAttnCfg, k_new, v_new, pos, k_pool, v_pool, bl
     if kd != vd:
         raise ValueError("k_pool and v_pool must have the same element type")
     n_blocks, block_size = k_pool.shape[:2]
+    S, Hkv = k_new.shape[0], cfg.num_kv_heads
+    _shape(k_new, "k_new", S, Hkv, 192); _shape(v_new, "v_new", S, Hkv, 128); _shape(pos, "pos", S)
+    _shape(k_pool, "k_pool", n_blocks, block_size, Hkv, 192); _shape(v_pool, "v_pool", n_blocks, block_size, Hkv, 128)
+    _shape(block_table, "block_table", S, block_table.shape[1])
     _check("mimo_kv_paged_append",
            lib.mimo_kv_paged_append(ctypes.byref(cfg), k_new.shape[0], _p(k_new), _p(v_new), _p(pos), _p(k_pool),
                                     _p(v_pool), n_blocks, block_size, KV_DTYPE[kd], k_scale, v_scale,
@@ -326,6 +377,9 @@ def mimo_kv_ring_append(cfg: MimoAttnCfg, k_new, v_new, pos, k_cache, v_cache, s
     _need(pos, torch.int64, "pos", 1)
     S = k_new.shape[0]
     cap = k_cache.shape[1]
+    Hkv = cfg.num_kv_heads
+    _shape(k_new, "k_new", S, Hkv, 192); _shape(v_new, "v_new", S, Hkv, 128); _shape(pos, "pos", S)
+    _shape(k_cache, "k_cache", S, cap, Hkv, 192); _shape(v_cache, "v_cache", S, cap, Hkv, 128)
     _check("mimo_kv_ring_append",
            lib.mimo_kv_ring_append(ctypes.byref(cfg), S, _p(k_new), _p(v_new), _p(pos), _p(k_cache),
                                    _p(v_cache), cap, _stream(stream)))
