@@ -453,8 +453,17 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const int n_qb = (qhi - q_first) / 32 + 1;
     const int n_stage = G * n_qb;
     const int Hq = a.Hq;
+    // block order within a head: step t takes the block congruent to (last block of the
+    // sequence - t) mod n_qb, so workgroups of neighbouring keys copy the same stage at
+    // the same step (one L2 fetch serves them all); under a causal mask, all later blocks
+    const int boff = ((a.T - 1) / 32 - q_first / 32) % n_qb;
+    auto stage_q0 = [&](int s_) {
+        int i = boff - s_ % n_qb;
+        if (i < 0) i += n_qb;
+        return q_first + 32 * i;
+    };
     auto copy_stage = [&](int s_, int buf) {
-        const int head = g * G + s_ / n_qb, q0 = q_first + 32 * (s_ % n_qb);
+        const int head = g * G + s_ / n_qb, q0 = stage_q0(s_);
         const int last = min(32, a.T - q0) - 1;   // rows past it re-read it: masked out of every product
         const size_t hrow = ((size_t)b * Hq + head) * a.T + q0;
         const size_t trow0 = ((size_t)b * a.T + q0) * Hq + head;
@@ -487,7 +496,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     copy_stage(0, 0);
     __syncthreads();   // also waits for this wave's copies
     for (int s_ = 0; s_ < n_stage; ++s_) {
-        const int q0 = q_first + 32 * (s_ % n_qb);
+        const int q0 = stage_q0(s_);
         const int buf = s_ & 1;
         // the next stage goes to the other buffer, last read in the previous stage
         if (s_ + 1 < n_stage) copy_stage(s_ + 1, buf ^ 1);
