@@ -262,7 +262,8 @@ size_t mimo_attn_decode_multi_workspace_size(const mimo_attn_cfg *cfg, int32_t S
  * num_kv_heads, 192], dv [B, T, num_kv_heads, 128] (gradients of the unrotated
  * inputs, bf16) and, when sinks are given, dsinks [num_q_heads] fp32 (summed
  * over the batch).  ws: at least mimo_attn_backward_workspace_size() bytes.
- * Deterministic: nothing is accumulated across workgroups.
+ * Deterministic: nothing is accumulated across workgroups.  B * T * num_q_heads
+ * above 2^30 returns MIMO_ERR_UNSUPPORTED.
  */
 mimo_status mimo_attn_prefill_backward(const mimo_attn_cfg *cfg, const uint16_t *q, const uint16_t *k,
                                        const uint16_t *v, const float *sinks, int32_t B, int32_t T, int64_t pos0,

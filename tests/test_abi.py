@@ -304,6 +304,8 @@ def test_backward_contract(lib):
     assert lib.mimo_attn_backward_workspace_size(ctypes.byref(c), 0, 64) == 0
     assert bwd(lib, c, ws_bytes=need - 1) == WS
     assert bwd(lib, cfg_swa(num_q_heads=16, num_kv_heads=8)) == UNSUP    # group of 2
+    assert bwd(lib, c, Bn=1, T=(1 << 24) + 1) == UNSUP                   # B * T * 64 heads past 2^30
+    assert bwd(lib, c, Bn=1, T=1 << 24, ws_bytes=0) == WS                # at 2^30 the size is accepted
     assert bwd(lib, c, T=0, lse=None) == OK
 
 
