@@ -120,6 +120,34 @@ def profiled_traffic(workload_label: str):
     return None
 
 
+_BACKWARD_SOURCES = ["global_attention_sinks_amd/csrc/backward.hip"]
+_BACKWARD_PROFILE = os.path.join(ROOT, "profiles", "backward_swa_b4_t8192_pmc_counters.md")
+
+
+def profiled_backward_traffic():
+    """Bytes one backward call moved to and from HBM (all its kernels), summed from the
+    committed FETCH_SIZE / WRITE_SIZE profile (already scaled by the copy calibration), or
+    None when the profile is missing or the backward source changed since it was taken."""
+    import hashlib
+    import re
+    if not os.path.exists(_BACKWARD_PROFILE):
+        return None
+    text = open(_BACKWARD_PROFILE).read()
+    h = hashlib.sha256()
+    for f in _BACKWARD_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    m = re.search(r"backward sha256\[:16\] ([0-9a-f]{16})", text)
+    if not m or m.group(1) != h.hexdigest()[:16]:
+        return None
+    total, found = 0.0, False
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.strip("|").split("|")]
+        if len(cells) == 6 and cells[0].startswith("bwd_"):
+            total += (float(cells[3]) + float(cells[4])) * 1e9
+            found = True
+    return total if found else None
+
+
 # ------------------------------------------------------------ workloads
 
 def _dev_bf16(torch, bits):
@@ -870,7 +898,7 @@ def bench_backward(torch, gen, Bd, warmup, steps, src=None):
     gbs = nbytes / (ms_ev * 1e-3) / 1e9
     return {"ms": ms_ev, "ms_wall": wall * 1e3 / steps, "tflops": tflops, "gbs": gbs,
             "frac_hbm_peak": gbs / PEAK_HBM_GBS, "frac_mfma_peak": tflops / PEAK_BF16_TFLOPS,
-            "algorithmic_flops": flops, "algorithmic_bytes": nbytes}
+            "algorithmic_flops": flops, "algorithmic_bytes": nbytes, "traffic": profiled_backward_traffic()}
 
 
 def main_backward(args, torch, gen, Bd):
@@ -883,7 +911,7 @@ def main_backward(args, torch, gen, Bd):
              "config": {"workload": "swa_backward_b4_t8192 (dq, dk, dv, d sink from the forward's output and LSE)"},
              "roofline": {"bound": "hbm", "kernel": "bwd_krot + bwd_dq + bwd_sink + bwd_dkdv (one call)",
                           "achieved": r["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": r["frac_hbm_peak"],
-                          "traffic": None, "algorithmic_flops": r["algorithmic_flops"],
+                          "traffic": r["traffic"], "algorithmic_flops": r["algorithmic_flops"],
                           "algorithmic_bytes": r["algorithmic_bytes"], "tflops": r["tflops"],
                           "frac_mfma_peak": r["frac_mfma_peak"]},
              "cpu_baseline": None, "ms_per_call_events": r["ms"]}
