@@ -43,6 +43,20 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), name
 
 
+def test_peak_loop_library_exports_its_header():
+    """include/mimo_peaks.h declares the on-box peak loops of libmimo_peaks.so (measurement
+    only): the library loads and exports each of them (none is called here)."""
+    text = open(os.path.join(ROOT, "include", "mimo_peaks.h")).read()
+    names = sorted(set(re.findall(r"^\s*int\s+(mimo_peak_\w+)\s*\(", text, re.M)))
+    assert len(names) == 5, names
+    if not os.path.exists(B.PEAKS_PATH):
+        from global_attention_sinks_amd import build
+        build.build()
+    peaks = B.load_peaks()
+    for name in names:
+        assert hasattr(peaks, name), name
+
+
 def cfg_swa(**kw):
     c = B.swa_cfg()
     for k, v in kw.items():
