@@ -132,7 +132,10 @@ void prefill_kernel(PrefillArgs a) {
     __shared__ float2 rope_base[2][kPairs];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    // w through readfirstlane: the head, and so its sink, are then known to be
+    // wave-uniform, and the sink comes by a scalar load whose wait is not a wait
+    // for Q's vector loads
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h2 = lane >> 5, l32 = lane & 31;
 
     int qb, b, pair;
@@ -185,23 +188,17 @@ void prefill_kernel(PrefillArgs a) {
     const int tile_lo = (int)(jlo / NK);
     const int tile_hi = jhi >= jlo ? (int)(jhi / NK) : tile_lo - 1;
 
-    // ---- Q in registers (B operand): lane holds dims [96*h2, 96*h2+96) of query q0 + l32
+    // ---- Q in registers (B operand): lane holds dims [96*h2, 96*h2+96) of query q0 + l32;
+    // rotated below, once the first tile's loads are in flight beside these
     u32x4 qr[12];
-    {
-        const int t = q0 + l32;
-        if (t < Tq) {
-            const uint16_t *src = a.q + ((q_tok0 + t) * a.Hq + head) * kDqk + 96 * h2;
+    const bool q_valid = q0 + l32 < Tq;
+    if (q_valid) {
+        const uint16_t *src = a.q + ((q_tok0 + q0 + l32) * a.Hq + head) * kDqk + 96 * h2;
 #pragma unroll
-            for (int ks = 0; ks < 12; ++ks) qr[ks] = ldg128(src + 8 * ks);
-            if (h2 == 0) {
-                const int64_t qp = q_pos0 + t;
+        for (int ks = 0; ks < 12; ++ks) qr[ks] = ldg128(src + 8 * ks);
+    } else {
 #pragma unroll
-                for (int cc = 0; cc < 4; ++cc) rope_rotate8(qr[cc], qr[cc + 4], a.rt, 8 * cc, qp);
-            }
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < 12; ++ks) qr[ks] = u32x4{0, 0, 0, 0};
-        }
+        for (int ks = 0; ks < 12; ++ks) qr[ks] = u32x4{0, 0, 0, 0};
     }
 
     // ---- softmax state of this lane's query column
@@ -341,11 +338,16 @@ void prefill_kernel(PrefillArgs a) {
     const int prow = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
     const int64_t qp = q_pos0 + q0 + l32;
 
+    // the first tile's loads go out beside Q's, so the two round trips overlap
+    if (tile_hi >= tile_lo) load_tile(tile_lo);
+    if (q_valid && h2 == 0) {
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) rope_rotate8(qr[cc], qr[cc + 4], a.rt, 8 * cc, qp);
+    }
     if (tile_hi >= tile_lo) {
         tile_bases(tile_lo);
         if (tile_lo + 1 <= tile_hi) tile_bases(tile_lo + 1);
         __syncthreads();
-        load_tile(tile_lo);
         store_tile(tile_lo, 0);
     }
     __syncthreads();
@@ -957,6 +959,10 @@ void prefill_band_kernel(PrefillArgs a) {
     const int r = blockIdx.x % runs, bg = blockIdx.x / runs;
     const int g = bg % a.Hkv, b = bg / a.Hkv;
     const int head = g * NW + w;
+    // the head's sink in the exp2 domain, read once by a scalar load (the index made
+    // wave-uniform): a vector load waited for at each block's start would also wait
+    // for every store and load issued before it
+    const float sink_l2 = a.sinks ? a.sinks[__builtin_amdgcn_readfirstlane(head)] * kLog2e : kNegInf;
 
     int Tq, Tk;
     size_t q_tok0, k_tok0, lse_off;
@@ -1106,7 +1112,7 @@ void prefill_band_kernel(PrefillArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 12; ++ks) qr[ks] = ldg128(src + 8 * ks);
         rope_rotate_block(qr, q_pos0 + q0, l32, h2, a.rt);
-        m_run = a.sinks ? a.sinks[head] * kLog2e : kNegInf;
+        m_run = sink_l2;
         l_run = (a.sinks && h2 == 0) ? 1.0f : 0.0f;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
